@@ -1,0 +1,353 @@
+"""Plain, slow, obviously correct NumPy oracle of the weight-only quantized linear path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; never by the product path.  It shares no code with the
+HIP library.
+
+Sources (cited by page title and section):
+
+* GPTQModel wiki, "MLX Apple Silicon": the Concepts table (MLX affine storage: packed uint32
+  codes, scales and additive biases, value = code*scale + bias) and "Packed layouts and exact
+  transcoding" (scales/biases laid out [out, groups]; whole codes per uint32 for 2/4/8 bits,
+  little-endian bit order; GGUF Q8_0 maps to 8-bit group-32 affine with the signed byte
+  plus 128).
+* tinygpt PRD "Quantized inference ... QuantizedLinear", section "Problem": 8 four-bit values
+  per uint32 with per-weight ``.scales`` and ``.biases`` companions.
+* gguf2mlx-stream, section "01 Tensor-bounded streaming": MLX affine quantization into packed
+  uint32 plus f16 scales/biases.
+* Nx_quant API docs: "Weights" (Mxfp4 codes/scales layout, Q8_0 block layout, the MXFP4
+  decode rule), ``quantize_q8_0``, and "Products" (``dequant``, ``apply``,
+  ``apply_experts``).
+
+Readings of points the pages leave open (each listed in the design doc):
+
+* quantizer: per (row, group of g along k): mn = min, mx = max over the group in fp32 (total
+  order, -0 < +0); s32 = fl32(fl32(mx - mn) / (2^bits - 1)); stored s = RNE(s32), stored
+  b = RNE(mn) in the parameter dtype; t = fl32(fl32(v - b) / s) with the stored b, s; code
+  q = clamp(round-half-even(t), 0, 2^bits - 1); q = 0 where the stored s is 0.
+* dequant: value = fl32(q*s + b) (one rounding; q*s is exact in fp32), then rounded once to
+  the output dtype.
+* apply: y = x . dequant(W)^T computed here exactly in fp64 from the fp32 values.
+
+Float storage types travel as uint16 bit patterns (``'f16'`` or ``'bf16'``); fp32 as numpy
+float32.  All arithmetic below is NumPy on the CPU.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "f32_to_bf16_bits",
+    "bf16_bits_to_f32",
+    "f32_to_f16_bits",
+    "f16_bits_to_f32",
+    "to_bits",
+    "bits_to_f64",
+    "round_f32_to",
+    "pack_codes",
+    "unpack_codes",
+    "group_min_max",
+    "affine_quantize",
+    "affine_dequant_f32",
+    "affine_dequant_to",
+    "apply",
+    "MXFP4_MAGNITUDES",
+    "mxfp4_dequant_f32",
+    "q8_0_dequant_f32",
+    "q8_0_quantize",
+    "route",
+    "apply_experts",
+    "rel_l2_per_row",
+]
+
+# --------------------------------------------------------------------------------------
+# 16-bit float storage types (IEEE binary16 and bfloat16), round to nearest even.
+# --------------------------------------------------------------------------------------
+
+
+def f32_to_bf16_bits(a) -> np.ndarray:
+    """Round fp32 to bfloat16 (nearest, ties to even); NaN maps to a quiet NaN of the same sign."""
+    a = np.asarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    nan = np.isnan(a)
+    if np.any(nan):
+        r = r.copy()
+        r[nan] = ((u[nan] >> np.uint64(16)).astype(np.uint16) | np.uint16(0x0040))
+    return r
+
+
+def bf16_bits_to_f32(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def f32_to_f16_bits(a) -> np.ndarray:
+    """Round fp32 to IEEE binary16 (NumPy's conversion rounds to nearest even)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b) -> np.ndarray:
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def to_bits(dtype: str, a_f32) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a_f32)
+    if dtype == "f16":
+        return f32_to_f16_bits(a_f32)
+    raise ValueError(f"not a 16-bit dtype: {dtype}")
+
+
+def bits_to_f64(dtype: str, bits) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_bits_to_f32(bits).astype(np.float64)
+    if dtype == "f16":
+        return f16_bits_to_f32(bits).astype(np.float64)
+    raise ValueError(f"not a 16-bit dtype: {dtype}")
+
+
+def round_f32_to(dtype: str, a_f32):
+    """Round an fp32 array once to ``dtype``: returns float32 for 'f32', bit patterns otherwise."""
+    if dtype == "f32":
+        return np.asarray(a_f32, dtype=np.float32)
+    return to_bits(dtype, a_f32)
+
+
+# --------------------------------------------------------------------------------------
+# Affine storage (GPTQModel wiki "MLX Apple Silicon": Concepts; Packed layouts).
+# --------------------------------------------------------------------------------------
+
+
+def pack_codes(q, bits: int) -> np.ndarray:
+    """Pack integer codes [rows, k] into uint32 words [rows, k*bits/32], low bits first.
+
+    Code c of a word sits at bit positions [bits*c, bits*(c+1)), c ascending along k
+    (whole codes per word for 2/4/8 bits, little-endian order)."""
+    q = np.asarray(q, dtype=np.int64)
+    rows, k = q.shape
+    per = 32 // bits
+    assert bits in (2, 4, 8) and k % per == 0
+    assert q.min(initial=0) >= 0 and q.max(initial=0) < (1 << bits)
+    qq = q.reshape(rows, k // per, per).astype(np.uint64)
+    words = np.zeros((rows, k // per), dtype=np.uint64)
+    for c in range(per):
+        words |= qq[:, :, c] << np.uint64(bits * c)
+    return words.astype(np.uint32)
+
+
+def unpack_codes(packed, bits: int, k: int) -> np.ndarray:
+    """Inverse of :func:`pack_codes`: words [rows, k*bits/32] -> codes [rows, k] (int64)."""
+    packed = np.asarray(packed, dtype=np.uint32)
+    per = 32 // bits
+    rows = packed.shape[0]
+    assert packed.shape[1] * per == k
+    mask = np.uint32((1 << bits) - 1)
+    out = np.empty((rows, k // per, per), dtype=np.int64)
+    for c in range(per):
+        out[:, :, c] = (packed >> np.uint32(bits * c)) & mask
+    return out.reshape(rows, k)
+
+
+def group_min_max(v_f32):
+    """Per-row min and max of fp32 values [..., g] under the IEEE total order (-0 < +0).
+
+    Only finite inputs are in the domain."""
+    v = np.asarray(v_f32, dtype=np.float32)
+    assert np.all(np.isfinite(v)), "the affine quantizer is defined for finite weights only"
+    mn = v.min(axis=-1)
+    mx = v.max(axis=-1)
+    neg0 = np.signbit(v) & (v == 0)
+    pos0 = (~np.signbit(v)) & (v == 0)
+    mn = np.where((mn == 0) & neg0.any(axis=-1), np.float32(-0.0), np.where(mn == 0, np.float32(0.0), mn))
+    mx = np.where((mx == 0) & pos0.any(axis=-1), np.float32(0.0), np.where(mx == 0, np.float32(-0.0), mx))
+    return mn.astype(np.float32), mx.astype(np.float32)
+
+
+def affine_quantize(w_f32, bits: int, group_size: int, param_dtype: str):
+    """Affine group quantizer: fp32 W [n, k] -> (packed u32 [n, k*bits/32], scale bits [n, k/g],
+    bias bits [n, k/g]).
+
+    Per (row, group): scale = (max - min) / (2^bits - 1), bias = min, stored in
+    ``param_dtype`` (round to nearest even); codes are the nearest level to each value,
+    computed as round-half-even((v - b) / s) with the stored b and s, clamped to
+    [0, 2^bits - 1]; a zero stored scale gives code 0 (readings listed in the module doc)."""
+    w = np.asarray(w_f32, dtype=np.float32)
+    n, k = w.shape
+    g = group_size
+    assert k % g == 0 and k % 32 == 0
+    levels = np.float32((1 << bits) - 1)
+    v = w.reshape(n, k // g, g)
+    mn, mx = group_min_max(v)
+    with np.errstate(over="ignore"):
+        s32 = ((mx - mn).astype(np.float32) / levels).astype(np.float32)
+    s_bits = to_bits(param_dtype, s32)
+    b_bits = to_bits(param_dtype, mn)
+    s = bits_to_f64(param_dtype, s_bits).astype(np.float32)
+    b = bits_to_f64(param_dtype, b_bits).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        t = ((v - b[..., None]).astype(np.float32) / s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(t), 0, levels)
+    q = np.where(s[..., None] == 0, 0, q)
+    q = np.where(np.isnan(q), 0, q).astype(np.int64).reshape(n, k)
+    return pack_codes(q, bits), s_bits, b_bits
+
+
+def affine_dequant_f32(packed, scale_bits, bias_bits, bits: int, group_size: int, param_dtype: str, k: int):
+    """value = fl32(q*s + b) for every weight (Nx_quant "Products", dequant: a value is a
+    float32 value).  q*s + b is exact in fp64 (q < 2^8, s has <= 11 significant bits), so the
+    single rounding to fp32 here is the only one."""
+    q = unpack_codes(packed, bits, k).astype(np.float64)
+    n = q.shape[0]
+    s = bits_to_f64(param_dtype, scale_bits)
+    b = bits_to_f64(param_dtype, bias_bits)
+    sg = np.repeat(s, group_size, axis=1).reshape(n, k)
+    bg = np.repeat(b, group_size, axis=1).reshape(n, k)
+    return (q * sg + bg).astype(np.float32)
+
+
+def affine_dequant_to(out_dtype: str, packed, scale_bits, bias_bits, bits, group_size, param_dtype, k):
+    """dequant at ``out_dtype``: the fp32 value rounded once (bit patterns for 16-bit types)."""
+    return round_f32_to(out_dtype, affine_dequant_f32(packed, scale_bits, bias_bits, bits, group_size, param_dtype, k))
+
+
+def apply(x_f64, w_values, layer_bias=None) -> np.ndarray:
+    """Nx_quant "Products", apply: y = x . W^T with W the dequantized (fp32) weight values, here
+    summed exactly enough in fp64 (NumPy matmul over fp64 copies).  x is [m, k], W [n, k]."""
+    x = np.asarray(x_f64, dtype=np.float64)
+    w = np.asarray(w_values, dtype=np.float64)
+    y = x @ w.T
+    if layer_bias is not None:
+        y = y + np.asarray(layer_bias, dtype=np.float64)[None, :]
+    return y
+
+
+# --------------------------------------------------------------------------------------
+# MXFP4 with its scales apart (Nx_quant "Weights": Mxfp4; OCP Microscaling 2023 E2M1/E8M0).
+# --------------------------------------------------------------------------------------
+
+MXFP4_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mxfp4_dequant_f32(codes_u8, scales_u8) -> np.ndarray:
+    """codes [..., n, k/2] (value 2i in byte i's low nibble, 2i+1 in its high nibble) and E8M0
+    scales [..., n, k/32] -> fp32 values [..., n, k].
+
+    Code bit 3 is the sign, bits 2..0 index the magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}; the value
+    is sign * magnitude * 2^(s - 127), rounded to fp32 (exact unless it overflows to inf); the
+    scale byte 255 makes its whole block NaN."""
+    codes = np.asarray(codes_u8, dtype=np.uint8)
+    scales = np.asarray(scales_u8, dtype=np.uint8)
+    lead = codes.shape[:-1]
+    k = codes.shape[-1] * 2
+    assert scales.shape == lead + (k // 32,)
+    nib = np.empty(lead + (k,), dtype=np.int64)
+    nib[..., 0::2] = codes & 0x0F
+    nib[..., 1::2] = codes >> 4
+    mag = np.asarray(MXFP4_MAGNITUDES, dtype=np.float64)[nib & 7]
+    sign = np.where(nib & 8, -1.0, 1.0)
+    sc = np.repeat(scales.astype(np.int64), 32, axis=-1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        val = sign * np.ldexp(mag, sc - 127)
+        val = np.where(sc == 255, np.nan, val)
+        return val.astype(np.float32)
+
+
+# --------------------------------------------------------------------------------------
+# Q8_0 blocks (Nx_quant "Weights": Q8_0; quantize_q8_0).
+# --------------------------------------------------------------------------------------
+
+
+def q8_0_dequant_f32(blocks_u8) -> np.ndarray:
+    """blocks [..., n, k/32*34]: per 32 values a little-endian fp16 scale d then 32 int8 quants;
+    value = d * q, exact in fp32."""
+    b = np.asarray(blocks_u8, dtype=np.uint8)
+    lead = b.shape[:-1]
+    assert b.shape[-1] % 34 == 0
+    nb = b.shape[-1] // 34
+    blk = b.reshape(lead + (nb, 34))
+    d_bits = blk[..., 0].astype(np.uint16) | (blk[..., 1].astype(np.uint16) << np.uint16(8))
+    d = f16_bits_to_f32(d_bits).astype(np.float64)
+    q = blk[..., 2:].view(np.int8).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return (d[..., None] * q).astype(np.float32).reshape(lead + (nb * 32,))
+
+
+def q8_0_quantize(w_f32) -> np.ndarray:
+    """quantize_q8_0 for finite fp32 input [..., n, k] -> blocks [..., n, k/32*34].
+
+    Per block of 32 values: d = amax/127 in fp32, stored as fp16 (nearest); quants are
+    v * (1/d) in fp32 rounded half away from zero, with 1/d taken from the fp32 d; a block
+    whose d is 0 or whose 1/d is infinite is all zero bytes."""
+    w = np.asarray(w_f32, dtype=np.float32)
+    assert np.all(np.isfinite(w)), "only the finite path of quantize_q8_0 is used as a test-data generator"
+    lead = w.shape[:-1]
+    k = w.shape[-1]
+    assert k % 32 == 0
+    v = w.reshape(lead + (k // 32, 32))
+    amax = np.abs(v).max(axis=-1).astype(np.float32)
+    d = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d == 0, np.float32(0.0), (np.float32(1.0) / d)).astype(np.float32)
+    zero_blk = (d == 0) | np.isinf(inv)
+    inv = np.where(zero_blk, np.float32(0.0), inv)
+    prod = (v * inv[..., None]).astype(np.float32).astype(np.float64)
+    q = (np.sign(prod) * np.floor(np.abs(prod) + 0.5)).astype(np.int64)
+    q = np.where(zero_blk[..., None], 0, q)
+    assert q.min(initial=0) >= -128 and q.max(initial=0) <= 127
+    d_bits = np.where(zero_blk, np.uint16(0), f32_to_f16_bits(d)).astype(np.uint16)
+    out = np.empty(lead + (k // 32, 34), dtype=np.uint8)
+    out[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    out[..., 1] = (d_bits >> 8).astype(np.uint8)
+    out[..., 2:] = q.astype(np.int8).view(np.uint8)
+    return out.reshape(lead + (k // 32 * 34,))
+
+
+# --------------------------------------------------------------------------------------
+# Routing and apply_experts (Nx_quant "Products": apply_experts).
+# --------------------------------------------------------------------------------------
+
+
+def route(ids, e: int):
+    """Group positions by expert: returns (offsets int32 [e+1], perm int32 [offsets[e]]).
+
+    Positions p with 0 <= ids[p] < e are listed expert by expert, each expert's positions in
+    increasing p (a stable counting sort); positions out of range are dropped."""
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    offsets = np.zeros(e + 1, dtype=np.int64)
+    buckets = [[] for _ in range(e)]
+    for p, i in enumerate(ids.tolist()):
+        if 0 <= i < e:
+            buckets[i].append(p)
+    for j in range(e):
+        offsets[j + 1] = offsets[j] + len(buckets[j])
+    perm = np.array([p for bkt in buckets for p in bkt], dtype=np.int64)
+    return offsets.astype(np.int32), perm.astype(np.int32)
+
+
+def apply_experts(w_values_e, ids, x_f64, pos_per_row: int = 1) -> np.ndarray:
+    """y[p, :] = x[p // pos_per_row] . W_{ids[p]}^T in fp64, zeros where ids[p] is not in [0, e).
+
+    ``w_values_e`` is [e, n, k] (the experts' dequantized fp32 values), ``ids`` [P] and ``x`` is
+    [P / pos_per_row, k]; the x row of a position is shared by ``pos_per_row`` consecutive
+    positions (a token's top-k slots)."""
+    w = np.asarray(w_values_e)
+    e, n, k = w.shape
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    x = np.asarray(x_f64, dtype=np.float64)
+    y = np.zeros((ids.size, n), dtype=np.float64)
+    for j in range(e):
+        pos = np.nonzero(ids == j)[0]
+        if pos.size:
+            y[pos] = x[pos // pos_per_row] @ w[j].astype(np.float64).T
+    return y
+
+
+def rel_l2_per_row(y, ref) -> np.ndarray:
+    """||y - ref||_2 / ||ref||_2 for each row (rows whose reference is all zero use 1 as norm)."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.sqrt(((y - ref) ** 2).sum(axis=-1))
+    den = np.sqrt((ref ** 2).sum(axis=-1))
+    return num / np.where(den == 0, 1.0, den)

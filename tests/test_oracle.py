@@ -1,0 +1,364 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: hand-derived fixtures
+under tests/golden/, closed forms, brute force over all code levels, invariants, a library
+routine (torch's fp32->bf16/fp16 conversion) or an independent bit-level definition.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- 16-bit rounding
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_rne_matches_torch_cpu(dtype):
+    """RNE to bf16/fp16 equals torch's CPU conversion, including exact ties, subnormals and NaN."""
+    g = np.random.default_rng(7)
+    a = np.concatenate(
+        [
+            g.standard_normal(20000).astype(np.float32) * np.float32(0.02),
+            g.standard_normal(2000).astype(np.float32) * np.float32(1e-38),
+            # exact bf16 ties: low 16 bits == 0x8000
+            (g.integers(0, 2**15, 2000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32),
+            np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65520.0, 1e-8, -1e-8], dtype=np.float32),
+        ]
+    )
+    a = a[np.isfinite(a) | np.isinf(a)]
+    t = torch.from_numpy(a.copy())
+    ref = t.to(torch.bfloat16 if dtype == "bf16" else torch.float16).view(torch.int16).numpy().view(np.uint16)
+    got = O.to_bits(dtype, a)
+    np.testing.assert_array_equal(got, ref)
+    nan = O.to_bits(dtype, np.array([np.nan], dtype=np.float32))
+    assert np.isnan(O.bits_to_f64(dtype, nan))[0]
+
+
+# ---------------------------------------------------------------- packing order
+
+
+def test_pack_low_bits_first_4bit():
+    q = np.arange(8)[None, :]
+    assert O.pack_codes(q, 4)[0, 0] == 0x76543210
+    q = np.arange(16)[None, :]
+    np.testing.assert_array_equal(O.pack_codes(q, 4)[0], [0x76543210, 0xFEDCBA98])
+
+
+def test_pack_low_bits_first_8bit_and_2bit():
+    assert O.pack_codes(np.arange(4)[None, :], 8)[0, 0] == 0x03020100
+    assert O.pack_codes(np.array([[255, 0, 0, 1]]), 8)[0, 0] == 0x010000FF
+    assert O.pack_codes(np.array([[1, 2, 3, 0] * 4]), 2)[0, 0] == int("".join(["00", "11", "10", "01"] * 4), 2)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_unpack_inverts_pack(bits):
+    g = np.random.default_rng(bits)
+    q = g.integers(0, 1 << bits, size=(5, 128))
+    np.testing.assert_array_equal(O.unpack_codes(O.pack_codes(q, bits), bits, 128), q)
+
+
+# ---------------------------------------------------------------- quantizer
+
+
+@pytest.mark.parametrize("pdt", ["f16", "bf16"])
+def test_quantize_golden_exact_group(pdt):
+    fx = _golden("affine_g64_exact_group.json")
+    w = np.array(fx["w"], dtype=np.float32)[None, :]
+    packed, sb, bb = O.affine_quantize(w, 4, 64, pdt)
+    np.testing.assert_array_equal(packed[0], np.array(fx["packed"], dtype=np.uint32))
+    assert sb[0, 0] == fx["scale_bits"][pdt]
+    assert bb[0, 0] == fx["bias_bits"][pdt]
+    deq = O.affine_dequant_f32(packed, sb, bb, 4, 64, pdt, 64)
+    np.testing.assert_array_equal(deq[0], w[0])
+
+
+def _brute_codes(w, s, b, bits):
+    """Nearest level index by exhaustive search over all 2^bits levels b + c*s in fp64, ties
+    to the even index; also returns the distance gap between the two best levels."""
+    L = (1 << bits) - 1
+    c = np.arange(L + 1, dtype=np.float64)
+    lv = b[..., None] + c * s[..., None]
+    d = np.abs(w[..., None] - lv)
+    best = d.min(axis=-1, keepdims=True)
+    tie = np.isclose(d, best, rtol=0, atol=0)
+    # among exact ties choose even index
+    even_pref = np.where(tie, np.where(c % 2 == 0, 0, 1), 2)
+    idx = np.argmin(even_pref * 1e6 + c * 0 + np.where(tie, 0, 1e9), axis=-1)
+    ds = np.sort(d, axis=-1)
+    gap = ds[..., 1] - ds[..., 0]
+    return idx, gap
+
+
+@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "f16"), (4, 32, "bf16"), (8, 64, "bf16"), (8, 128, "f16"), (4, 128, "bf16")])
+def test_quantize_codes_equal_brute_force_nearest_level(bits, g, pdt):
+    n, k = 6, 256
+    w = synth.weights_f32(11 + bits + g, n, k)
+    packed, sb, bb = O.affine_quantize(w, bits, g, pdt)
+    q = O.unpack_codes(packed, bits, k).reshape(n, k // g, g)
+    s = O.bits_to_f64(pdt, sb)[..., None].repeat(g, -1)
+    b = O.bits_to_f64(pdt, bb)[..., None].repeat(g, -1)
+    wv = w.astype(np.float64).reshape(n, k // g, g)
+    idx, gap = _brute_codes(wv, s, b, bits)
+    diff = idx != q
+    # A mismatch is allowed only where the two nearest levels are within fp32 rounding of a tie.
+    assert np.all(gap[diff] <= 4e-7 * np.maximum(1.0, np.abs(wv[diff]) / s[diff]) * s[diff] + 1e-12)
+    assert diff.sum() <= 2
+
+
+@pytest.mark.parametrize("bits,pdt", [(4, "f16"), (4, "bf16"), (8, "bf16"), (8, "f16")])
+def test_quantize_scale_is_range_over_levels_and_bias_is_min(bits, pdt):
+    """scale = RNE((max-min)/(2^bits-1)) and bias = RNE(min), with max/min found by a loop."""
+    w = synth.weights_f32(5, 3, 128)
+    g = 64
+    _, sb, bb = O.affine_quantize(w, bits, g, pdt)
+    for r in range(3):
+        for j in range(2):
+            vals = [float(v) for v in w[r, j * g:(j + 1) * g]]
+            lo, hi = vals[0], vals[0]
+            for v in vals:
+                lo = v if v < lo else lo
+                hi = v if v > hi else hi
+            s32 = np.float32(np.float32(hi) - np.float32(lo)) / np.float32((1 << bits) - 1)
+            want_s = torch.tensor([float(s32)], dtype=torch.float32).to(torch.bfloat16 if pdt == "bf16" else torch.float16)
+            want_b = torch.tensor([lo], dtype=torch.float32).to(torch.bfloat16 if pdt == "bf16" else torch.float16)
+            assert sb[r, j] == want_s.view(torch.int16).numpy().view(np.uint16)[0]
+            assert bb[r, j] == want_b.view(torch.int16).numpy().view(np.uint16)[0]
+
+
+@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "bf16"), (4, 64, "f16"), (8, 32, "bf16"), (8, 64, "f16")])
+def test_quantize_round_trip_bound(bits, g, pdt):
+    """|w - dequant| <= s/2 inside [b, b + L*s]; outside, only by the clamp distance, which is
+    bounded by the storage rounding of the min and of the scale."""
+    n, k = 64, 512
+    w = synth.weights_f32(21 + bits, n, k)
+    packed, sb, bb = O.affine_quantize(w, bits, g, pdt)
+    deq = O.affine_dequant_f32(packed, sb, bb, bits, g, pdt, k).astype(np.float64).reshape(n, k // g, g)
+    L = (1 << bits) - 1
+    s = O.bits_to_f64(pdt, sb)[..., None]
+    b = O.bits_to_f64(pdt, bb)[..., None]
+    wv = w.astype(np.float64).reshape(n, k // g, g)
+    err = np.abs(wv - deq)
+    outside = np.maximum(0.0, np.maximum(b - wv, wv - (b + L * s)))
+    assert np.all(err <= s / 2 * (1 + 1e-6) + outside + 1e-12)
+    mn = wv.min(-1, keepdims=True)
+    mx = wv.max(-1, keepdims=True)
+    slack = np.abs(b - mn) + L * np.abs(s - (mx - mn) / L) + 1e-7 * np.abs(mx - mn)
+    assert np.all(outside <= slack)
+
+
+@pytest.mark.parametrize("bits,pdt", [(4, "bf16"), (4, "f16"), (8, "bf16"), (8, "f16")])
+def test_quantize_identity_on_exact_grid(bits, pdt):
+    """W = q*s + b with dyadic s, b (exact in fp32 and in the param dtype) and both end codes in
+    every group requantizes to the same codes, scale and bias, bit for bit."""
+    g = np.random.default_rng(3 + bits)
+    n, k, gs = 8, 256, 64
+    L = (1 << bits) - 1
+    q = g.integers(0, L + 1, size=(n, k // gs, gs))
+    q[..., 0] = 0
+    q[..., 1] = L
+    s = np.exp2(g.integers(-10, -4, size=(n, k // gs))).astype(np.float64)
+    b = -np.exp2(g.integers(-6, -2, size=(n, k // gs))).astype(np.float64) * g.integers(1, 4, size=(n, k // gs))
+    w = (q * s[..., None] + b[..., None]).astype(np.float32).reshape(n, k)
+    packed, sb, bb = O.affine_quantize(w, bits, gs, pdt)
+    np.testing.assert_array_equal(O.unpack_codes(packed, bits, k), q.reshape(n, k))
+    np.testing.assert_array_equal(O.bits_to_f64(pdt, sb), s)
+    np.testing.assert_array_equal(O.bits_to_f64(pdt, bb), b)
+
+
+def test_quantize_constant_group_and_signed_zero():
+    w = np.zeros((2, 64), dtype=np.float32)
+    w[0, :] = 0.125
+    w[1, :] = 0.0
+    w[1, 5] = -0.0
+    packed, sb, bb = O.affine_quantize(w, 4, 64, "bf16")
+    assert np.all(packed == 0)
+    assert sb[0, 0] == 0 and sb[1, 0] == 0
+    assert bb[0, 0] == O.f32_to_bf16_bits(np.float32(0.125))
+    assert bb[1, 0] == 0x8000  # min under the total order is -0
+    mn, mx = O.group_min_max(np.array([[0.0, -0.0], [-0.0, -0.0], [0.0, 0.0]], dtype=np.float32))
+    assert list(np.signbit(mn)) == [True, True, False]
+    assert list(np.signbit(mx)) == [False, True, False]
+
+
+# ---------------------------------------------------------------- dequant and apply
+
+
+def test_dequant_closed_form_and_output_rounding():
+    packed = O.pack_codes(np.array([[0, 1, 2, 15] * 16]), 4)
+    sb = O.to_bits("f16", np.array([[0.5]], dtype=np.float32))
+    bb = O.to_bits("f16", np.array([[-3.0]], dtype=np.float32))
+    v = O.affine_dequant_f32(packed, sb, bb, 4, 64, "f16", 64)
+    np.testing.assert_array_equal(v[0, :4], [-3.0, -2.5, -2.0, 4.5])
+    # a value not representable in bf16 is rounded once to nearest even
+    sb = O.to_bits("f16", np.array([[2.0 ** -10 * 1.0009765625]], dtype=np.float32))
+    bb = O.to_bits("f16", np.array([[1.0]], dtype=np.float32))
+    v = O.affine_dequant_f32(packed, sb, bb, 4, 64, "f16", 64)
+    exact = 1.0 + 15 * O.bits_to_f64("f16", sb)[0, 0]
+    assert float(v[0, 3]) == float(np.float32(exact))
+    want = torch.tensor([float(v[0, 3])], dtype=torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert O.affine_dequant_to("bf16", packed, sb, bb, 4, 64, "f16", 64)[0, 3] == want[0]
+
+
+def test_apply_one_hot_gives_columns_and_matches_loops():
+    w = synth.weights_f32(9, 12, 64)
+    packed, sb, bb = O.affine_quantize(w, 4, 32, "bf16")
+    D = O.affine_dequant_f32(packed, sb, bb, 4, 32, "bf16", 64)
+    for j in (0, 17, 63):
+        x = np.zeros((1, 64))
+        x[0, j] = 1.0
+        np.testing.assert_array_equal(O.apply(x, D)[0], D[:, j].astype(np.float64))
+    x = O.bits_to_f64("bf16", synth.acts_bits(10, 3, 64, "bf16"))
+    y = O.apply(x, D, layer_bias=np.arange(12) * 0.5)
+    for m in range(3):
+        for n in range(12):
+            acc = math.fsum(float(x[m, kk]) * float(D[n, kk]) for kk in range(64)) + n * 0.5
+            assert abs(y[m, n] - acc) <= 1e-12 * (1 + abs(acc))
+
+
+# ---------------------------------------------------------------- MXFP4
+
+
+def _e2m1_bit_level(c):
+    """OCP MX E2M1 bit-level definition: S E1 E0 M; E>0: 2^(E-1)*(1+M/2); E=0: M*0.5."""
+    sgn = -1.0 if c & 8 else 1.0
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = 2.0 ** (e - 1) * (1 + m / 2) if e > 0 else 0.5 * m
+    return sgn * mag
+
+
+def test_mxfp4_magnitude_table_equals_bit_level_definition():
+    for c in range(16):
+        tab = (-1.0 if c & 8 else 1.0) * O.MXFP4_MAGNITUDES[c & 7]
+        assert tab == _e2m1_bit_level(c)
+        assert math.copysign(1.0, tab) == math.copysign(1.0, _e2m1_bit_level(c))
+
+
+def test_mxfp4_golden_row():
+    fx = _golden("mxfp4_row_codes_0_15.json")
+    codes = np.array(fx["codes"], dtype=np.uint8)[None, :]
+    scales = np.array([[fx["scale"]]], dtype=np.uint8)
+    got = O.mxfp4_dequant_f32(codes, scales)[0]
+    want = np.array([float(v) for v in fx["values"]], dtype=np.float32)
+    np.testing.assert_array_equal(got, want)
+    np.testing.assert_array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_mxfp4_exhaustive_codes_and_scales():
+    """All 16 codes x 256 scale bytes: NaN at 255, inf for magnitude >= 4 at 253 and >= 2 at 254,
+    every other value exact (equal to its fp64 value), and exactly representable in bf16."""
+    codes = np.array([[(c | (c << 4)) for c in range(16)] * 1], dtype=np.uint8)  # 32 values
+    codes = np.repeat(codes, 256, axis=0)
+    scales = np.arange(256, dtype=np.uint8)[:, None]
+    v = O.mxfp4_dequant_f32(codes, scales)
+    for s in range(256):
+        for c in range(16):
+            got = float(v[s, 2 * c])
+            assert float(v[s, 2 * c + 1]) == got or (math.isnan(got) and math.isnan(float(v[s, 2 * c + 1])))
+            mag = O.MXFP4_MAGNITUDES[c & 7]
+            if s == 255:
+                assert math.isnan(got)
+            elif (s == 253 and mag >= 4) or (s == 254 and mag >= 2):
+                assert math.isinf(got)
+            else:
+                assert got == _e2m1_bit_level(c) * 2.0 ** (s - 127)
+                b = O.f32_to_bf16_bits(np.float32(got))
+                assert float(O.bf16_bits_to_f32(b)) == got
+    zero = O.mxfp4_dequant_f32(np.zeros((1, 16), np.uint8), np.zeros((1, 1), np.uint8))
+    assert np.all(zero == 0) and not np.any(np.signbit(zero))
+
+
+# ---------------------------------------------------------------- Q8_0
+
+
+def test_q8_0_equals_8bit_g32_affine_with_offset_128():
+    """GGUF Q8_0 is 8-bit group-32 affine with code q+128, scale d, bias -128*d."""
+    blocks = synth.q8_0_random_blocks(4, 1, 8, 256)[0]
+    v = O.q8_0_dequant_f32(blocks)
+    blk = blocks.reshape(8, 8, 34)
+    d_bits = blk[..., 0].astype(np.uint16) | (blk[..., 1].astype(np.uint16) << 8)
+    q = blk[..., 2:].view(np.int8).astype(np.int64)
+    codes = (q + 128).reshape(8, 256)
+    d = O.bits_to_f64("f16", d_bits)
+    packed = O.pack_codes(codes, 8)
+    sb = d_bits
+    bb = O.to_bits("f16", (-128.0 * d).astype(np.float32))  # -128*d is exact in fp16 unless it overflows
+    np.testing.assert_array_equal(O.bits_to_f64("f16", bb), -128.0 * d)
+    va = O.affine_dequant_f32(packed, sb, bb, 8, 32, "f16", 256)
+    np.testing.assert_array_equal(v, va)
+
+
+def test_q8_0_hand_block_and_zero_block():
+    blk = np.zeros(34, dtype=np.uint8)
+    blk[0], blk[1] = 0x00, 0x38  # fp16 0.5, little-endian
+    blk[2:] = np.arange(-128, -96, dtype=np.int64).astype(np.int8).view(np.uint8)
+    v = O.q8_0_dequant_f32(blk[None, :])[0]
+    np.testing.assert_array_equal(v, np.arange(-128, -96) * 0.5)
+    z = O.q8_0_dequant_f32(np.zeros((1, 68), np.uint8))
+    assert np.all(z == 0)
+
+
+def test_q8_0_quantize_golden_halves_away():
+    fx = _golden("q8_0_halves_away_block.json")
+    w = np.array(fx["w"], dtype=np.float32)[None, :]
+    blk = O.q8_0_quantize(w)[0]
+    assert int(blk[0]) | (int(blk[1]) << 8) == fx["d_bits"]
+    np.testing.assert_array_equal(blk[2:].view(np.int8), np.array(fx["quants"], dtype=np.int8))
+
+
+def test_q8_0_quantize_round_trip_bound():
+    w = synth.weights_f32(31, 16, 512)
+    v = O.q8_0_dequant_f32(O.q8_0_quantize(w)).astype(np.float64)
+    wb = w.reshape(16, 16, 32).astype(np.float64)
+    d32 = np.abs(wb).max(-1, keepdims=True) / 127
+    d16 = O.bits_to_f64("f16", O.f32_to_f16_bits(d32.astype(np.float32)))
+    bound = d32 / 2 * (1 + 1e-6) + 127 * np.abs(d16 - d32)
+    assert np.all(np.abs(wb - v.reshape(16, 16, 32)) <= bound)
+
+
+# ---------------------------------------------------------------- routing and apply_experts
+
+
+def test_route_is_stable_counting_sort():
+    g = np.random.default_rng(12)
+    ids = g.integers(-2, 9, size=300)
+    offsets, perm = O.route(ids, 7)
+    pairs = sorted([(int(i), p) for p, i in enumerate(ids) if 0 <= i < 7])
+    assert list(perm) == [p for _, p in pairs]
+    for e in range(7):
+        assert offsets[e + 1] - offsets[e] == int(np.sum(ids == e))
+    assert offsets[0] == 0 and offsets[-1] == len(pairs)
+
+
+def test_apply_experts_rows_and_out_of_range_zero():
+    e, n, k = 4, 6, 64
+    W = np.stack([O.affine_dequant_f32(*O.affine_quantize(synth.weights_f32(40 + j, n, k), 4, 32, "bf16"), 4, 32, "bf16", k) for j in range(e)])
+    x = O.bits_to_f64("bf16", synth.acts_bits(41, 5, k, "bf16"))
+    ids = np.array([[0, 3], [1, -1], [4, 2], [2, 2], [3, 0]])
+    y = O.apply_experts(W, ids.reshape(-1), x, pos_per_row=2)
+    for p, i in enumerate(ids.reshape(-1)):
+        if 0 <= i < e:
+            ref = np.array([math.fsum(x[p // 2, kk] * float(W[i, r, kk]) for kk in range(k)) for r in range(n)])
+            np.testing.assert_allclose(y[p], ref, rtol=1e-12, atol=1e-15)
+        else:
+            assert np.all(y[p] == 0)
+
+
+def test_rel_l2_tolerance_helper():
+    ref = np.array([[3.0, 4.0], [0.0, 0.0]])
+    y = np.array([[3.0, 4.0 + 5e-3], [0.0, 0.0]])
+    np.testing.assert_allclose(O.rel_l2_per_row(y, ref), [1e-3, 0.0])
