@@ -1,0 +1,331 @@
+"""Benchmark of the weight-only quantized linear path on one MI355X.
+
+Headline (`value`): decode GEMV weight GB/s of one decode step of a Qwen3-0.6B-shaped model
+(28 layers x {q,k,v,o,gate,up,down} + lm_head = 197 projections, 595,984,384 weights, 4-bit
+g64 affine with bf16 scales/biases, bf16 activations, batch 1): one step = one problem-list
+launch over all 197 projections.  Weights are resident in HBM; three distinct weight copies
+are used in rotation so that a repeat never finds the previous step's weights in the 256 MB
+Infinity Cache.  Other legs in the same JSON line: 8-bit decode at batch 1 and 8, the prefill
+GEMM of a 9B-class layer (M=2048), routed experts (32 x 5760x2880, 512 tokens, top-4) in MXFP4
+and Q8_0, and the quantizer.  `roofline` is the decode kernel's achieved HBM GB/s (algorithmic
+bytes / average kernel time measured with HIP events on the launch stream) against 8 TB/s;
+`cpu_baseline` times the NumPy oracle on a bounded sample of the same decode workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-legs] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "qlinear GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s, 4-bit g64"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--no-legs", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path runs on a single "
+              "MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import synth
+    import weight_only_quantized_affine_amd as q
+
+    q.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    def gen(seed):
+        return torch.Generator(device=dev).manual_seed(seed)
+
+    # ------------------------------------------------------------ decode workload
+    def build_decode(bits, m, copies, seed_base):
+        """`copies` independent weight sets of the 197 projections, GPU-quantized."""
+        sets = []
+        wbytes = 0
+        for c in range(copies):
+            probs = []
+            for i, (name, k, n) in enumerate(synth.QWEN3_0_6B_DECODE):
+                w = torch.randn((n, k), generator=gen(seed_base + 1000 * c + i), device=dev) * 0.02
+                pk, sc, bi = q.qlinear_quantize(w, bits, 64, torch.bfloat16)
+                del w
+                x = torch.randn((m, k), generator=gen(seed_base + 500000 + 1000 * c + i), device=dev).to(torch.bfloat16)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                probs.append(dict(x=x, packed=pk, scales=sc, biases=bi, y=y, bits=bits, group_size=64))
+                if c == 0:
+                    wbytes += pk.numel() * 4 + sc.numel() * 2 + bi.numel() * 2
+            ws = torch.empty(q.qlinear_gemv_batched_workspace_size(len(probs)), dtype=torch.uint8, device=dev)
+            kw = dict(x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.bfloat16, workspace=ws)
+            q.qlinear_gemv_batched(probs, upload=True, **kw)  # uploads the problem table once
+            sets.append((probs, kw))
+        torch.cuda.synchronize()
+        io_bytes = sum(p["x"].numel() * 2 + p["y"].numel() * 2 for p in sets[0][0])
+        return sets, wbytes, io_bytes
+
+    def time_decode(sets, steps, warmup):
+        for i in range(warmup):
+            probs, kw = sets[i % len(sets)]
+            q.qlinear_gemv_batched(probs, upload=False, **kw)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            probs, kw = sets[i % len(sets)]
+            ev[i][0].record(stream)
+            q.qlinear_gemv_batched(probs, upload=False, **kw)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kms = [a.elapsed_time(b) for a, b in ev]
+        return wall, kms
+
+    log("building the 4-bit decode workload (3 weight copies)")
+    sets4, wbytes4, io4 = build_decode(4, 1, args.copies, 20_000)
+    log(f"weights per step {wbytes4} B; timing {args.steps} steps after {args.warmup} warmup")
+    wall, kms = time_decode(sets4, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    value = wbytes4 * args.steps / wall / 1e9
+    kern_ms = sorted(kms)
+    avg_ms = sum(kms) / len(kms)
+    achieved = (wbytes4 + io4) / (avg_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u4-affine-g64 x bf16 -> f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights quantized on the GPU, N(0,1) bf16 activations)",
+        "config": {
+            "workload": "qwen3-0.6b-shaped decode step: 197 GEMVs (28 layers x q,k,v,o,gate,up,down + lm_head), "
+                        "batch 1, 4-bit affine g64, bf16 scales/biases, bf16 in/out, one problem-list launch",
+            "weights_bytes_per_step": wbytes4,
+            "weights": 595984384,
+            "weight_copies_rotated": args.copies,
+            "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+            "kernel_ms": {"avg": round(avg_ms, 5), "min": round(kern_ms[0], 5),
+                          "median": round(kern_ms[len(kern_ms) // 2], 5), "max": round(kern_ms[-1], 5)},
+            "tokens_per_s_gemv_only": round(1e3 / avg_ms, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "gemv_kernel<1,4,bf16,bf16> (one launch per step)",
+            "bytes_per_launch": wbytes4 + io4,
+        },
+    }
+    del sets4
+    torch.cuda.empty_cache()
+
+    legs = {}
+    if not args.no_legs:
+        legs = run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode)
+    result["legs"] = legs
+    if "prefill_gemm_9b_layer" in legs:
+        result["prefill_gemm_tflops"] = legs["prefill_gemm_9b_layer"]["tflops"]
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+def _time_launches(fn, reps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
+
+
+def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
+    legs = {}
+    # ---------------- 8-bit decode, batch 1 and 8
+    for m in (1, 8):
+        log(f"leg: 8-bit decode m={m}")
+        sets8, wb8, io8 = build_decode(8, m, 2, 30_000 + m)
+        wall, kms = time_decode(sets8, 10, 3)
+        avg = sum(kms) / len(kms)
+        legs[f"decode_8bit_m{m}"] = {
+            "weight_gbs": round(wb8 / (avg * 1e-3) / 1e9, 2),
+            "kernel_ms": round(avg, 5),
+            "pct_hbm_peak": round(100 * (wb8 + io8) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "weights_bytes": wb8,
+        }
+        del sets8
+        torch.cuda.empty_cache()
+
+    # ---------------- prefill GEMM, 9B-class layer at M = 2048
+    log("leg: prefill GEMM 9B layer, M=2048")
+    m = 2048
+    per = {}
+    tot_flop = 0.0
+    tot_ms = 0.0
+    for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
+        w = torch.randn((n, k), generator=gen(40_000 + i), device=dev) * 0.02
+        pk, sc, bi = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
+        del w
+        x = torch.randn((m, k), generator=gen(41_000 + i), device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(q.qlinear_gemm_workspace_size(m, k, 64), dtype=torch.uint8, device=dev)
+        avg, med = _time_launches(
+            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 10, 3, stream)
+        flop = 2.0 * m * n * k
+        per[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+        tot_flop += flop
+        tot_ms += avg
+        del pk, sc, bi, x, y, ws
+    torch.cuda.empty_cache()
+    tflops = tot_flop / (tot_ms * 1e-3) / 1e12
+    legs["prefill_gemm_9b_layer"] = {
+        "tflops": round(tflops, 1),
+        "layer_ms": round(tot_ms, 4),
+        "gflop": round(tot_flop / 1e9, 1),
+        "prefill_tokens_per_s_per_layer": round(m / (tot_ms * 1e-3), 0),
+        "per_projection": per,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_kernel<4,64,bf16,bf16> + xsum pre-pass"},
+    }
+
+    # ---------------- routed experts, MXFP4 and Q8_0
+    cfg = synth.EXPERTS_32x5760x2880
+    e, n, k, tokens, top = cfg["e"], cfg["n"], cfg["k"], cfg["tokens"], cfg["top"]
+    ids = torch.from_numpy(synth.topk_ids(synth.seed_for(5, part=2), tokens, top, e).reshape(-1)).to(dev)
+    x = torch.randn((tokens, k), generator=gen(50_000), device=dev).to(torch.bfloat16)
+    y = torch.empty((tokens * top, n), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(q.qlinear_apply_experts_workspace_size(tokens * top, e), dtype=torch.uint8, device=dev)
+    flop = 2.0 * tokens * top * n * k
+    for fmt, fname in ((q.QL_MXFP4, "mxfp4"), (q.QL_Q8_0, "q8_0")):
+        log(f"leg: experts {fname}")
+        copies = []
+        for c in range(3):
+            if fmt == q.QL_MXFP4:
+                codes = torch.randint(0, 256, (e, n, k // 2), generator=gen(51_000 + c), device=dev,
+                                      dtype=torch.int32).to(torch.uint8)
+                scales = torch.randint(118, 131, (e, n, k // 32), generator=gen(52_000 + c), device=dev,
+                                       dtype=torch.int32).to(torch.uint8)
+                copies.append((codes, scales))
+                wb = codes.numel() + scales.numel()
+            else:
+                nb = k // 32
+                d = torch.exp2(torch.empty((e, n, nb), device=dev).uniform_(-14, -9, generator=gen(53_000 + c)))
+                d = d.to(torch.float16).view(torch.uint8).view(e, n, nb, 2)
+                qv = torch.randint(-127, 128, (e, n, nb, 32), generator=gen(54_000 + c), device=dev,
+                                   dtype=torch.int32).to(torch.int8).view(torch.uint8)
+                blocks = torch.cat([d, qv], dim=3).reshape(e, n, nb * 34).contiguous()
+                copies.append((blocks, None))
+                wb = blocks.numel()
+        avg, med = _time_launches(
+            lambda i: q.qlinear_apply_experts(fmt, copies[i % 3][0], copies[i % 3][1], ids, x, n=n, k=k,
+                                              pos_per_row=top, y=y, workspace=ws), 12, 3, stream)
+        byts = wb + x.numel() * 2 + y.numel() * 2
+        gbs = byts / (avg * 1e-3) / 1e9
+        legs[f"experts_{fname}"] = {
+            "ms": round(avg, 4),
+            "gbs": round(gbs, 1),
+            "tflops": round(flop / (avg * 1e-3) / 1e12, 1),
+            "weights_bytes": wb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": f"route + experts_kernel<{fname}>"},
+        }
+        del copies
+        torch.cuda.empty_cache()
+
+    # ---------------- quantizer on the lm_head-sized matrix (151936 x 1024)
+    log("leg: quantize")
+    w = torch.randn((151936, 1024), generator=gen(60_000), device=dev) * 0.02
+    pk = torch.empty((151936, 128), dtype=torch.int32, device=dev)
+    sc = torch.empty((151936, 16), dtype=torch.bfloat16, device=dev)
+    bi = torch.empty_like(sc)
+    avg, _ = _time_launches(lambda _i: q.qlinear_quantize(w, 4, 64, torch.bfloat16, pk, sc, bi), 10, 2, stream)
+    byts = w.numel() * 4 + pk.numel() * 4 + sc.numel() * 4
+    legs["quantize_4bit_g64_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                             "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    out = torch.empty((151936, 1024), dtype=torch.bfloat16, device=dev)
+    avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_AFFINE, pk, sc, bi, rows=151936, k=1024, bits=4,
+                                                         group_size=64, out=out), 10, 2, stream)
+    byts = out.numel() * 2 + pk.numel() * 4 + sc.numel() * 4
+    legs["dequant_4bit_g64_151936x1024_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1)}
+    return legs
+
+
+def cpu_baseline():
+    """The NumPy oracle (unpack + fp64 dequant + matmul) on a bounded sample of the decode workload:
+    layers 0-1 (14 projections) and the first 16384 rows of the lm_head, batch 1."""
+    import numpy as np
+
+    import oracle as O
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    log("cpu baseline: oracle on layers 0-1 + 16384 lm_head rows")
+    items = [(k, n) for (_, k, n) in synth.QWEN3_0_6B_DECODE[:14]] + [(1024, 16384)]
+    prepared = []
+    for i, (k, n) in enumerate(items):
+        w = synth.weights_f32(900 + i, n, k)
+        pk, sb, bb = O.affine_quantize(w, 4, 64, "bf16")
+        xb = synth.acts_bits(950 + i, 1, k, "bf16")
+        prepared.append((pk, sb, bb, O.bits_to_f64("bf16", xb), k, n))
+    wbytes = sum(pk.nbytes + sb.nbytes + bb.nbytes for (pk, sb, bb, _, _, _) in prepared)
+    t0 = time.perf_counter()
+    for (pk, sb, bb, x, k, n) in prepared:
+        D = O.affine_dequant_f32(pk, sb, bb, 4, 64, "bf16", k)
+        O.apply(x, D)
+    dt = time.perf_counter() - t0
+    return {"value": round(wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"layers 0-1 (14 projections) + lm_head rows 0..16383 of the qwen3-0.6b-shaped decode step, "
+                      f"batch 1, 4-bit g64 bf16: {wbytes} weight bytes in {dt:.2f} s (unpack + fp64 dequant + "
+                      f"matmul; dequant single-threaded, matmul on {threads} BLAS threads)",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * qlinear.h - C ABI of the weight-only quantized linear library for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (cited by page title and section):
+ *   - MLX affine storage: packed uint32 codes plus one scale and one ADDITIVE bias per group of
+ *     k-values, value = code*scale + bias (GPTQModel wiki "MLX Apple Silicon", Concepts table;
+ *     tinygpt PRD "Quantized inference ... QuantizedLinear", Problem; gguf2mlx-stream, section 01).
+ *   - Packing: whole codes per uint32 for 4 and 8 bits, code c of a word at bits
+ *     [bits*c, bits*(c+1)), ascending along k; scales/biases laid out [out, groups]
+ *     (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact transcoding).
+ *   - dequant / apply / apply_experts and the MXFP4 and Q8_0 block formats
+ *     (Nx_quant API docs, Weights and Products).
+ *
+ * Conventions for every entry point:
+ *   - W is [n, k]: n outputs by k inputs, quantized along k.  x is [m, k], y is [m, n], row-major,
+ *     contiguous.  Integer sizes are element counts.
+ *   - Every pointer except the host problem list of qlinear_gemv_batched is DEVICE memory on the
+ *     current HIP device, owned by the caller.  The library allocates nothing and keeps no state
+ *     between calls (no decoded or dense weight cache).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are asynchronous on it; none
+ *     synchronizes.  Results are deterministic: the same inputs give the same bits.
+ *   - Validation is host-only and runs before any launch.  On error the call returns a status,
+ *     launches nothing, and qlinear_last_error() names the offending argument.
+ *   - Zero-size outputs (m == 0 or n == 0) return QL_OK without a launch.
+ *   - Alignment (QL_ERR_ALIGN otherwise): w, packed words, x, MXFP4 codes, dequant outputs and
+ *     workspaces 16-byte aligned; scales, biases, layer_bias and Q8_0 blocks 2-byte aligned;
+ *     y aligned to its element size; ids 8-byte, offsets/perm 4-byte aligned.
+ */
+#ifndef QLINEAR_H
+#define QLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QL_OK = 0,
+  QL_ERR_NULL = 1,        /* a required pointer is NULL */
+  QL_ERR_SHAPE = 2,       /* a size is negative or the shapes do not agree */
+  QL_ERR_DTYPE = 3,       /* a dtype outside the supported table */
+  QL_ERR_ALIGN = 4,       /* a pointer is not aligned as required */
+  QL_ERR_UNSUPPORTED = 5, /* bits / group_size / format not supported */
+  QL_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the *_workspace_size query */
+  QL_ERR_LAUNCH = 7       /* the HIP runtime rejected a launch or copy */
+} ql_status;
+
+typedef enum { QL_F32 = 0, QL_F16 = 1, QL_BF16 = 2 } ql_dtype;
+typedef enum { QL_AFFINE = 0, QL_MXFP4 = 1, QL_Q8_0 = 2 } ql_format;
+
+/* One GEMV of a problem list: y[m,n] = x[m,k] . dequant(W[n,k])^T (+ layer_bias[n]).
+ * All pointers are device memory; layer_bias may be NULL. */
+typedef struct {
+  const void* x;
+  const uint32_t* packed;
+  const void* scales;
+  const void* biases;
+  const void* layer_bias;
+  void* y;
+  int64_t m, n, k;
+  int32_t bits, group_size;
+} ql_problem;
+
+/* Affine group quantizer (the step that produces the affine storage; gguf2mlx-stream section 01
+ * and the MLX affine storage of the GPTQModel wiki Concepts table).
+ * w [n,k] fp32 -> packed [n, k*bits/32] uint32, scales and biases [n, k/group_size] in
+ * param_dtype (QL_F16 or QL_BF16).  Per (row, group): mn/mx = min/max in fp32 under the total
+ * order (-0 < +0); scale = RNE(fl32(mx - mn) / (2^bits - 1)); bias = RNE(mn);
+ * code = clamp(round-half-even(fl32(v - bias) / scale), 0, 2^bits - 1), 0 where scale == 0.
+ * IEEE fp32 arithmetic, correctly rounded division.  w must be finite (otherwise the
+ * outputs are unspecified).  bits in {4, 8}; group_size in {32, 64, 128} dividing k; k % 32 == 0. */
+ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size,
+                           ql_dtype param_dtype, uint32_t* packed, void* scales, void* biases,
+                           void* stream);
+
+/* dequant (Nx_quant Products, dequant): every value of W as a float32 value, rounded once to
+ * out_dtype (QL_F32, QL_F16 or QL_BF16).  out is [rows, k].
+ *   QL_AFFINE: w0 = packed [rows, k*bits/32], w1 = scales, w2 = biases [rows, k/group_size] in
+ *              param_dtype; value = fl32(code*scale + bias).
+ *   QL_MXFP4:  w0 = codes [rows, k/2] (value 2i in byte i's low nibble, 2i+1 in its high one),
+ *              w1 = E8M0 scale bytes [rows, k/32]; value = e2m1(code) * 2^(s-127), NaN for
+ *              s == 255, -0 for code 8 (Nx_quant Weights, Mxfp4).  bits/group_size/param_dtype
+ *              are ignored; w2 must be NULL.
+ *   QL_Q8_0:   w0 = blocks [rows, k/32*34] (little-endian fp16 d, then 32 int8), value = d*q
+ *              (Nx_quant Weights, Q8_0).  w1 and w2 must be NULL.
+ * For MXFP4 and Q8_0, `rows` may count the rows of a whole expert stack ([e*n]). */
+ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const void* w2,
+                          ql_dtype param_dtype, int64_t rows, int64_t k, int bits,
+                          int group_size, void* out, ql_dtype out_dtype, void* stream);
+
+/* Decode GEMV (Nx_quant Products, apply; GPTQModel wiki "MLX Apple Silicon", Executing MLX
+ * qlinear kernels: FP32 accumulation, output in the activation dtype):
+ * y[m,n] = RNE_y( sum_k x[m,k]*(code*scale + bias) [+ layer_bias[n]] ), summed in fp32 straight
+ * from the packed words (no stored decoded weight).  Built for small m (1..8); any m >= 0 works
+ * (m > 8 runs in slices of 8).  x_dtype in {QL_F16, QL_BF16}; layer_bias (nullable) has x_dtype;
+ * y_dtype in {QL_F32, QL_F16, QL_BF16}.  bits in {4, 8}; group_size in {32, 64, 128}. */
+ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
+                       const uint32_t* packed, const void* scales, const void* biases,
+                       ql_dtype param_dtype, int64_t n, int bits, int group_size,
+                       const void* layer_bias, void* y, ql_dtype y_dtype, void* stream);
+
+/* Prefill GEMM: the same product as qlinear_gemv, for large m, on the matrix cores.  The codes
+ * enter the bf16 MFMA as exact small integers and each group's scale is applied to that group's
+ * fp32 partial sum (the block-scaled contraction of Nx_quant Products, apply); the additive
+ * bias enters through the per-group sums of x.  Needs a device workspace of
+ * qlinear_gemm_workspace_size(m, k, group_size) bytes (16-byte aligned), overwritten by the call. */
+size_t qlinear_gemm_workspace_size(int64_t m, int64_t k, int group_size);
+ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
+                       const uint32_t* packed, const void* scales, const void* biases,
+                       ql_dtype param_dtype, int64_t n, int bits, int group_size,
+                       const void* layer_bias, void* y, ql_dtype y_dtype, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
+ * 1/2/4/8, bits); bits and group_size may differ between problems.  `probs` is HOST memory
+ * (count entries), validated on the host like qlinear_gemv; the device table built from it is
+ * written to `workspace` (device, qlinear_gemv_batched_workspace_size(count) bytes).
+ * upload != 0 copies the table host-to-device on `stream` and waits for that copy (the only
+ * synchronizing call of the library); upload == 0 reuses the table an earlier call with the
+ * SAME list left in the same workspace (the caller guarantees it is unchanged), so only the
+ * launches are enqueued.  The dtypes are shared by the whole list. */
+size_t qlinear_gemv_batched_workspace_size(int count);
+ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dtype,
+                               ql_dtype param_dtype, ql_dtype y_dtype, void* workspace,
+                               size_t ws_bytes, int upload, void* stream);
+
+/* Routing (Nx_quant Products, apply_experts): group positions p of ids[n_pos] (int64) by expert.
+ * offsets[e+1] (int32) gets the exclusive prefix of the per-expert counts; perm[n_pos] (int32)
+ * gets, expert by expert, the positions with that id in increasing p (a stable counting sort);
+ * ids outside [0, e) are dropped and perm[offsets[e] .. n_pos) is left unwritten.
+ * Requires e <= 4096 and n_pos < 2^31. */
+ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets,
+                        int32_t* perm, void* stream);
+
+/* Routed apply (Nx_quant Products, apply_experts): for each position p of ids[n_pos],
+ * y[p, :] = RNE_y( x[p / pos_per_row, :] . W_{ids[p]}^T ) summed in fp32, or zeros when
+ * ids[p] is not in [0, e).  A row's bits do not depend on the other positions' experts.
+ *   QL_MXFP4: w0 = codes [e, n, k/2], w1 = scales [e, n, k/32].
+ *   QL_Q8_0:  w0 = blocks [e, n, k/32*34], w1 = NULL.
+ * x is [n_pos / pos_per_row, k] (pos_per_row divides n_pos; a token's top-k slots share its row);
+ * x_dtype must be QL_BF16 (MXFP4 values are exact in bf16, and so are int8 codes); y is
+ * [n_pos, n] in y_dtype.  k % 32 == 0; 0 <= e <= 4096.  Needs a workspace of
+ * qlinear_apply_experts_workspace_size(n_pos, e) bytes (routing scratch: offsets then perm,
+ * as qlinear_route writes them). */
+size_t qlinear_apply_experts_workspace_size(int64_t n_pos, int64_t e);
+ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, int64_t e,
+                                int64_t n, int64_t k, const int64_t* ids, int64_t n_pos,
+                                const void* x, ql_dtype x_dtype, int64_t pos_per_row, void* y,
+                                ql_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/* Message of the last failing call on this thread ("" after a successful call). */
+const char* qlinear_last_error(void);
+/* Library version string. */
+const char* qlinear_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLINEAR_H */

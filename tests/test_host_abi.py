@@ -1,0 +1,166 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments on the host before any launch (no compute call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import weight_only_quantized_affine_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlinear.h")
+
+QL_OK, QL_ERR_NULL, QL_ERR_SHAPE, QL_ERR_DTYPE, QL_ERR_ALIGN, QL_ERR_UNSUPPORTED, QL_ERR_WORKSPACE = range(7)
+F32, F16, BF16 = 0, 1, 2
+FAKE = 0x100000  # a 16-byte aligned non-NULL address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(q.lib_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return q.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^;(]*?\b(qlinear_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ["qlinear_quantize", "qlinear_dequant", "qlinear_gemv", "qlinear_gemm", "qlinear_gemv_batched",
+                 "qlinear_route", "qlinear_apply_experts", "qlinear_last_error"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_library_exports_no_torch_types():
+    # the boundary is plain C: no C++ mangled names among the qlinear_ symbols
+    out = os.popen(f"nm -D --defined-only {q.lib_path()}").read()
+    syms = [ln.split()[-1] for ln in out.splitlines() if ln.strip()]
+    assert all(not s.startswith("_Z") for s in syms if "qlinear" in s)
+    assert set(_declared()) <= set(syms)
+
+
+def _err(lib):
+    return lib.qlinear_last_error().decode()
+
+
+def test_quantize_rejects_bad_arguments(lib):
+    assert lib.qlinear_quantize(None, 4, 64, 4, 64, BF16, None, None, None, None) == QL_ERR_NULL
+    assert "must not be NULL" in _err(lib)
+    assert lib.qlinear_quantize(FAKE, 4, 64, 3, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
+    assert "bits=3" in _err(lib)
+    assert lib.qlinear_quantize(FAKE, 4, 64, 4, 48, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_quantize(FAKE, 4, 96, 4, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_SHAPE
+    assert lib.qlinear_quantize(FAKE, 4, 48, 4, 32, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_SHAPE  # k % 32
+    assert lib.qlinear_quantize(FAKE, -1, 64, 4, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_SHAPE
+    assert lib.qlinear_quantize(FAKE, 4, 64, 4, 64, F32, FAKE, FAKE, FAKE, None) == QL_ERR_DTYPE
+    assert lib.qlinear_quantize(FAKE + 4, 4, 64, 4, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_ALIGN
+    assert lib.qlinear_quantize(FAKE, 4, 64, 4, 64, BF16, FAKE, FAKE + 1, FAKE, None) == QL_ERR_ALIGN
+    # zero-size: OK without a launch
+    assert lib.qlinear_quantize(None, 0, 64, 4, 64, BF16, None, None, None, None) == QL_OK
+    assert _err(lib) == ""
+
+
+def test_dequant_rejects_bad_arguments(lib):
+    assert lib.qlinear_dequant(7, FAKE, FAKE, FAKE, BF16, 4, 64, 4, 64, FAKE, F32, None) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_dequant(0, FAKE, FAKE, None, BF16, 4, 64, 4, 64, FAKE, F32, None) == QL_ERR_NULL
+    assert lib.qlinear_dequant(0, FAKE, FAKE, FAKE, BF16, 4, 64, 4, 64, FAKE, 9, None) == QL_ERR_DTYPE
+    assert lib.qlinear_dequant(1, FAKE, FAKE, FAKE, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE  # w2 set
+    assert lib.qlinear_dequant(1, FAKE, FAKE, None, BF16, 4, 48, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
+    assert lib.qlinear_dequant(1, FAKE + 8, FAKE, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_ALIGN
+    assert lib.qlinear_dequant(2, FAKE, FAKE, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE  # w1 set
+    assert lib.qlinear_dequant(2, FAKE + 1, None, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_ALIGN
+    assert lib.qlinear_dequant(2, None, None, None, BF16, 0, 64, 0, 0, None, F32, None) == QL_OK
+
+
+def _gemv_args(**kw):
+    a = dict(x=FAKE, xdt=BF16, m=1, k=1024, packed=FAKE, scales=FAKE, biases=FAKE, pdt=BF16, n=256, bits=4, g=64,
+             lb=None, y=FAKE, ydt=F32, s=None)
+    a.update(kw)
+    return [a[k] for k in ["x", "xdt", "m", "k", "packed", "scales", "biases", "pdt", "n", "bits", "g", "lb", "y",
+                           "ydt", "s"]]
+
+
+def test_gemv_rejects_bad_arguments(lib):
+    assert lib.qlinear_gemv(*_gemv_args(x=None)) == QL_ERR_NULL
+    assert lib.qlinear_gemv(*_gemv_args(xdt=F32)) == QL_ERR_DTYPE
+    assert lib.qlinear_gemv(*_gemv_args(ydt=5)) == QL_ERR_DTYPE
+    assert lib.qlinear_gemv(*_gemv_args(bits=2)) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_gemv(*_gemv_args(k=1000)) == QL_ERR_SHAPE
+    assert lib.qlinear_gemv(*_gemv_args(m=-2)) == QL_ERR_SHAPE
+    assert lib.qlinear_gemv(*_gemv_args(x=FAKE + 2)) == QL_ERR_ALIGN
+    assert lib.qlinear_gemv(*_gemv_args(packed=FAKE + 4)) == QL_ERR_ALIGN
+    assert lib.qlinear_gemv(*_gemv_args(ydt=F32, y=FAKE + 2)) == QL_ERR_ALIGN
+    assert lib.qlinear_gemv(*_gemv_args(m=0, x=None, y=None)) == QL_OK
+    assert lib.qlinear_gemv(*_gemv_args(n=0, x=None, y=None, packed=None)) == QL_OK
+
+
+def test_gemm_rejects_missing_or_small_workspace(lib):
+    need = lib.qlinear_gemm_workspace_size(2048, 4096, 64)
+    assert need == 2048 * 64 * 4
+    args = _gemv_args(m=2048, k=4096, n=4096)
+    assert lib.qlinear_gemm(*args[:-1], None, 0, None) == QL_ERR_WORKSPACE
+    assert lib.qlinear_gemm(*args[:-1], FAKE, need - 1, None) == QL_ERR_WORKSPACE
+    assert "smaller" in _err(lib)
+    assert lib.qlinear_gemm(*args[:-1], FAKE + 4, need, None) == QL_ERR_ALIGN
+    assert lib.qlinear_gemm(*_gemv_args(bits=5)[:-1], FAKE, need, None) == QL_ERR_UNSUPPORTED
+
+
+def test_gemv_batched_validates_every_problem(lib):
+    P = q._Problem
+    good = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1024, 4, 64)
+    bad = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1000, 4, 64)
+    arr = (P * 2)(good, bad)
+    need = lib.qlinear_gemv_batched_workspace_size(2)
+    assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_SHAPE
+    assert "problem 1" in _err(lib)
+    big_m = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 9, 256, 1024, 4, 64)
+    arr = (P * 2)(good, big_m)
+    assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_UNSUPPORTED
+    arr = (P * 2)(good, good)
+    assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need - 1, 1, None) == QL_ERR_WORKSPACE
+    assert lib.qlinear_gemv_batched(arr, 0, BF16, BF16, F32, None, 0, 1, None) == QL_OK
+
+
+def test_route_and_experts_reject_bad_arguments(lib):
+    assert lib.qlinear_route(FAKE, 16, 0, FAKE, FAKE, None) == QL_ERR_SHAPE
+    assert lib.qlinear_route(FAKE, 16, 5000, FAKE, FAKE, None) == QL_ERR_SHAPE
+    assert lib.qlinear_route(FAKE + 4, 16, 4, FAKE, FAKE, None) == QL_ERR_ALIGN
+    assert lib.qlinear_route(FAKE, 16, 4, None, FAKE, None) == QL_ERR_NULL
+    ws = lib.qlinear_apply_experts_workspace_size(2048, 32)
+    assert ws >= 33 * 4 + 2048 * 4
+    base = [1, FAKE, FAKE, 32, 5760, 2880, FAKE, 2048, FAKE, BF16, 4, FAKE, BF16, FAKE, ws, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["fmt", "w0", "w1", "e", "n", "k", "ids", "n_pos", "x", "xdt", "ppr", "y", "ydt", "ws", "wsb", "s"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return lib.qlinear_apply_experts(*a)
+
+    assert call(fmt=0) == QL_ERR_UNSUPPORTED
+    assert call(xdt=F16) == QL_ERR_DTYPE
+    assert call(k=2881) == QL_ERR_SHAPE
+    assert call(ppr=3) == QL_ERR_SHAPE
+    assert call(wsb=ws - 1) == QL_ERR_WORKSPACE
+    assert call(w1=None) == QL_ERR_NULL
+    assert call(fmt=2) == QL_ERR_SHAPE  # Q8_0 takes no w1
+    assert call(fmt=2, w1=None, w0=FAKE + 1) == QL_ERR_ALIGN
+    assert call(n_pos=0) == QL_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(q, "_LIB", None)
+    monkeypatch.setattr(q, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        q.load_library()

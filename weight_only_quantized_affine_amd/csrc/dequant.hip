@@ -1,0 +1,150 @@
+// dequant (Nx_quant API docs, Products: dequant): every weight as its float32 value, rounded
+// once to the output dtype.  Affine: value = fl32(code*scale + bias) (GPTQModel wiki "MLX Apple
+// Silicon", Concepts).  MXFP4: e2m1 code * 2^(s-127) (Nx_quant Weights, Mxfp4).  Q8_0: d*q
+// (Nx_quant Weights, Q8_0).  Elementwise and HBM-bound: each lane turns one 16-byte chunk of
+// packed data (or one 34-byte Q8_0 block) into its values and writes them out contiguously.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ql {
+namespace {
+
+__device__ __forceinline__ void store8(void* out, int64_t i0, const float* v, int odt) {
+  if (odt == DT_F32) {
+    f32x4_t a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    *(f32x4_t*)((float*)out + i0) = a;
+    *(f32x4_t*)((float*)out + i0 + 4) = b;
+  } else {
+    uint32_t h[8];
+    if (odt == DT_BF16) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = f32_to_bf16_bits(v[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = f32_to_f16_bits(v[j]);
+    }
+    u32x4_t p = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+    *(u32x4_t*)((uint16_t*)out + i0) = p;
+  }
+}
+
+template <int BITS, typename PT>
+__global__ __launch_bounds__(256) void dequant_affine_kernel(const uint32_t* __restrict__ packed,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases, int64_t rows,
+                                                             int64_t k, int g, void* __restrict__ out, int odt) {
+  constexpr int PER = 128 / BITS;  // values per 16-byte chunk
+  const int64_t chunks_per_row = k / PER;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * chunks_per_row) return;
+  const int64_t row = t / chunks_per_row;
+  const int64_t c = t - row * chunks_per_row;
+  const int64_t k0 = c * PER;
+  const int64_t gi = row * (k / g) + k0 / g;  // a chunk never straddles a group (g >= 32)
+  const float s = param_to_f32<PT>(scales[gi]);
+  const float b = param_to_f32<PT>(biases[gi]);
+  u32x4_t w = load16(packed + row * (k * BITS / 32) + c * 4);
+  float v[PER];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 32 / BITS; ++i) {
+      uint32_t q = (w[j] >> (BITS * i)) & ((1u << BITS) - 1);
+      v[j * (32 / BITS) + i] = __builtin_fmaf((float)q, s, b);  // q*s is exact: one rounding
+    }
+  }
+  const int64_t o = row * k + k0;
+#pragma unroll
+  for (int j = 0; j < PER / 8; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
+}
+
+// 2^(s-127) as an fp32 value (s = 0 gives the subnormal 2^-127); s == 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  if (s == 0) return __uint_as_float(0x00400000u);
+  if (s == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(s << 23);
+}
+
+__global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales, int64_t rows,
+                                                            int64_t k, void* __restrict__ out, int odt) {
+  // Twice the e2m1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 (OCP Microscaling Formats, named by the
+  // Nx_quant page) as 4-bit fields of one word, indexed by the code's low three bits.
+  const uint32_t twice_mag = 0xC8643210u;
+  const int64_t blocks_per_row = k / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * blocks_per_row) return;
+  const int64_t row = t / blocks_per_row;
+  const int64_t blk = t - row * blocks_per_row;
+  const float half_p2 = 0.5f * e8m0_to_f32(scales[row * blocks_per_row + blk]);  // exact
+  u32x4_t w = load16(codes + row * (k / 2) + blk * 16);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t c = (w[j] >> (4 * i)) & 15u;  // value 2m in byte m's low nibble, 2m+1 in its high one
+      float m = (float)((twice_mag >> (4 * (c & 7u))) & 15u) * half_p2;  // exact, inf past fp32, or NaN
+      v[j * 8 + i] = __uint_as_float(__float_as_uint(m) | ((c & 8u) << 28));
+    }
+  }
+  const int64_t o = row * k + blk * 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
+}
+
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t rows,
+                                                           int64_t k, void* __restrict__ out, int odt) {
+  const int64_t blocks_per_row = k / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * blocks_per_row) return;
+  // 34-byte blocks are 2-byte aligned: read 17 half-words.
+  const uint16_t* bp = (const uint16_t*)(blocks + t * 34);
+  const float d = f16_bits_to_f32(bp[0]);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    uint32_t h = bp[1 + j];
+    v[2 * j] = d * (float)(int8_t)(h & 0xffu);
+    v[2 * j + 1] = d * (float)(int8_t)(h >> 8);
+  }
+  const int64_t row = t / blocks_per_row;
+  const int64_t blk = t - row * blocks_per_row;
+  const int64_t o = row * k + blk * 32;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
+}
+
+}  // namespace
+
+hipError_t launch_dequant_affine(const uint32_t* packed, const void* scales, const void* biases, int pdt,
+                                 int64_t rows, int64_t k, int bits, int g, void* out, int odt, hipStream_t s) {
+  const int64_t total = rows * (k * bits / 128);
+  const unsigned nb = (unsigned)((total + 255) / 256);
+  const uint16_t* sc = (const uint16_t*)scales;
+  const uint16_t* bi = (const uint16_t*)biases;
+  if (bits == 4 && pdt == DT_BF16)
+    dequant_affine_kernel<4, BF16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+  else if (bits == 4)
+    dequant_affine_kernel<4, F16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+  else if (pdt == DT_BF16)
+    dequant_affine_kernel<8, BF16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+  else
+    dequant_affine_kernel<8, F16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, void* out,
+                                int odt, hipStream_t s) {
+  const int64_t total = rows * (k / 32);
+  dequant_mxfp4_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(codes, scales, rows, k, out, odt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt, hipStream_t s) {
+  const int64_t total = rows * (k / 32);
+  dequant_q8_0_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(blocks, rows, k, out, odt);
+  return hipGetLastError();
+}
+
+}  // namespace ql

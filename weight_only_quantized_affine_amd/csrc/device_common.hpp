@@ -1,0 +1,73 @@
+// Device-side helpers shared by the gfx950 kernels: 16-bit float storage conversions, output
+// stores and small vector types.  Everything here is plain HIP for CDNA4 (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ql {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+
+// dtype codes (same values as ql_dtype in qlinear.h)
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+struct BF16 {};  // tag: bfloat16 storage
+struct F16 {};   // tag: IEEE binary16 storage
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Round fp32 to bfloat16, nearest with ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// Round fp32 to binary16 (the hardware conversion rounds to nearest even).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <typename T> __device__ __forceinline__ float param_to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float param_to_f32<BF16>(uint32_t b) { return bf16_bits_to_f32(b); }
+template <> __device__ __forceinline__ float param_to_f32<F16>(uint32_t b) { return f16_bits_to_f32(b); }
+
+template <typename T> __device__ __forceinline__ uint32_t f32_to_bits(float f);
+template <> __device__ __forceinline__ uint32_t f32_to_bits<BF16>(float f) { return f32_to_bf16_bits(f); }
+template <> __device__ __forceinline__ uint32_t f32_to_bits<F16>(float f) { return f32_to_f16_bits(f); }
+
+// Store one fp32 result rounded once to the output dtype.
+__device__ __forceinline__ void store_out(void* y, int64_t i, float v, int dt) {
+  if (dt == DT_F32) {
+    ((float*)y)[i] = v;
+  } else if (dt == DT_BF16) {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+  } else {
+    ((uint16_t*)y)[i] = (uint16_t)f32_to_f16_bits(v);
+  }
+}
+
+// 2-wide dot products with fp32 accumulation (v_dot2c_f32_bf16 / v_dot2c_f32_f16).
+__device__ __forceinline__ float dot2(BF16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+__device__ __forceinline__ float dot2(F16, uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) { return *(const u32x4_t*)p; }
+
+}  // namespace ql

@@ -1,0 +1,368 @@
+// C ABI of the library (declared in include/qlinear.h): host-side validation, then dispatch
+// to the gfx950 kernels.  Validation touches no device state, so every error path is testable
+// without a GPU; on error nothing is launched and qlinear_last_error() names the argument.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/qlinear.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ql_status fail(ql_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+ql_status ok() {
+  g_last_error.clear();
+  return QL_OK;
+}
+ql_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(QL_ERR_LAUNCH, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool is16(ql_dtype d) { return d == QL_F16 || d == QL_BF16; }
+bool is_out(ql_dtype d) { return d == QL_F32 || d == QL_F16 || d == QL_BF16; }
+size_t esize(ql_dtype d) { return d == QL_F32 ? 4 : 2; }
+
+#define CHECK(cond, st, ...)          \
+  do {                                \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+// Shared checks of the affine layout: bits, group size, k.
+ql_status check_affine(const char* fn, int64_t n, int64_t k, int bits, int g, ql_dtype pdt) {
+  CHECK(n >= 0 && k >= 0, QL_ERR_SHAPE, "%s: n=%lld and k=%lld must be >= 0", fn, (long long)n, (long long)k);
+  CHECK(bits == 4 || bits == 8, QL_ERR_UNSUPPORTED, "%s: bits=%d not supported (4 or 8)", fn, bits);
+  CHECK(g == 32 || g == 64 || g == 128, QL_ERR_UNSUPPORTED, "%s: group_size=%d not supported (32, 64 or 128)", fn,
+        g);
+  CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+  CHECK(k % g == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of group_size=%d", fn, (long long)k, g);
+  CHECK(is16(pdt), QL_ERR_DTYPE, "%s: param_dtype must be QL_F16 or QL_BF16", fn);
+  return QL_OK;
+}
+
+ql_status check_product(const char* fn, const void* x, ql_dtype xdt, int64_t m, int64_t k, const uint32_t* packed,
+                        const void* scales, const void* biases, ql_dtype pdt, int64_t n, int bits, int g,
+                        const void* layer_bias, const void* y, ql_dtype ydt) {
+  CHECK(m >= 0, QL_ERR_SHAPE, "%s: m=%lld must be >= 0", fn, (long long)m);
+  ql_status st = check_affine(fn, n, k, bits, g, pdt);
+  if (st != QL_OK) return st;
+  CHECK(is16(xdt), QL_ERR_DTYPE, "%s: x_dtype must be QL_F16 or QL_BF16", fn);
+  CHECK(is_out(ydt), QL_ERR_DTYPE, "%s: y_dtype must be QL_F32, QL_F16 or QL_BF16", fn);
+  if (m == 0 || n == 0) return QL_OK;
+  CHECK(x && y, QL_ERR_NULL, "%s: x and y must not be NULL", fn);
+  if (k > 0) CHECK(packed && scales && biases, QL_ERR_NULL, "%s: packed, scales and biases must not be NULL", fn);
+  CHECK(aligned(x, 16), QL_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+  CHECK(aligned(packed, 16), QL_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+  CHECK(aligned(scales, 2) && aligned(biases, 2), QL_ERR_ALIGN, "%s: scales and biases must be 2-byte aligned", fn);
+  CHECK(aligned(layer_bias, 2), QL_ERR_ALIGN, "%s: layer_bias must be 2-byte aligned", fn);
+  CHECK(aligned(y, esize(ydt)), QL_ERR_ALIGN, "%s: y must be aligned to its element size", fn);
+  return QL_OK;
+}
+
+int dt(ql_dtype d) { return (int)d; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qlinear_last_error(void) { return g_last_error.c_str(); }
+const char* qlinear_version(void) { return "qlinear-gfx950 0.1"; }
+
+ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size, ql_dtype param_dtype,
+                           uint32_t* packed, void* scales, void* biases, void* stream) {
+  const char* fn = "qlinear_quantize";
+  ql_status st = check_affine(fn, n, k, bits, group_size, param_dtype);
+  if (st != QL_OK) return st;
+  if (n == 0 || k == 0) return ok();
+  CHECK(w && packed && scales && biases, QL_ERR_NULL, "%s: w, packed, scales and biases must not be NULL", fn);
+  CHECK(aligned(w, 16), QL_ERR_ALIGN, "%s: w must be 16-byte aligned", fn);
+  CHECK(aligned(packed, 16), QL_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+  CHECK(aligned(scales, 2) && aligned(biases, 2), QL_ERR_ALIGN, "%s: scales and biases must be 2-byte aligned", fn);
+  return launched(ql::launch_quantize(w, n, k, bits, group_size, dt(param_dtype), packed, scales, biases,
+                                      (hipStream_t)stream),
+                  fn);
+}
+
+ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const void* w2, ql_dtype param_dtype,
+                          int64_t rows, int64_t k, int bits, int group_size, void* out, ql_dtype out_dtype,
+                          void* stream) {
+  const char* fn = "qlinear_dequant";
+  CHECK(is_out(out_dtype), QL_ERR_DTYPE, "%s: out_dtype must be QL_F32, QL_F16 or QL_BF16", fn);
+  CHECK(rows >= 0 && k >= 0, QL_ERR_SHAPE, "%s: rows and k must be >= 0", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (fmt == QL_AFFINE) {
+    ql_status st = check_affine(fn, rows, k, bits, group_size, param_dtype);
+    if (st != QL_OK) return st;
+    if (rows == 0 || k == 0) return ok();
+    CHECK(w0 && w1 && w2 && out, QL_ERR_NULL, "%s: packed (w0), scales (w1), biases (w2) and out must not be NULL", fn);
+    CHECK(aligned(w0, 16), QL_ERR_ALIGN, "%s: packed (w0) must be 16-byte aligned", fn);
+    CHECK(aligned(w1, 2) && aligned(w2, 2), QL_ERR_ALIGN, "%s: scales and biases must be 2-byte aligned", fn);
+    CHECK(aligned(out, 16), QL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+    return launched(ql::launch_dequant_affine((const uint32_t*)w0, w1, w2, dt(param_dtype), rows, k, bits,
+                                              group_size, out, dt(out_dtype), s),
+                    fn);
+  }
+  if (fmt == QL_MXFP4 || fmt == QL_Q8_0) {
+    CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+    CHECK(w2 == nullptr, QL_ERR_SHAPE, "%s: w2 must be NULL for block formats", fn);
+    if (rows == 0 || k == 0) return ok();
+    CHECK(w0 && out, QL_ERR_NULL, "%s: w0 and out must not be NULL", fn);
+    CHECK(aligned(out, 16), QL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+    if (fmt == QL_MXFP4) {
+      CHECK(w1 != nullptr, QL_ERR_NULL, "%s: MXFP4 scales (w1) must not be NULL", fn);
+      CHECK(aligned(w0, 16), QL_ERR_ALIGN, "%s: MXFP4 codes (w0) must be 16-byte aligned", fn);
+      return launched(ql::launch_dequant_mxfp4((const uint8_t*)w0, (const uint8_t*)w1, rows, k, out, dt(out_dtype), s),
+                      fn);
+    }
+    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0", fn);
+    CHECK(aligned(w0, 2), QL_ERR_ALIGN, "%s: Q8_0 blocks (w0) must be 2-byte aligned", fn);
+    return launched(ql::launch_dequant_q8_0((const uint8_t*)w0, rows, k, out, dt(out_dtype), s), fn);
+  }
+  return fail(QL_ERR_UNSUPPORTED, "%s: unknown format %d", fn, (int)fmt);
+}
+
+ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, const uint32_t* packed,
+                       const void* scales, const void* biases, ql_dtype param_dtype, int64_t n, int bits,
+                       int group_size, const void* layer_bias, void* y, ql_dtype y_dtype, void* stream) {
+  const char* fn = "qlinear_gemv";
+  ql_status st = check_product(fn, x, x_dtype, m, k, packed, scales, biases, param_dtype, n, bits, group_size,
+                               layer_bias, y, y_dtype);
+  if (st != QL_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  for (int64_t m0 = 0; m0 < m; m0 += 8) {
+    const int64_t mm = std::min<int64_t>(8, m - m0);
+    ql::GemvDesc d;
+    d.x = (const uint8_t*)x + m0 * k * 2;
+    d.packed = packed;
+    d.scales = scales;
+    d.biases = biases;
+    d.layer_bias = layer_bias;
+    d.y = (uint8_t*)y + m0 * n * esize(y_dtype);
+    d.m = mm;
+    d.n = n;
+    d.k = k;
+    d.bits = bits;
+    d.group_size = group_size;
+    const ql::GemvGeom g = ql::gemv_geometry(k, bits, ql::gemv_mt(mm));
+    const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
+    hipError_t e = ql::launch_gemv(d, nullptr, nullptr, 0, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype),
+                                   dt(y_dtype), (hipStream_t)stream);
+    if (e != hipSuccess) return launched(e, fn);
+  }
+  return ok();
+}
+
+size_t qlinear_gemm_workspace_size(int64_t m, int64_t k, int group_size) {
+  if (m <= 0 || k <= 0 || group_size <= 0) return 0;
+  return ql::gemm_workspace_bytes(m, k, group_size);
+}
+
+ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, const uint32_t* packed,
+                       const void* scales, const void* biases, ql_dtype param_dtype, int64_t n, int bits,
+                       int group_size, const void* layer_bias, void* y, ql_dtype y_dtype, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  const char* fn = "qlinear_gemm";
+  ql_status st = check_product(fn, x, x_dtype, m, k, packed, scales, biases, param_dtype, n, bits, group_size,
+                               layer_bias, y, y_dtype);
+  if (st != QL_OK) return st;
+  if (m == 0 || n == 0) return ok();
+  if (k == 0)  // no codes to read: the GEMV path writes the bias (or zeros)
+    return qlinear_gemv(x, x_dtype, m, k, packed, scales, biases, param_dtype, n, bits, group_size, layer_bias, y,
+                        y_dtype, stream);
+  const size_t need = qlinear_gemm_workspace_size(m, k, group_size);
+  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
+  CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
+        need);
+  CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return launched(ql::launch_gemm(x, dt(x_dtype), m, k, packed, scales, biases, dt(param_dtype), n, bits, group_size,
+                                  layer_bias, y, dt(y_dtype), workspace, (hipStream_t)stream),
+                  fn);
+}
+
+size_t qlinear_gemv_batched_workspace_size(int count) {
+  if (count <= 0) return 0;
+  return (size_t)count * sizeof(ql::GemvDesc) + (size_t)(2 * count + 1) * sizeof(int64_t) + 64;
+}
+
+ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dtype, ql_dtype param_dtype,
+                               ql_dtype y_dtype, void* workspace, size_t ws_bytes, int upload, void* stream) {
+  const char* fn = "qlinear_gemv_batched";
+  CHECK(count >= 0, QL_ERR_SHAPE, "%s: count=%d must be >= 0", fn, count);
+  if (count == 0) return ok();
+  CHECK(probs != nullptr, QL_ERR_NULL, "%s: probs must not be NULL", fn);
+  for (int i = 0; i < count; ++i) {
+    const ql_problem& p = probs[i];
+    char name[64];
+    snprintf(name, sizeof(name), "%s: problem %d", fn, i);
+    ql_status st = check_product(name, p.x, x_dtype, p.m, p.k, p.packed, p.scales, p.biases, param_dtype, p.n, p.bits,
+                                 p.group_size, p.layer_bias, p.y, y_dtype);
+    if (st != QL_OK) return st;
+    CHECK(p.m <= 8, QL_ERR_UNSUPPORTED, "%s: problem %d has m=%lld > 8 (use qlinear_gemv or qlinear_gemm)", fn, i,
+          (long long)p.m);
+  }
+  const size_t need = qlinear_gemv_batched_workspace_size(count);
+  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
+  CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
+        need);
+  CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+
+  // Classes of problems sharing (m template, bits): one launch each.  The device table holds
+  // the descs ordered by class, then per class its tile prefix (class_count + 1 entries).
+  std::vector<int> order;
+  order.reserve(count);
+  for (int i = 0; i < count; ++i)
+    if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
+  auto key = [&](int i) { return ql::gemv_mt(probs[i].m) * 16 + probs[i].bits; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key(a) < key(b); });
+  const int live = (int)order.size();
+  if (live == 0) return ok();
+
+  std::vector<ql::GemvDesc> descs(live);
+  std::vector<int64_t> starts;
+  starts.reserve(2 * count + 1);
+  struct Cls {
+    int first, count, m, bits;
+    size_t start_off;
+    int64_t tiles;
+  };
+  std::vector<Cls> classes;
+  for (int j = 0; j < live;) {
+    int e = j;
+    while (e < live && key(order[e]) == key(order[j])) ++e;
+    Cls c;
+    c.first = j;
+    c.count = e - j;
+    c.m = (int)probs[order[j]].m;
+    c.bits = probs[order[j]].bits;
+    c.start_off = starts.size();
+    int64_t t = 0;
+    int mmax = 0;
+    for (int q = j; q < e; ++q) {
+      const ql_problem& p = probs[order[q]];
+      ql::GemvDesc& d = descs[q];
+      d.x = p.x;
+      d.packed = p.packed;
+      d.scales = p.scales;
+      d.biases = p.biases;
+      d.layer_bias = p.layer_bias;
+      d.y = p.y;
+      d.m = p.m;
+      d.n = p.n;
+      d.k = p.k;
+      d.bits = p.bits;
+      d.group_size = p.group_size;
+      mmax = std::max<int>(mmax, (int)p.m);
+      starts.push_back(t);
+      const ql::GemvGeom g = ql::gemv_geometry(p.k, p.bits, ql::gemv_mt(p.m));
+      t += (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
+    }
+    starts.push_back(t);
+    c.m = mmax;
+    c.tiles = t;
+    classes.push_back(c);
+    j = e;
+  }
+
+  uint8_t* ws = (uint8_t*)workspace;
+  ql::GemvDesc* d_descs = (ql::GemvDesc*)ws;
+  int64_t* d_starts = (int64_t*)(ws + (((size_t)live * sizeof(ql::GemvDesc) + 15) & ~(size_t)15));
+  hipStream_t s = (hipStream_t)stream;
+  if (upload) {
+    std::vector<uint8_t> host((uint8_t*)d_starts - ws + starts.size() * sizeof(int64_t));
+    memcpy(host.data(), descs.data(), descs.size() * sizeof(ql::GemvDesc));
+    memcpy(host.data() + ((uint8_t*)d_starts - ws), starts.data(), starts.size() * sizeof(int64_t));
+    hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return launched(e, fn);
+    e = hipStreamSynchronize(s);  // the staging vector is released on return
+    if (e != hipSuccess) return launched(e, fn);
+  }
+  for (const Cls& c : classes) {
+    ql::GemvDesc none{};
+    hipError_t e = ql::launch_gemv(none, d_descs + c.first, d_starts + c.start_off, c.count, c.tiles, c.m, c.bits,
+                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), s);
+    if (e != hipSuccess) return launched(e, fn);
+  }
+  return ok();
+}
+
+ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm,
+                        void* stream) {
+  const char* fn = "qlinear_route";
+  CHECK(n_pos >= 0 && n_pos < (int64_t(1) << 31), QL_ERR_SHAPE, "%s: n_pos=%lld must be in [0, 2^31)", fn,
+        (long long)n_pos);
+  CHECK(e >= 1 && e <= 4096, QL_ERR_SHAPE, "%s: e=%lld must be in [1, 4096]", fn, (long long)e);
+  CHECK(offsets != nullptr, QL_ERR_NULL, "%s: offsets must not be NULL", fn);
+  CHECK(n_pos == 0 || (ids && perm), QL_ERR_NULL, "%s: ids and perm must not be NULL", fn);
+  CHECK(aligned(ids, 8) && aligned(offsets, 4) && aligned(perm, 4), QL_ERR_ALIGN,
+        "%s: ids must be 8-byte and offsets/perm 4-byte aligned", fn);
+  return launched(ql::launch_route(ids, n_pos, e, offsets, perm, (hipStream_t)stream), fn);
+}
+
+size_t qlinear_apply_experts_workspace_size(int64_t n_pos, int64_t e) {
+  if (n_pos < 0 || e < 0) return 0;
+  return (size_t)(((e + 1) * 4 + 15) / 16 * 16) + (size_t)n_pos * 4;
+}
+
+ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
+                                const int64_t* ids, int64_t n_pos, const void* x, ql_dtype x_dtype,
+                                int64_t pos_per_row, void* y, ql_dtype y_dtype, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  const char* fn = "qlinear_apply_experts";
+  CHECK(fmt == QL_MXFP4 || fmt == QL_Q8_0, QL_ERR_UNSUPPORTED, "%s: format must be QL_MXFP4 or QL_Q8_0", fn);
+  CHECK(e >= 0 && e <= 4096, QL_ERR_SHAPE, "%s: e=%lld must be in [0, 4096]", fn, (long long)e);
+  CHECK(n >= 0 && k >= 0 && n_pos >= 0 && n_pos < (int64_t(1) << 31), QL_ERR_SHAPE,
+        "%s: n, k must be >= 0 and n_pos in [0, 2^31)", fn);
+  CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+  CHECK(pos_per_row >= 1 && n_pos % pos_per_row == 0, QL_ERR_SHAPE,
+        "%s: pos_per_row=%lld must be >= 1 and divide n_pos=%lld", fn, (long long)pos_per_row, (long long)n_pos);
+  CHECK(x_dtype == QL_BF16, QL_ERR_DTYPE, "%s: x_dtype must be QL_BF16", fn);
+  CHECK(is_out(y_dtype), QL_ERR_DTYPE, "%s: y_dtype must be QL_F32, QL_F16 or QL_BF16", fn);
+  if (n_pos == 0 || n == 0) return ok();
+  CHECK(ids && y, QL_ERR_NULL, "%s: ids and y must not be NULL", fn);
+  CHECK(aligned(ids, 8), QL_ERR_ALIGN, "%s: ids must be 8-byte aligned", fn);
+  CHECK(aligned(y, esize(y_dtype)), QL_ERR_ALIGN, "%s: y must be aligned to its element size", fn);
+  hipStream_t s = (hipStream_t)stream;
+  if (e == 0) {  // every position is out of range: zeros
+    hipError_t err = ql::launch_apply_experts((int)fmt, nullptr, nullptr, 0, n, 0, ids, n_pos, nullptr, 0,
+                                              pos_per_row, y, dt(y_dtype), nullptr, nullptr, s);
+    return launched(err, fn);
+  }
+  CHECK(w0 && x, QL_ERR_NULL, "%s: w0 and x must not be NULL", fn);
+  CHECK(aligned(x, 16), QL_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
+  if (fmt == QL_MXFP4) {
+    CHECK(w1 != nullptr, QL_ERR_NULL, "%s: MXFP4 scales (w1) must not be NULL", fn);
+    CHECK(aligned(w0, 16), QL_ERR_ALIGN, "%s: MXFP4 codes (w0) must be 16-byte aligned", fn);
+  } else {
+    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0", fn);
+    CHECK(aligned(w0, 2), QL_ERR_ALIGN, "%s: Q8_0 blocks (w0) must be 2-byte aligned", fn);
+  }
+  const size_t need = qlinear_apply_experts_workspace_size(n_pos, e);
+  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
+  CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
+        need);
+  CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  int32_t* offsets = (int32_t*)workspace;
+  int32_t* perm = (int32_t*)((uint8_t*)workspace + ((e + 1) * 4 + 15) / 16 * 16);
+  return launched(ql::launch_apply_experts((int)fmt, w0, w1, e, n, k, ids, n_pos, x, dt(x_dtype), pos_per_row, y,
+                                           dt(y_dtype), offsets, perm, s),
+                  fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Affine group quantize + pack (MLX affine storage: code*scale + additive bias, codes packed
+// low bits first into uint32 words, scales/biases [n, k/g]; GPTQModel wiki "MLX Apple
+// Silicon", Concepts and Packed layouts; gguf2mlx-stream section 01).
+//
+// One lane owns 8 consecutive weights of a row: one packed word at 4 bits, two at 8 bits.
+// The g/8 lanes of a group are consecutive in the wave, so the group min/max is a butterfly
+// over g/8 lanes.  HBM traffic per weight: 4 B read, bits/8 B + 4/g B written.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace ql {
+namespace {
+
+// Monotone integer key of an fp32 value under the IEEE total order (-0 < +0).
+__device__ __forceinline__ int32_t order_key(float f) {
+  int32_t i = __float_as_int(f);
+  return i ^ ((i >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float from_order_key(int32_t i) { return __int_as_float(i ^ ((i >> 31) & 0x7fffffff)); }
+
+template <int BITS, typename PT>
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ w, int64_t n, int64_t k, int g,
+                                                       uint32_t* __restrict__ packed, uint16_t* __restrict__ scales,
+                                                       uint16_t* __restrict__ biases) {
+  const int64_t lanes_per_row = k >> 3;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = n * lanes_per_row;
+  // Lanes past the end still take part in the shuffles (their group is wholly past the end
+  // because totals are multiples of g/8), they only skip loads and stores.
+  const bool live = t < total;
+  const int64_t tt = live ? t : total - 1;
+  const int64_t row = tt / lanes_per_row;
+  const int64_t c8 = tt - row * lanes_per_row;
+  const float* src = w + row * k + c8 * 8;
+  f32x4_t a = *(const f32x4_t*)src;
+  f32x4_t b = *(const f32x4_t*)(src + 4);
+  float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  int32_t kmin = order_key(v[0]), kmax = kmin;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    int32_t key = order_key(v[i]);
+    kmin = min(kmin, key);
+    kmax = max(kmax, key);
+  }
+  const int lpg = g >> 3;  // lanes per group: 4, 8 or 16
+  for (int off = 1; off < lpg; off <<= 1) {
+    kmin = min(kmin, __shfl_xor(kmin, off));
+    kmax = max(kmax, __shfl_xor(kmax, off));
+  }
+  const float mn = from_order_key(kmin);
+  const float mx = from_order_key(kmax);
+  const float levels = (float)((1 << BITS) - 1);
+  const float s32 = __fdiv_rn(mx - mn, levels);
+  const uint32_t sbits = f32_to_bits<PT>(s32);
+  const uint32_t bbits = f32_to_bits<PT>(mn);
+  const float s = param_to_f32<PT>(sbits);
+  const float bb = param_to_f32<PT>(bbits);
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float tq = __fdiv_rn(v[i] - bb, s);
+    float r = __builtin_rintf(tq);
+    r = r > levels ? levels : r;
+    r = r > 0.0f ? r : 0.0f;  // also maps NaN to 0
+    q[i] = (s == 0.0f) ? 0u : (uint32_t)r;
+  }
+  if (!live) return;
+  if (BITS == 4) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= q[i] << (4 * i);
+    packed[row * (k >> 3) + c8] = word;
+  } else {
+    uint32_t w0 = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    uint32_t w1 = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+    u32x2_t pr = {w0, w1};
+    *(u32x2_t*)(packed + row * (k >> 2) + c8 * 2) = pr;
+  }
+  if ((c8 & (lpg - 1)) == 0) {
+    const int64_t gi = row * (k / g) + (c8 * 8) / g;
+    scales[gi] = (uint16_t)sbits;
+    biases[gi] = (uint16_t)bbits;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* w, int64_t n, int64_t k, int bits, int g, int pdt, uint32_t* packed,
+                           void* scales, void* biases, hipStream_t s) {
+  const int64_t total = n * (k >> 3);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  uint16_t* sc = (uint16_t*)scales;
+  uint16_t* bi = (uint16_t*)biases;
+  if (bits == 4 && pdt == DT_BF16)
+    quantize_kernel<4, BF16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);
+  else if (bits == 4)
+    quantize_kernel<4, F16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);
+  else if (pdt == DT_BF16)
+    quantize_kernel<8, BF16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);
+  else
+    quantize_kernel<8, F16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);
+  return hipGetLastError();
+}
+
+}  // namespace ql
