@@ -115,13 +115,14 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
 
 /* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
  * 1/2/4/8, bits); bits and group_size may differ between problems.  `probs` is HOST memory
- * (count entries), validated on the host like qlinear_gemv; the device table built from it is
- * written to `workspace` (device, qlinear_gemv_batched_workspace_size(count) bytes).
+ * (count entries), validated on the host like qlinear_gemv; the device table built from it (the
+ * problems and their row tiles) is written to `workspace` (device memory of at least
+ * qlinear_gemv_batched_workspace_size(probs, count) bytes, which depends on the shapes).
  * upload != 0 copies the table host-to-device on `stream` and waits for that copy (the only
  * synchronizing call of the library); upload == 0 reuses the table an earlier call with the
  * SAME list left in the same workspace (the caller guarantees it is unchanged), so only the
  * launches are enqueued.  The dtypes are shared by the whole list. */
-size_t qlinear_gemv_batched_workspace_size(int count);
+size_t qlinear_gemv_batched_workspace_size(const ql_problem* probs, int count);
 ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dtype,
                                ql_dtype param_dtype, ql_dtype y_dtype, void* workspace,
                                size_t ws_bytes, int upload, void* stream);

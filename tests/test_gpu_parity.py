@@ -341,7 +341,7 @@ def test_gemv_batched_mixed_bits_small_list():
     probs4, checks4 = _decode_problems(4, 1, shapes, 70000)
     probs8, checks8 = _decode_problems(8, 1, shapes[:2], 71000)
     probs = probs4 + probs8
-    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(len(probs)), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(probs), dtype=torch.uint8, device=DEV)
     q.qlinear_gemv_batched(probs, x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.float32,
                            workspace=ws)
     _sync()
@@ -356,7 +356,7 @@ def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     reusing the uploaded table gives identical bits."""
     probs, checks = _decode_problems(bits, m, synth.QWEN3_0_6B_DECODE, synth.seed_for(2 if bits == 4 else 3),
                                      check_rows=4)
-    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(len(probs)), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(probs), dtype=torch.uint8, device=DEV)
     kw = dict(x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.float32, workspace=ws)
     q.qlinear_gemv_batched(probs, upload=True, **kw)
     _sync()
@@ -365,6 +365,31 @@ def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     _sync()
     assert all(torch.equal(a, p["y"]) for a, p in zip(first, probs))
     _verify_decode(checks, bits, f"qwen3-0.6b decode {bits}-bit m={m}")
+
+
+def test_gemv_batched_graph_replay_matches_eager():
+    """The decode step captured in a HIP graph and replayed 5 times (eager work in between)
+    gives the eager result bit for bit every time."""
+    shapes = synth.QWEN3_0_6B_LAYER + [("head", 1024, 8192)]
+    probs, _ = _decode_problems(4, 1, shapes, 72000)
+    for p in probs:
+        p["y"] = torch.empty(p["y"].shape, dtype=torch.bfloat16, device=DEV)
+    arr = q.qlinear_problem_list(probs)
+    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(arr), dtype=torch.uint8, device=DEV)
+    kw = dict(x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.bfloat16, workspace=ws)
+    q.qlinear_gemv_batched(arr, upload=True, **kw)
+    _sync()
+    eager = [p["y"].clone() for p in probs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlinear_gemv_batched(arr, upload=False, **kw)
+    for rep in range(5):
+        for p in probs:
+            p["y"].fill_(rep + 1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, p["y"]) for a, p in zip(eager, probs)), f"replay {rep}"
 
 
 # ============================================================ routing and routed experts

@@ -93,6 +93,7 @@ def _gemv_args(**kw):
 
 def test_gemv_rejects_bad_arguments(lib):
     assert lib.qlinear_gemv(*_gemv_args(x=None)) == QL_ERR_NULL
+    assert lib.qlinear_gemv(*_gemv_args(y=None)) == QL_ERR_NULL
     assert lib.qlinear_gemv(*_gemv_args(xdt=F32)) == QL_ERR_DTYPE
     assert lib.qlinear_gemv(*_gemv_args(ydt=5)) == QL_ERR_DTYPE
     assert lib.qlinear_gemv(*_gemv_args(bits=2)) == QL_ERR_UNSUPPORTED
@@ -121,7 +122,8 @@ def test_gemv_batched_validates_every_problem(lib):
     good = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1024, 4, 64)
     bad = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1000, 4, 64)
     arr = (P * 2)(good, bad)
-    need = lib.qlinear_gemv_batched_workspace_size(2)
+    need = lib.qlinear_gemv_batched_workspace_size((P * 2)(good, good), 2)
+    assert need > 2 * ctypes.sizeof(P)
     assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_SHAPE
     assert "problem 1" in _err(lib)
     big_m = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 9, 256, 1024, 4, 64)

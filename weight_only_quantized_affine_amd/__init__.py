@@ -26,6 +26,7 @@ __all__ = [
     "qlinear_gemm_workspace_size",
     "qlinear_gemv_batched",
     "qlinear_gemv_batched_workspace_size",
+    "qlinear_problem_list",
     "qlinear_route",
     "qlinear_apply_experts",
     "qlinear_apply_experts_workspace_size",
@@ -73,7 +74,7 @@ _SIGNATURES = {
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
-    "qlinear_gemv_batched_workspace_size": (_SZ, [_INT]),
+    "qlinear_gemv_batched_workspace_size": (_SZ, [ctypes.POINTER(_Problem), _INT]),
     "qlinear_gemv_batched": (_INT, [ctypes.POINTER(_Problem), _INT, _INT, _INT, _INT, _P, _SZ, _INT, _P]),
     "qlinear_route": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "qlinear_apply_experts_workspace_size": (_SZ, [_I64, _I64]),
@@ -201,19 +202,33 @@ def qlinear_gemm(x, packed, scales, biases, *, bits: int, group_size: int, layer
     return y
 
 
-def qlinear_gemv_batched_workspace_size(count: int) -> int:
-    return int(load_library().qlinear_gemv_batched_workspace_size(count))
+def qlinear_problem_list(problems):
+    """Marshal a list of GEMV problems (dicts with tensors x, packed, scales, biases, y, optional
+    layer_bias, and ints bits, group_size) into the C array qlinear_gemv_batched takes; pass the
+    result instead of the list to skip re-marshalling on every call."""
+    return _problem_array(problems)
+
+
+def _problem_array(problems):
+    if isinstance(problems, ctypes.Array):
+        return problems
+    arr = (_Problem * len(problems))()
+    for i, p in enumerate(problems):
+        x, packed, y = p["x"], p["packed"], p["y"]
+        arr[i] = _Problem(_ptr(x), _ptr(packed), _ptr(p["scales"]), _ptr(p["biases"]), _ptr(p.get("layer_bias")),
+                          _ptr(y), x.shape[0], packed.shape[0], x.shape[1], p["bits"], p["group_size"])
+    return arr
+
+
+def qlinear_gemv_batched_workspace_size(problems: Sequence[dict]) -> int:
+    return int(load_library().qlinear_gemv_batched_workspace_size(_problem_array(problems), len(problems)))
 
 
 def qlinear_gemv_batched(problems: Sequence[dict], *, x_dtype, param_dtype, y_dtype, workspace, upload: bool = True):
     """One launch (per class) over a list of GEMVs.  Each problem is a dict with tensors x, packed,
     scales, biases, y, optional layer_bias, and ints bits, group_size."""
     lib = load_library()
-    arr = (_Problem * len(problems))()
-    for i, p in enumerate(problems):
-        x, packed, y = p["x"], p["packed"], p["y"]
-        arr[i] = _Problem(_ptr(x), _ptr(packed), _ptr(p["scales"]), _ptr(p["biases"]), _ptr(p.get("layer_bias")),
-                          _ptr(y), x.shape[0], packed.shape[0], x.shape[1], p["bits"], p["group_size"])
+    arr = _problem_array(problems)
     _check(lib.qlinear_gemv_batched(arr, len(problems), _dt(x_dtype), _dt(param_dtype), _dt(y_dtype), _ptr(workspace),
                                     workspace.numel(), 1 if upload else 0, _stream()))
 

@@ -47,12 +47,14 @@ template <> __device__ __forceinline__ uint32_t f32_to_bits<F16>(float f) { retu
 
 // Store one fp32 result rounded once to the output dtype.
 __device__ __forceinline__ void store_out(void* y, int64_t i, float v, int dt) {
+  typedef __attribute__((address_space(1))) float gf32;
+  typedef __attribute__((address_space(1))) uint16_t gu16;
   if (dt == DT_F32) {
-    ((float*)y)[i] = v;
+    ((gf32*)y)[i] = v;
   } else if (dt == DT_BF16) {
-    ((uint16_t*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
+    ((gu16*)y)[i] = (uint16_t)f32_to_bf16_bits(v);
   } else {
-    ((uint16_t*)y)[i] = (uint16_t)f32_to_f16_bits(v);
+    ((gu16*)y)[i] = (uint16_t)f32_to_f16_bits(v);
   }
 }
 

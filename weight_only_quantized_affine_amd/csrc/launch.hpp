@@ -6,7 +6,7 @@
 
 namespace ql {
 
-// Device problem descriptor of one GEMV (mirrors ql_problem without the per-list constants).
+// Device problem descriptor of one GEMV (mirrors ql_problem plus the host-chosen batch count).
 struct GemvDesc {
   const void* x;
   const uint32_t* packed;
@@ -16,31 +16,48 @@ struct GemvDesc {
   void* y;
   int64_t m, n, k;
   int32_t bits, group_size;
+  int32_t batches;  // row batches per workgroup (see GemvGeom)
+  int32_t pad_;
+};
+// Tile of a problem list: problem index in the device table and tile index inside the problem.
+struct GemvTile {
+  int32_t prob;
+  int32_t local;
 };
 
 // GEMV work split: lanes_per_row lanes of a wave share a row, each streaming 16-byte chunks
-// of packed words; each lane keeps rows_per_lane rows in flight; rows_per_wg rows go to one
-// 256-thread (4-wave) workgroup.  Shared by the host (grid size) and the kernel.
+// of packed words and holding 4 rows; a 256-thread (4-wave) workgroup walks `batches` sets of
+// 4 * (64 / lanes_per_row) * 4 rows.  Shared by the host (grid, tiles) and the kernel.
 struct GemvGeom {
   int lanes_per_row;    // largest power of two <= 64 dividing the 16-byte chunks of a row
   int chunks_per_lane;  // chunks of a row / lanes_per_row
-  int rows_per_lane;
-  int rows_per_wg;      // 4 waves * (64 / lanes_per_row) * rows_per_lane
+  int batches;
+  int64_t rows_per_wg;  // 4 waves * (64 / lanes_per_row) * 4 rows * batches
 };
 // Template row count M_T (1, 2, 4 or 8) a GEMV of m rows runs with.
 __host__ __device__ inline int gemv_mt(int64_t m) { return m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8; }
-__host__ __device__ inline int gemv_rows_per_lane(int mt) { return mt <= 2 ? 4 : 2; }
-__host__ __device__ inline GemvGeom gemv_geometry(int64_t k, int bits, int mt) {
+__host__ __device__ inline GemvGeom gemv_geometry(int64_t k, int bits, int batches) {
   GemvGeom g;
   const int64_t chunks = k * bits / 128;
   int L = 64;
   while (L > 1 && (chunks % L) != 0) L >>= 1;
   g.lanes_per_row = L;
   g.chunks_per_lane = (int)(chunks / L);
-  g.rows_per_lane = gemv_rows_per_lane(mt);
-  g.rows_per_wg = 4 * (64 / L) * g.rows_per_lane;
+  g.batches = batches;
+  g.rows_per_wg = (int64_t)4 * (64 / L) * 4 * batches;
   return g;
 }
+// Host choice of the batch count: about 64 KiB of packed words per workgroup, fewer batches
+// when `min_tiles` workgroups would otherwise not be reached.
+inline int gemv_batches(int64_t n, int64_t k, int bits, int64_t min_tiles) {
+  const GemvGeom g1 = gemv_geometry(k, bits, 1);
+  const int64_t set_bytes = g1.rows_per_wg * (k * bits / 8);
+  int nb = set_bytes > 0 ? (int)((65536 + set_bytes / 2) / set_bytes) : 1;
+  nb = nb < 1 ? 1 : (nb > 8 ? 8 : nb);
+  while (nb > 1 && (n + g1.rows_per_wg * nb - 1) / (g1.rows_per_wg * nb) < min_tiles) --nb;
+  return nb;
+}
+size_t gemv_lds_bytes(int64_t k, int bits, int64_t m);  // 0 when x does not fit: x is read from HBM
 
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, int bits, int g, int pdt, uint32_t* packed,
                            void* scales, void* biases, hipStream_t s);
@@ -50,10 +67,10 @@ hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int
                                 int odt, hipStream_t s);
 hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt, hipStream_t s);
 
-// One GEMV (desc passed by value) or a device table of `count` descs with tile prefix
-// `tile_start[count+1]` (all descs of the table share m, bits and group size).
-hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const int64_t* tile_start, int count,
-                       int64_t total_tiles, int m, int bits, int xdt, int pdt, int ydt, hipStream_t s);
+// One GEMV (desc passed by value, table == NULL) or `grid` tiles of a device problem table
+// (all problems of one launch share the row-count template of m and bits).
+hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m,
+                       int bits, int xdt, int pdt, int ydt, size_t lds_bytes, hipStream_t s);
 
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,

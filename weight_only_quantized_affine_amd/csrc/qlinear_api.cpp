@@ -66,8 +66,9 @@ ql_status check_product(const char* fn, const void* x, ql_dtype xdt, int64_t m, 
   CHECK(is16(xdt), QL_ERR_DTYPE, "%s: x_dtype must be QL_F16 or QL_BF16", fn);
   CHECK(is_out(ydt), QL_ERR_DTYPE, "%s: y_dtype must be QL_F32, QL_F16 or QL_BF16", fn);
   if (m == 0 || n == 0) return QL_OK;
-  CHECK(x && y, QL_ERR_NULL, "%s: x and y must not be NULL", fn);
-  if (k > 0) CHECK(packed && scales && biases, QL_ERR_NULL, "%s: packed, scales and biases must not be NULL", fn);
+  CHECK(y != nullptr, QL_ERR_NULL, "%s: y must not be NULL", fn);
+  if (k > 0)
+    CHECK(x && packed && scales && biases, QL_ERR_NULL, "%s: x, packed, scales and biases must not be NULL", fn);
   CHECK(aligned(x, 16), QL_ERR_ALIGN, "%s: x must be 16-byte aligned", fn);
   CHECK(aligned(packed, 16), QL_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
   CHECK(aligned(scales, 2) && aligned(biases, 2), QL_ERR_ALIGN, "%s: scales and biases must be 2-byte aligned", fn);
@@ -146,9 +147,10 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
                                layer_bias, y, y_dtype);
   if (st != QL_OK) return st;
   if (m == 0 || n == 0) return ok();
+  CHECK(n * k * bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: packed weights of 2 GiB or more", fn);
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int64_t mm = std::min<int64_t>(8, m - m0);
-    ql::GemvDesc d;
+    ql::GemvDesc d{};
     d.x = (const uint8_t*)x + m0 * k * 2;
     d.packed = packed;
     d.scales = scales;
@@ -160,10 +162,11 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
     d.k = k;
     d.bits = bits;
     d.group_size = group_size;
-    const ql::GemvGeom g = ql::gemv_geometry(k, bits, ql::gemv_mt(mm));
+    d.batches = ql::gemv_batches(n, k, bits, 1024);
+    const ql::GemvGeom g = ql::gemv_geometry(k, bits, d.batches);
     const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
-    hipError_t e = ql::launch_gemv(d, nullptr, nullptr, 0, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype),
-                                   dt(y_dtype), (hipStream_t)stream);
+    hipError_t e = ql::launch_gemv(d, nullptr, nullptr, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype),
+                                   dt(y_dtype), ql::gemv_lds_bytes(k, bits, ql::gemv_mt(mm)), (hipStream_t)stream);
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
@@ -196,9 +199,75 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
                   fn);
 }
 
-size_t qlinear_gemv_batched_workspace_size(int count) {
-  if (count <= 0) return 0;
-  return (size_t)count * sizeof(ql::GemvDesc) + (size_t)(2 * count + 1) * sizeof(int64_t) + 64;
+namespace {
+// Device table of a problem list: descs (ordered by class), then the tiles of every class.
+struct BatchedPlan {
+  std::vector<ql::GemvDesc> descs;
+  std::vector<ql::GemvTile> tiles;
+  struct Cls {
+    int m, bits;
+    size_t first_tile, n_tiles, lds;
+  };
+  std::vector<Cls> classes;
+  size_t tiles_offset = 0, bytes = 0;
+};
+
+void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
+  std::vector<int> order;
+  for (int i = 0; i < count; ++i)
+    if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
+  auto key = [&](int i) { return ql::gemv_mt(probs[i].m) * 16 + probs[i].bits; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key(a) < key(b); });
+  const int live = (int)order.size();
+  plan.descs.resize(live);
+  for (int j = 0; j < live;) {
+    int e = j;
+    while (e < live && key(order[e]) == key(order[j])) ++e;
+    BatchedPlan::Cls c;
+    c.m = 0;
+    c.bits = probs[order[j]].bits;
+    c.first_tile = plan.tiles.size();
+    bool fits = true;
+    size_t lds = 0;
+    for (int q = j; q < e; ++q) {
+      const ql_problem& p = probs[order[q]];
+      ql::GemvDesc& d = plan.descs[q];
+      d = ql::GemvDesc{};
+      d.x = p.x;
+      d.packed = p.packed;
+      d.scales = p.scales;
+      d.biases = p.biases;
+      d.layer_bias = p.layer_bias;
+      d.y = p.y;
+      d.m = p.m;
+      d.n = p.n;
+      d.k = p.k;
+      d.bits = p.bits;
+      d.group_size = p.group_size;
+      d.batches = ql::gemv_batches(p.n, p.k, p.bits, 1);
+      c.m = std::max<int>(c.m, (int)p.m);
+      const size_t need = ql::gemv_lds_bytes(p.k, p.bits, ql::gemv_mt(p.m));
+      if (need == 0 && p.k > 0) fits = false;
+      lds = std::max(lds, need);
+      const ql::GemvGeom g = ql::gemv_geometry(p.k, p.bits, d.batches);
+      const int64_t t = (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
+      for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
+    }
+    c.n_tiles = plan.tiles.size() - c.first_tile;
+    c.lds = fits ? lds : 0;
+    plan.classes.push_back(c);
+    j = e;
+  }
+  plan.tiles_offset = (plan.descs.size() * sizeof(ql::GemvDesc) + 15) & ~(size_t)15;
+  plan.bytes = plan.tiles_offset + plan.tiles.size() * sizeof(ql::GemvTile);
+}
+}  // namespace
+
+size_t qlinear_gemv_batched_workspace_size(const ql_problem* probs, int count) {
+  if (count <= 0 || probs == nullptr) return 0;
+  BatchedPlan plan;
+  make_plan(probs, count, plan);
+  return plan.bytes;
 }
 
 ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dtype, ql_dtype param_dtype,
@@ -216,87 +285,33 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
     if (st != QL_OK) return st;
     CHECK(p.m <= 8, QL_ERR_UNSUPPORTED, "%s: problem %d has m=%lld > 8 (use qlinear_gemv or qlinear_gemm)", fn, i,
           (long long)p.m);
+    CHECK(p.n * p.k * p.bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+          "%s: problem %d has packed weights of 2 GiB or more", fn, i);
   }
-  const size_t need = qlinear_gemv_batched_workspace_size(count);
-  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
-  CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
-        need);
+  BatchedPlan plan;
+  make_plan(probs, count, plan);
+  if (plan.descs.empty()) return ok();
+  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, plan.bytes);
+  CHECK(ws_bytes >= plan.bytes, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+        ws_bytes, plan.bytes);
   CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
-
-  // Classes of problems sharing (m template, bits): one launch each.  The device table holds
-  // the descs ordered by class, then per class its tile prefix (class_count + 1 entries).
-  std::vector<int> order;
-  order.reserve(count);
-  for (int i = 0; i < count; ++i)
-    if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
-  auto key = [&](int i) { return ql::gemv_mt(probs[i].m) * 16 + probs[i].bits; };
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key(a) < key(b); });
-  const int live = (int)order.size();
-  if (live == 0) return ok();
-
-  std::vector<ql::GemvDesc> descs(live);
-  std::vector<int64_t> starts;
-  starts.reserve(2 * count + 1);
-  struct Cls {
-    int first, count, m, bits;
-    size_t start_off;
-    int64_t tiles;
-  };
-  std::vector<Cls> classes;
-  for (int j = 0; j < live;) {
-    int e = j;
-    while (e < live && key(order[e]) == key(order[j])) ++e;
-    Cls c;
-    c.first = j;
-    c.count = e - j;
-    c.m = (int)probs[order[j]].m;
-    c.bits = probs[order[j]].bits;
-    c.start_off = starts.size();
-    int64_t t = 0;
-    int mmax = 0;
-    for (int q = j; q < e; ++q) {
-      const ql_problem& p = probs[order[q]];
-      ql::GemvDesc& d = descs[q];
-      d.x = p.x;
-      d.packed = p.packed;
-      d.scales = p.scales;
-      d.biases = p.biases;
-      d.layer_bias = p.layer_bias;
-      d.y = p.y;
-      d.m = p.m;
-      d.n = p.n;
-      d.k = p.k;
-      d.bits = p.bits;
-      d.group_size = p.group_size;
-      mmax = std::max<int>(mmax, (int)p.m);
-      starts.push_back(t);
-      const ql::GemvGeom g = ql::gemv_geometry(p.k, p.bits, ql::gemv_mt(p.m));
-      t += (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
-    }
-    starts.push_back(t);
-    c.m = mmax;
-    c.tiles = t;
-    classes.push_back(c);
-    j = e;
-  }
-
   uint8_t* ws = (uint8_t*)workspace;
-  ql::GemvDesc* d_descs = (ql::GemvDesc*)ws;
-  int64_t* d_starts = (int64_t*)(ws + (((size_t)live * sizeof(ql::GemvDesc) + 15) & ~(size_t)15));
   hipStream_t s = (hipStream_t)stream;
   if (upload) {
-    std::vector<uint8_t> host((uint8_t*)d_starts - ws + starts.size() * sizeof(int64_t));
-    memcpy(host.data(), descs.data(), descs.size() * sizeof(ql::GemvDesc));
-    memcpy(host.data() + ((uint8_t*)d_starts - ws), starts.data(), starts.size() * sizeof(int64_t));
+    std::vector<uint8_t> host(plan.bytes);
+    memcpy(host.data(), plan.descs.data(), plan.descs.size() * sizeof(ql::GemvDesc));
+    memcpy(host.data() + plan.tiles_offset, plan.tiles.data(), plan.tiles.size() * sizeof(ql::GemvTile));
     hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return launched(e, fn);
     e = hipStreamSynchronize(s);  // the staging vector is released on return
     if (e != hipSuccess) return launched(e, fn);
   }
-  for (const Cls& c : classes) {
+  const ql::GemvDesc* d_descs = (const ql::GemvDesc*)ws;
+  const ql::GemvTile* d_tiles = (const ql::GemvTile*)(ws + plan.tiles_offset);
+  for (const BatchedPlan::Cls& c : plan.classes) {
     ql::GemvDesc none{};
-    hipError_t e = ql::launch_gemv(none, d_descs + c.first, d_starts + c.start_off, c.count, c.tiles, c.m, c.bits,
-                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), s);
+    hipError_t e = ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
+                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s);
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
