@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqlinear.so")
-SOURCES = ["qlinear_api.cpp", "quantize.hip", "dequant.hip", "gemv.hip", "gemm.hip", "experts.hip"]
+SOURCES = ["qlinear_api.cpp", "quantize.hip", "dequant.hip", "gemv.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip",
+           "gemv_m8.hip", "gemm.hip", "experts.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
@@ -34,14 +35,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+def build(verbose: bool = False, jobs: int = 8, extra_flags=(), out: str = LIB) -> str:
+    """Compile every source and link `out` (default lib/libqlinear.so); `extra_flags` are added
+    to each compile line (for example -D overrides of the launch tunables)."""
     hipcc = _hipcc()
-    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     with tempfile.TemporaryDirectory(prefix="qlinear_build_") as tmp:
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [hipcc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -53,13 +56,13 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
 
         with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
             objs = list(ex.map(compile_one, SOURCES))
-        out_tmp = LIB + ".tmp"
+        out_tmp = out + ".tmp"
         cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out_tmp]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
-        os.replace(out_tmp, LIB)
-    return LIB
+        os.replace(out_tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -165,8 +165,10 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
     d.batches = ql::gemv_batches(n, k, bits, 1024);
     const ql::GemvGeom g = ql::gemv_geometry(k, bits, d.batches);
     const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
+    const ql::GemvLds lds = ql::gemv_lds(k, bits, ql::gemv_mt(mm), d.batches);
     hipError_t e = ql::launch_gemv(d, nullptr, nullptr, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype),
-                                   dt(y_dtype), ql::gemv_lds_bytes(k, bits, ql::gemv_mt(mm)), (hipStream_t)stream);
+                                   dt(y_dtype), lds.bytes, lds.xlds, bits == 4 && group_size == 32,
+                                   (hipStream_t)stream);
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
@@ -205,7 +207,8 @@ struct BatchedPlan {
   std::vector<ql::GemvDesc> descs;
   std::vector<ql::GemvTile> tiles;
   struct Cls {
-    int m, bits;
+    int m, bits, xlds;
+    bool g2;
     size_t first_tile, n_tiles, lds;
   };
   std::vector<Cls> classes;
@@ -216,7 +219,10 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
   std::vector<int> order;
   for (int i = 0; i < count; ++i)
     if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
-  auto key = [&](int i) { return ql::gemv_mt(probs[i].m) * 16 + probs[i].bits; };
+  auto key = [&](int i) {
+    const bool g2 = probs[i].bits == 4 && probs[i].group_size == 32;
+    return ql::gemv_mt(probs[i].m) * 32 + probs[i].bits * 2 + (g2 ? 1 : 0);
+  };
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return key(a) < key(b); });
   const int live = (int)order.size();
   plan.descs.resize(live);
@@ -226,9 +232,10 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     BatchedPlan::Cls c;
     c.m = 0;
     c.bits = probs[order[j]].bits;
+    c.g2 = c.bits == 4 && probs[order[j]].group_size == 32;
     c.first_tile = plan.tiles.size();
     bool fits = true;
-    size_t lds = 0;
+    size_t lds_x = 0, lds_lb = 0;
     for (int q = j; q < e; ++q) {
       const ql_problem& p = probs[order[q]];
       ql::GemvDesc& d = plan.descs[q];
@@ -246,15 +253,17 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       d.group_size = p.group_size;
       d.batches = ql::gemv_batches(p.n, p.k, p.bits, 1);
       c.m = std::max<int>(c.m, (int)p.m);
-      const size_t need = ql::gemv_lds_bytes(p.k, p.bits, ql::gemv_mt(p.m));
-      if (need == 0 && p.k > 0) fits = false;
-      lds = std::max(lds, need);
+      const ql::GemvLds need = ql::gemv_lds(p.k, p.bits, ql::gemv_mt(p.m), d.batches);
       const ql::GemvGeom g = ql::gemv_geometry(p.k, p.bits, d.batches);
+      if (!need.xlds) fits = false;
+      lds_x = std::max(lds_x, need.bytes);
+      lds_lb = std::max(lds_lb, (size_t)g.rows_per_wg * 4);
       const int64_t t = (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
       for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
     }
     c.n_tiles = plan.tiles.size() - c.first_tile;
-    c.lds = fits ? lds : 0;
+    c.xlds = fits ? 1 : 0;
+    c.lds = fits ? lds_x : lds_lb;
     plan.classes.push_back(c);
     j = e;
   }
@@ -311,7 +320,7 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
   for (const BatchedPlan::Cls& c : plan.classes) {
     ql::GemvDesc none{};
     hipError_t e = ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
-                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s);
+                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, c.xlds, c.g2, s);
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
