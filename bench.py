@@ -49,7 +49,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path runs on a single "
-              "MI355X; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "MI355X; the product shards along its output rows with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
 

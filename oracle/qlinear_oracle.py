@@ -19,7 +19,7 @@ Sources (cited by page title and section):
   decode rule), ``quantize_q8_0``, and "Products" (``dequant``, ``apply``,
   ``apply_experts``).
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
 
 * quantizer: per (row, group of g along k): mn = min, mx = max over the group in fp32 (total
   order, -0 < +0); s32 = fl32(fl32(mx - mn) / (2^bits - 1)); stored s = RNE(s32), stored
