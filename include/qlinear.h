@@ -105,8 +105,12 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
  * enter the bf16 MFMA as exact small integers and each group's scale is applied to that group's
  * fp32 partial sum (the block-scaled contraction of Nx_quant Products, apply); the additive
  * bias enters through the per-group sums of x.  Needs a device workspace of
- * qlinear_gemm_workspace_size(m, k, group_size) bytes (16-byte aligned), overwritten by the call. */
-size_t qlinear_gemm_workspace_size(int64_t m, int64_t k, int group_size);
+ * qlinear_gemm_workspace_size(m, n, k, group_size) bytes (16-byte aligned), overwritten by the
+ * call: the per-group sums of x (m * k/group_size words), per-group records of the weight's
+ * scales and biases (n * k/group_size x 16 bytes), each padded to 256 bytes, then a copy of x
+ * (m * k 16-bit values) rearranged for the matrix-core operand order.  x and the packed words must
+ * each be smaller than 2 GiB (QL_ERR_UNSUPPORTED otherwise). */
+size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int group_size);
 ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        const uint32_t* packed, const void* scales, const void* biases,
                        ql_dtype param_dtype, int64_t n, int bits, int group_size,

@@ -26,6 +26,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
+# Matrix-core kernels keep their accumulators in the architectural VGPRs (the VALU reads them
+# every group to apply the scales; accumulation registers would need a move per element).
+FILE_FLAGS = {
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "experts.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -44,7 +50,7 @@ def build(verbose: bool = False, jobs: int = 8, extra_flags=(), out: str = LIB) 
         def compile_one(src: str) -> str:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".cpp") else []
-            cmd = [hipcc, *FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *FLAGS, *FILE_FLAGS.get(src, []), *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -90,7 +90,7 @@ hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const Gemv
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,
                        int ydt, void* ws, hipStream_t s);
-size_t gemm_workspace_bytes(int64_t m, int64_t k, int g);
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int g);
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm,
                         hipStream_t s);
