@@ -380,6 +380,10 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
     CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0", fn);
     CHECK(aligned(w0, 2), QL_ERR_ALIGN, "%s: Q8_0 blocks (w0) must be 2-byte aligned", fn);
   }
+  // the kernel addresses x and the expert weights with 32-bit buffer offsets
+  const int64_t wbytes = fmt == QL_MXFP4 ? e * n * (k / 2) : e * n * (k / 32) * 34;
+  CHECK((n_pos / pos_per_row) * k * 2 < (int64_t(1) << 31) && wbytes < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+        "%s: x and the expert weights must each be smaller than 2 GiB", fn);
   const size_t need = qlinear_apply_experts_workspace_size(n_pos, e);
   CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
   CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
