@@ -38,7 +38,59 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of 1 GiB (4 times): the reference for the HBM byte "
+                         "counters that the roofline traffic figure is scaled by")
     return ap.parse_args()
+
+
+# Source files that define the decode GEMV kernel; the measured HBM traffic recorded under
+# profiles/ is reported only while their contents hash to the value recorded with it.
+GEMV_SOURCES = ["device_common.hpp", "launch.hpp", "gemv_impl.hpp", "gemv.hip", "gemv_m1.hip", "qlinear_api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_kernel_qwen3_0.6b_decode_4bit_g64.txt")
+
+
+def gemv_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "weight_only_quantized_affine_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter runs (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the same counter's reading for a plain copy of known size), or None when the
+    kernel sources changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != gemv_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device-to-device copy of 1 GiB, four times (for the byte-counter calibration)."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "repeats": 4}), flush=True)
 
 
 def log(msg):
@@ -47,6 +99,9 @@ def log(msg):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path runs on a single "
               "MI355X; the product shards along its output rows with no exchange)", file=sys.stderr)
@@ -160,7 +215,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(),
             "kernel": "gemv_kernel<1,4,bf16,bf16> (one launch per step)",
             "bytes_per_launch": wbytes4 + io4,
         },

@@ -195,7 +195,7 @@ __device__ __forceinline__ void expert_chunk(const int32_t* __restrict__ sPos, i
     xoff[j] = (uint32_t)(((int64_t)(pos / pos_per_row) * K + 8 * c) * 2);
     xc[j] = c;
   }
-  auto copy_x = [&](int kt, uint8_t* stage) {
+  auto copy_x = [&](int kt, uint8_t* stage) __attribute__((always_inline)) {
     const int k0 = kt * EBK;
 #pragma unroll
     for (int j = 0; j < MS; ++j) {
@@ -205,7 +205,7 @@ __device__ __forceinline__ void expert_chunk(const int32_t* __restrict__ sPos, i
     }
   };
   // weight loads of this lane's rows (one per column tile)
-  auto load_w = [&](int kt, WBuf<FMT>* wb) {
+  auto load_w = [&](int kt, WBuf<FMT>* wb) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < ECT; ++ct) {
       if constexpr (FMT == FMT_MXFP4) {
@@ -243,7 +243,7 @@ __device__ __forceinline__ void expert_chunk(const int32_t* __restrict__ sPos, i
       for (int b = 0; b < 2; ++b) qsh[ct][b] = (uint32_t)((wrow[ct] * (K / 32) * 34 + 34 * b + 2 + 16 * h) & 3);
   }
 
-  auto compute = [&](int kt, const uint8_t* stage, const WBuf<FMT>* wb) {
+  auto compute = [&](int kt, const uint8_t* stage, const WBuf<FMT>* wb) __attribute__((always_inline)) {
     if constexpr (FMT == FMT_MXFP4) {
       // the scale of this lane half's block: 2^(s-127) as fp32 (s = 0: the subnormal 2^-127),
       // NaN for s = 255, and 0 past K
@@ -322,7 +322,7 @@ __device__ __forceinline__ void expert_chunk(const int32_t* __restrict__ sPos, i
   // copies below refill), copy x of kt + ENS - 1, compute, load the weights of kt + ENS into the
   // ring slot just consumed.  Steps past the last tile (completing a round) load clamped tiles and
   // compute nothing.
-  auto step = [&](int kt, const uint8_t* cur, uint8_t* refill, WBuf<FMT>* wb) {
+  auto step = [&](int kt, const uint8_t* cur, uint8_t* refill, WBuf<FMT>* wb) __attribute__((always_inline)) {
     ex_wait_vmcnt<L>();
     __builtin_amdgcn_s_barrier();
     copy_x(kt + ENS - 1 < KT ? kt + ENS - 1 : KT - 1, refill);

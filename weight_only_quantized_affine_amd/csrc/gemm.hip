@@ -305,7 +305,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void gemm_kernel(const uint
   }
   const __amdgpu_buffer_rsrc_t rsA = gemm_rsrc(xa, M * K * 2);
   const __amdgpu_buffer_rsrc_t rsB = gemm_rsrc(packed, N * words_per_row * 4);
-  auto copy_tile = [&](int kt, uint8_t* stage) {
+  auto copy_tile = [&](int kt, uint8_t* stage) __attribute__((always_inline)) {
     const int64_t k0 = kt * BK;
     const uint32_t sa = (uint32_t)(k0 * 2), sbo = (uint32_t)(k0 * BITS / 8);
     uint32_t ashift[4], bshift[LB];
@@ -341,14 +341,14 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void gemm_kernel(const uint
   const int ngroups = (int)groups;
   uint32_t rx = 0;
   u32x4_t rw = {0, 0, 0, 0};
-  auto load_scalars = [&](int kt) {
+  auto load_scalars = [&](int kt) __attribute__((always_inline)) {
     const int ga = min((kt * BK + 32 * a_half) >> gshift, ngroups - 1);
     const int gs = min((kt * BK + 32 * s_half) >> gshift, ngroups - 1);
     rx = xs_row[ga];
     rw = wr_row[gs];
   };
   const int kint = (int)K;
-  auto store_scalars = [&](int kt) {
+  auto store_scalars = [&](int kt) __attribute__((always_inline)) {
     const int ka = kt * BK + 32 * a_half, ks = kt * BK + 32 * s_half;
     if (ka < kint && (ka & (G - 1)) == 0) sX[a_row * XR_PITCH + ((ka >> gshift) & 7)] = rx;
     sS[kt & 1][s_col][s_half] = ks < kint ? __uint_as_float(rw[0]) : 0.0f;
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void gemm_kernel(const uint
   const f32x16_t zero16 = {0.0f};
 
   // Bias terms of the group pair p (groups 2p, 2p+1): see the comment above the kernel.
-  auto bias_pair = [&](int p) {
+  auto bias_pair = [&](int p) __attribute__((always_inline)) {
     const int gi = 2 * p + h;
     const bool live = gi < (int)groups;
     const int slot = gi & 7;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void gemm_kernel(const uint
   };
 
   // ---- compute of one tile from a stage
-  auto compute = [&](int kt, const uint8_t* stage) {
+  auto compute = [&](int kt, const uint8_t* stage) __attribute__((always_inline)) {
     // x fragments: 2 row-tiles x 4 k-steps
     u32x4_t af[2][4];
 #pragma unroll
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(256, BITS == 4 ? 2 : 1) void gemm_kernel(const uint
   // of tile kt + 2 (clamped: past the end they refill the stage computed in the previous
   // iteration, which no wave reads again) and the scalars of tile kt + 1, then compute.
   const int KTi = (int)KT;
-  auto step = [&](int kt, const uint8_t* cur, uint8_t* ahead2, auto first) {
+  auto step = [&](int kt, const uint8_t* cur, uint8_t* ahead2, auto first) __attribute__((always_inline)) {
     // steps past the last tile (to complete a round of three) wait, copy and load like the
     // others, so that the wait counts are the same on every path, and compute nothing
     const int kc = kt < KTi ? kt : KTi - 1;

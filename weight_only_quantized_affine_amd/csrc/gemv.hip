@@ -16,9 +16,8 @@ hipError_t launch_gemv_m8(const GemvDesc&, const GemvDesc*, const GemvTile*, int
 
 GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches) {
   const GemvGeom g = gemv_geometry(k, bits, batches);
-  const int64_t ck = 128 / bits;
   const int64_t lb = g.rows_per_wg * 4;
-  const int64_t xb = mt * g.chunks * ((ck + 8) * 2 + 4);
+  const int64_t xb = mt * g.chunks * (gemv_x_pitch((int)mt, bits) * 2 + 4);
   GemvLds r;
   r.xlds = (xb + lb) <= 64 * 1024 ? 1 : 0;
   r.bytes = (size_t)((r.xlds ? xb : 0) + lb);

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
   using U = Unpack<BITS, XT>;
   constexpr int NP = U::NP;       // operand pairs per 16-byte chunk
   constexpr int CK = 128 / BITS;  // k-values per chunk
-  constexpr int CP = CK + 8;      // LDS pitch of a chunk of x (16-bit elements)
+  constexpr int CP = gemv_x_pitch(MT, BITS);  // LDS pitch of a chunk of x (16-bit elements)
   extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
 
   GemvDesc d;
@@ -190,11 +190,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
   const __amdgpu_buffer_rsrc_t rb = make_rsrc((const uint16_t*)d.biases + wg_row * groups, rows_left * groups * 2);
   const int lrow0 = wave * P * R + rg;  // this lane's first row, relative to the workgroup
 
-  auto step_of = [&](int st, int& b, int& i) {
+  auto step_of = [&](int st, int& b, int& i) __attribute__((always_inline)) {
     b = st / cpl;
     i = st - b * cpl;
   };
-  auto issue = [&](int st, StepBuf& q) {
+  auto issue = [&](int st, StepBuf& q) __attribute__((always_inline)) {
     int b, i;
     step_of(st, b, i);
     const bool live = st < steps;
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
   const __amdgpu_buffer_rsrc_t ry = make_rsrc(d.y, (int64_t)m * n * esz);
   // End of a batch: reduce over the L lanes of each row; lane li == 0 of each row stores (all
   // lanes issue the stores, the others with an out-of-range offset).
-  auto finish_batch = [&](int b) {
+  auto finish_batch = [&](int b) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int lr = lrow0 + b * rows_per_set + r * P;
@@ -271,63 +271,66 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
     }
   };
 
-  auto compute = [&](int i, const StepBuf& q) {
+  // The codes of the R rows are unpacked once; each row of x is then read (LDS or memory) and
+  // dotted with all R of them, so the live registers do not grow with MT.
+  auto compute = [&](int i, const StepBuf& q) __attribute__((always_inline)) {
     const int c = li + i * L;
-    uint32_t xp[MT][NP];
-    float xs[MT];
+    uint32_t t[R][NP];
+    float sr[R], br[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      U::codes(q.w[r], t[r]);
+      sr[r] = param_to_f32<PT>(q.s[r]);
+      br[r] = param_to_f32<PT>(q.b[r]);
+    }
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const int jj = j < m ? j : 0;  // rows past m reuse row 0 and are never stored
+      uint32_t xp[NP];
+      float xs;
       if (XLDS) {
 #pragma unroll
         for (int e = 0; e < NP / 4; ++e) {
           const u32x4_t u = *(const u32x4_t*)&sx[(jj * C + c) * CP + 8 * e];
-          xp[j][4 * e + 0] = u[0];
-          xp[j][4 * e + 1] = u[1];
-          xp[j][4 * e + 2] = u[2];
-          xp[j][4 * e + 3] = u[3];
+          xp[4 * e + 0] = u[0];
+          xp[4 * e + 1] = u[1];
+          xp[4 * e + 2] = u[2];
+          xp[4 * e + 3] = u[3];
         }
-        xs[j] = sX[jj * C + c];
+        xs = sX[jj * C + c];
       } else {
         gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
-        float t = 0.0f;
+        float tsum = 0.0f;
 #pragma unroll
         for (int e = 0; e < NP / 4; ++e) {
           const u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)jj * k + (int64_t)c * CK + 8 * e);
 #pragma unroll
-          for (int z = 0; z < 4; ++z) t = dot2(XT{}, raw[z], XTraits<XT>::kOnes, t);
+          for (int z = 0; z < 4; ++z) tsum = dot2(XT{}, raw[z], XTraits<XT>::kOnes, tsum);
           const u32x4_t u = U::xperm(raw);
-          xp[j][4 * e + 0] = u[0];
-          xp[j][4 * e + 1] = u[1];
-          xp[j][4 * e + 2] = u[2];
-          xp[j][4 * e + 3] = u[3];
+          xp[4 * e + 0] = u[0];
+          xp[4 * e + 1] = u[1];
+          xp[4 * e + 2] = u[2];
+          xp[4 * e + 3] = u[3];
         }
-        xs[j] = t;
+        xs = tsum;
       }
-    }
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      uint32_t t[NP];
-      U::codes(q.w[r], t);
-      const float sr = param_to_f32<PT>(q.s[r]);
-      const float br = param_to_f32<PT>(q.b[r]);
-#pragma unroll
-      for (int j = 0; j < MT; ++j) {
+      for (int r = 0; r < R; ++r) {
         float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
         for (int e = 0; e < NP; e += 2) {
-          p0 = dot2(XT{}, t[e], xp[j][e], p0);
-          p1 = dot2(XT{}, t[e + 1], xp[j][e + 1], p1);
+          p0 = dot2(XT{}, t[r][e], xp[e], p0);
+          p1 = dot2(XT{}, t[r][e + 1], xp[e + 1], p1);
         }
-        const float pq = __builtin_fmaf(-U::kOff, xs[j], p0 + p1);  // sum x*q
-        acc[r][j] = __builtin_fmaf(sr, pq, __builtin_fmaf(br, xs[j], acc[r][j]));
+        const float pq = __builtin_fmaf(-U::kOff, xs, p0 + p1);  // sum x*q
+        acc[r][j] = __builtin_fmaf(sr[r], pq, __builtin_fmaf(br[r], xs, acc[r][j]));
       }
     }
   };
 
   // Every load is issued on every path (past the end with an out-of-range offset), so the wait
   // counts are the same whichever way a branch goes.
-  auto run = [&](int st, const StepBuf& q) {
+  auto run = [&](int st, const StepBuf& q) __attribute__((always_inline)) {
     if (st < steps) {
       int b, i;
       step_of(st, b, i);

@@ -66,8 +66,11 @@ inline int gemv_batches(int64_t n, int64_t k, int bits, int64_t min_tiles) {
   while (nb > 1 && (n + g1.rows_per_wg * nb - 1) / (g1.rows_per_wg * nb) < min_tiles) --nb;
   return nb;
 }
-// Dynamic LDS of a GEMV launch: x chunks, their half sums and the layer-bias rows; x is kept
-// in LDS (xlds) when it fits in 64 KiB, else read from HBM by every lane.
+// LDS pitch (16-bit elements) of a 16-byte chunk of x (128 / bits values): padded by 8 against
+// bank conflicts for up to 2 rows of x, unpadded for more (so that 8 rows of k = 3072 fit).
+__host__ __device__ constexpr int gemv_x_pitch(int mt, int bits) { return 128 / bits + (mt <= 2 ? 8 : 0); }
+// Dynamic LDS of a GEMV launch: x chunks, their sums and the layer-bias rows; x is kept in LDS
+// (xlds) when it fits in 64 KiB, else read from memory by every lane.
 struct GemvLds {
   size_t bytes;
   int xlds;
