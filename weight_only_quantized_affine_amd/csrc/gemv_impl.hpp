@@ -48,17 +48,28 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // and the permutation of 8 consecutive x values that matches the pair order.
 template <int BITS, typename XT> struct Unpack;
 
+// A 32-bit constant placed in a VGPR once.  The VOP3 encodings of this target take no literal
+// operand, so shift-and-mask-and-or only folds into one v_and_or_b32 when the mask and the magic
+// bits are registers.
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
 template <typename XT> struct Unpack<4, XT> {
   static constexpr int NP = 16;
   static constexpr float kOff = XTraits<XT>::kOff4;
-  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t) {
+  static constexpr uint32_t kMask = 0x000F000Fu, kMagic = XTraits<XT>::kMagic4;
+  // mk, mg: kMask and kMagic held in registers (see vconst)
+  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t, uint32_t mk, uint32_t mg) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t v = w[j];
-      t[4 * j + 0] = (v & 0x000F000Fu) | XTraits<XT>::kMagic4;          // codes 0, 4
-      t[4 * j + 1] = ((v >> 4) & 0x000F000Fu) | XTraits<XT>::kMagic4;   // codes 1, 5
-      t[4 * j + 2] = ((v >> 8) & 0x000F000Fu) | XTraits<XT>::kMagic4;   // codes 2, 6
-      t[4 * j + 3] = ((v >> 12) & 0x000F000Fu) | XTraits<XT>::kMagic4;  // codes 3, 7
+      t[4 * j + 0] = (v & mk) | mg;          // codes 0, 4
+      t[4 * j + 1] = ((v >> 4) & mk) | mg;   // codes 1, 5
+      t[4 * j + 2] = ((v >> 8) & mk) | mg;   // codes 2, 6
+      t[4 * j + 3] = ((v >> 12) & mk) | mg;  // codes 3, 7
     }
   }
   // x0..x7 -> (x0,x4),(x1,x5),(x2,x6),(x3,x7)
@@ -71,7 +82,8 @@ template <typename XT> struct Unpack<4, XT> {
 template <> struct Unpack<8, BF16> {
   static constexpr int NP = 8;
   static constexpr float kOff = 0.0f;
-  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t) {
+  static constexpr uint32_t kMask = 0u, kMagic = 0u;
+  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t, uint32_t, uint32_t) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t v = w[j];
@@ -85,12 +97,13 @@ template <> struct Unpack<8, BF16> {
 template <> struct Unpack<8, F16> {
   static constexpr int NP = 8;
   static constexpr float kOff = 1024.0f;
-  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t) {
+  static constexpr uint32_t kMask = 0x00FF00FFu, kMagic = 0x64006400u;
+  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t, uint32_t mk, uint32_t mg) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t v = w[j];
-      t[2 * j + 0] = (v & 0x00FF00FFu) | 0x64006400u;         // codes 0, 2
-      t[2 * j + 1] = ((v >> 8) & 0x00FF00FFu) | 0x64006400u;  // codes 1, 3
+      t[2 * j + 0] = (v & mk) | mg;         // codes 0, 2
+      t[2 * j + 1] = ((v >> 8) & mk) | mg;  // codes 1, 3
     }
   }
   // x0..x7 -> (x0,x2),(x1,x3),(x4,x6),(x5,x7)
@@ -151,6 +164,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
                                                    const GemvTile* __restrict__ tiles, int ydt) {
   using U = Unpack<BITS, XT>;
   constexpr int NP = U::NP;       // operand pairs per 16-byte chunk
+  const uint32_t mk = vconst(U::kMask), mg = vconst(U::kMagic);
   constexpr int CK = 128 / BITS;  // k-values per chunk
   constexpr int CP = gemv_x_pitch(MT, BITS);  // LDS pitch of a chunk of x (16-bit elements)
   extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
@@ -279,7 +293,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvDesc single, const GemvDe
     float sr[R], br[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      U::codes(q.w[r], t[r]);
+      U::codes(q.w[r], t[r], mk, mg);
       sr[r] = param_to_f32<PT>(q.s[r]);
       br[r] = param_to_f32<PT>(q.b[r]);
     }
