@@ -46,7 +46,8 @@ def parse():
 
 # Source files that define the decode GEMV kernel; the measured HBM traffic recorded under
 # profiles/ is reported only while their contents hash to the value recorded with it.
-GEMV_SOURCES = ["device_common.hpp", "launch.hpp", "gemv_impl.hpp", "gemv.hip", "gemv_m1.hip", "qlinear_api.cpp"]
+GEMV_SOURCES = ["device_common.hpp", "launch.hpp", "gemv_impl.hpp", "gemv_mfma.hpp", "gemv.hip", "gemv_m1.hip",
+                "qlinear_api.cpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_kernel_qwen3_0.6b_decode_4bit_g64.txt")
 
 
@@ -216,7 +217,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic(),
-            "kernel": "gemv_kernel<1,4,bf16,bf16> (one launch per step)",
+            "kernel": "gemv_mf_kernel<1,64,bf16,bf16> (one launch per step)",
             "bytes_per_launch": wbytes4 + io4,
         },
     }

@@ -190,6 +190,18 @@ GEMV_CASES = [
     (8, 250, 2048, 4, 64, "f16", "f16", "f32"),
     (11, 90, 512, 4, 64, "bf16", "bf16", "f32"),
     (1, 77, 96, 8, 32, "bf16", "f16", "bf16"),
+    # 4-bit, k a multiple of 128: the matrix-core kernel (ragged rows, u-blocks past the row end,
+    # every group size and row-count template, x rows that fill the accumulator rows partly)
+    (1, 1000, 640, 4, 64, "bf16", "bf16", "f32"),
+    (2, 64, 128, 4, 64, "f16", "f16", "f16"),
+    (3, 257, 384, 4, 32, "f16", "bf16", "f32"),
+    (4, 200, 1024, 4, 32, "bf16", "bf16", "f32"),
+    (4, 130, 1152, 4, 128, "bf16", "f16", "bf16"),
+    (6, 300, 2560, 4, 64, "bf16", "bf16", "f32"),
+    (8, 70, 768, 4, 128, "bf16", "bf16", "f32"),
+    (7, 1100, 3072, 4, 64, "f16", "bf16", "bf16"),
+    # m = 5..8 with group size 32 needs 32 accumulator rows: the vector-ALU kernel
+    (5, 100, 512, 4, 32, "bf16", "bf16", "f32"),
 ]
 
 

@@ -29,8 +29,8 @@ FLAGS = [
 # Matrix-core kernels keep their accumulators in the architectural VGPRs (the VALU reads them
 # every group to apply the scales; accumulation registers would need a move per element).
 FILE_FLAGS = {
-    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "experts.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    f: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    for f in ("gemm.hip", "experts.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip", "gemv_m8.hip")
 }
 
 

@@ -162,13 +162,22 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
     d.k = k;
     d.bits = bits;
     d.group_size = group_size;
-    d.batches = ql::gemv_batches(n, k, bits, 1024);
-    const ql::GemvGeom g = ql::gemv_geometry(k, bits, d.batches);
-    const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
-    const ql::GemvLds lds = ql::gemv_lds(k, bits, ql::gemv_mt(mm), d.batches);
-    hipError_t e = ql::launch_gemv(d, nullptr, nullptr, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype),
-                                   dt(y_dtype), lds.bytes, lds.xlds, bits == 4 && group_size == 32,
-                                   (hipStream_t)stream);
+    hipError_t e;
+    if (ql::gemv_mf_eligible(mm, k, bits, group_size, scales, biases)) {
+      const int mt = ql::gemv_mt(mm);
+      d.batches = ql::gemv_mf_batches(n, k, group_size, mt, 1024);
+      const ql::GemvMfGeom g = ql::gemv_mf_geometry(k, d.batches);
+      const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
+      e = ql::launch_gemv_mf(d, nullptr, nullptr, tiles, (int)mm, group_size, dt(x_dtype), dt(param_dtype),
+                             dt(y_dtype), ql::gemv_mf_lds(k, mt, group_size, d.batches).bytes, (hipStream_t)stream);
+    } else {
+      d.batches = ql::gemv_batches(n, k, bits, 1024);
+      const ql::GemvGeom g = ql::gemv_geometry(k, bits, d.batches);
+      const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
+      const ql::GemvLds lds = ql::gemv_lds(k, bits, ql::gemv_mt(mm), d.batches);
+      e = ql::launch_gemv(d, nullptr, nullptr, tiles, (int)mm, bits, dt(x_dtype), dt(param_dtype), dt(y_dtype),
+                          lds.bytes, lds.xlds, bits == 4 && group_size == 32, (hipStream_t)stream);
+    }
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
@@ -210,7 +219,7 @@ struct BatchedPlan {
   std::vector<ql::GemvDesc> descs;
   std::vector<ql::GemvTile> tiles;
   struct Cls {
-    int m, bits, xlds;
+    int m, bits, xlds, mf_g;  // mf_g: group size of a matrix-core class, 0 for the vector-ALU kernel
     bool g2;
     size_t first_tile, n_tiles, lds;
   };
@@ -222,7 +231,12 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
   std::vector<int> order;
   for (int i = 0; i < count; ++i)
     if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
+  auto mf = [&](int i) {
+    return ql::gemv_mf_eligible(probs[i].m, probs[i].k, probs[i].bits, probs[i].group_size, probs[i].scales,
+                                probs[i].biases);
+  };
   auto key = [&](int i) {
+    if (mf(i)) return (1 << 16) + ql::gemv_mt(probs[i].m) * 1024 + probs[i].group_size;
     const bool g2 = probs[i].bits == 4 && probs[i].group_size == 32;
     return ql::gemv_mt(probs[i].m) * 32 + probs[i].bits * 2 + (g2 ? 1 : 0);
   };
@@ -236,6 +250,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     c.m = 0;
     c.bits = probs[order[j]].bits;
     c.g2 = c.bits == 4 && probs[order[j]].group_size == 32;
+    c.mf_g = mf(order[j]) ? probs[order[j]].group_size : 0;
     c.first_tile = plan.tiles.size();
     bool fits = true;
     size_t lds_x = 0, lds_lb = 0;
@@ -254,8 +269,16 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       d.k = p.k;
       d.bits = p.bits;
       d.group_size = p.group_size;
-      d.batches = ql::gemv_batches(p.n, p.k, p.bits, 1);
       c.m = std::max<int>(c.m, (int)p.m);
+      if (c.mf_g) {
+        d.batches = ql::gemv_mf_batches(p.n, p.k, p.group_size, ql::gemv_mt(p.m), 1);
+        const ql::GemvMfGeom g = ql::gemv_mf_geometry(p.k, d.batches);
+        lds_x = std::max(lds_x, ql::gemv_mf_lds(p.k, ql::gemv_mt(p.m), p.group_size, d.batches).bytes);
+        const int64_t t = (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
+        for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
+        continue;
+      }
+      d.batches = ql::gemv_batches(p.n, p.k, p.bits, 1);
       const ql::GemvLds need = ql::gemv_lds(p.k, p.bits, ql::gemv_mt(p.m), d.batches);
       const ql::GemvGeom g = ql::gemv_geometry(p.k, p.bits, d.batches);
       if (!need.xlds) fits = false;
@@ -266,7 +289,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     }
     c.n_tiles = plan.tiles.size() - c.first_tile;
     c.xlds = fits ? 1 : 0;
-    c.lds = fits ? lds_x : lds_lb;
+    c.lds = (fits || c.mf_g) ? lds_x : lds_lb;
     plan.classes.push_back(c);
     j = e;
   }
@@ -322,8 +345,11 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
   const ql::GemvTile* d_tiles = (const ql::GemvTile*)(ws + plan.tiles_offset);
   for (const BatchedPlan::Cls& c : plan.classes) {
     ql::GemvDesc none{};
-    hipError_t e = ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
-                                   dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, c.xlds, c.g2, s);
+    hipError_t e =
+        c.mf_g ? ql::launch_gemv_mf(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.mf_g,
+                                    dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s)
+               : ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
+                                 dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, c.xlds, c.g2, s);
     if (e != hipSuccess) return launched(e, fn);
   }
   return ok();
