@@ -5,7 +5,9 @@ Headline (`value`): decode GEMV weight GB/s of one decode step of a Qwen3-0.6B-s
 g64 affine with bf16 scales/biases, bf16 activations, batch 1): one step = one problem-list
 launch over all 197 projections.  Weights are resident in HBM; three distinct weight copies
 are used in rotation so that a repeat never finds the previous step's weights in the 256 MB
-Infinity Cache.  Other legs in the same JSON line: 8-bit decode at batch 1 and 8, the prefill
+Infinity Cache.  The default warmup (1000 steps, about 60 ms) brings the clocks to their
+sustained level before the timed steps.  Other legs in the same JSON line: 8-bit decode at
+batch 1 and 8, 4-bit decode at batch 8, the prefill
 GEMM of a 9B-class layer (M=2048), routed experts (32 x 5760x2880, 512 tokens, top-4) in MXFP4
 and Q8_0, and the quantizer.  `roofline` is the decode kernel's achieved HBM GB/s (algorithmic
 bytes / average kernel time measured with HIP events on the launch stream) against 8 TB/s;
@@ -33,8 +35,8 @@ METRIC = "qlinear GEMV weight GB/s (% HBM peak) + prefill GEMM TFLOP/s, 4-bit g6
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -253,18 +255,18 @@ def _time_launches(fn, reps, warmup, stream):
 
 def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
     legs = {}
-    # ---------------- 8-bit decode, batch 1 and 8
-    for m in (1, 8):
-        log(f"leg: 8-bit decode m={m}")
-        sets8, wb8, io8 = build_decode(8, m, 2, 30_000 + m)
-        wall, avg = time_decode(sets8, 10, 3)
-        legs[f"decode_8bit_m{m}"] = {
-            "weight_gbs": round(wb8 / (avg * 1e-3) / 1e9, 2),
+    # ---------------- 8-bit decode at batch 1 and 8, 4-bit decode at batch 8
+    for bits, m in ((8, 1), (8, 8), (4, 8)):
+        log(f"leg: {bits}-bit decode m={m}")
+        sets_b, wb, io = build_decode(bits, m, 2, 30_000 + 100 * bits + m)
+        wall, avg = time_decode(sets_b, 100, 10)
+        legs[f"decode_{bits}bit_m{m}"] = {
+            "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 2),
             "kernel_ms": round(avg, 5),
-            "pct_hbm_peak": round(100 * (wb8 + io8) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "weights_bytes": wb8,
+            "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "weights_bytes": wb,
         }
-        del sets8
+        del sets_b
         torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM, 9B-class layer at M = 2048

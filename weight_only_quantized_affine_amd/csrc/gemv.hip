@@ -26,7 +26,7 @@ hipError_t launch_gemv_mf_m8(const GemvDesc&, const GemvDesc*, const GemvTile*, 
 int gemv_mf_batches(int64_t n, int64_t k, int g, int mt, int64_t min_tiles) {
   const int64_t rows = gemv_mf_geometry(k, 1).rows_per_wg;
   const int64_t set_bytes = rows * (k / 2);
-  int nb = set_bytes > 0 ? (int)((GEMV_WG_BYTES + set_bytes / 2) / set_bytes) : 1;
+  int nb = set_bytes > 0 ? (int)((GEMV_MF_WG_BYTES + set_bytes / 2) / set_bytes) : 1;
   nb = nb < 1 ? 1 : (nb > 32 ? 32 : nb);
   while (nb > 1 && ((n + rows * nb - 1) / (rows * nb) < min_tiles || gemv_mf_lds(k, mt, g, nb).bytes > 64 * 1024))
     --nb;

@@ -79,7 +79,7 @@ template <> struct MfParams<128> {
 };
 
 template <int MT, int G, typename XT, typename PT>
-__global__ __launch_bounds__(256) void gemv_mf_kernel(GemvDesc single, const GemvDesc* __restrict__ table,
+__global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc single, const GemvDesc* __restrict__ table,
                                                       const GemvTile* __restrict__ tiles, int ydt) {
   using U = Unpack<4, XT>;
   constexpr int GU = gemv_mf_gu(G);                // groups per u-block
@@ -159,8 +159,11 @@ __global__ __launch_bounds__(256) void gemv_mf_kernel(GemvDesc single, const Gem
     }
   }
   {
+    // One thread per 8 values: stage them, and sum them with the GW/8 neighbours of the same
+    // accumulator row and u-block (aligned lane groups; (MT+1) * KP/8 is a multiple of 16).
     gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
     const int c8n = KP / 8;
+    constexpr int GL = GW / 8;  // lanes per x sum: 16, 8 or 4
     for (int t = threadIdx.x; t < (MT + 1) * c8n; t += 256) {
       const int xr = t / c8n, c8 = t - xr * c8n;
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -169,21 +172,18 @@ __global__ __launch_bounds__(256) void gemv_mf_kernel(GemvDesc single, const Gem
         v = U::xperm(raw);
       }
       *(u32x4_t*)&sx[xr * XP + 8 * c8] = v;
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < SR * MNU * 16; t += 256) {
-    const int ub = t >> 4, i = t & 15, xr = i / GU, gp = i - xr * GU;
-    float sum = 0.0f;
-    if (xr < m && ub < UB) {
+      float sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < GW / 8; ++q) {
-        const u32x4_t v = *(const u32x4_t*)&sx[xr * XP + ub * 128 + gp * GW + 8 * q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sum = dot2(XT{}, v[e], XTraits<XT>::kOnes, sum);
-      }
+      for (int e = 0; e < 4; ++e) sum = dot2(XT{}, v[e], XTraits<XT>::kOnes, sum);
+      sum = group_sum(sum, GL);
+      const int ub = c8 >> 4, gp = (c8 & 15) / GL;
+      if (xr < MT && (c8 & (GL - 1)) == 0) xsum[ub * 16 + xr * GU + gp] = sum;
     }
-    xsum[t] = sum;
+    // accumulator rows past MT * GU have no x row: zero sums
+    for (int t = threadIdx.x; t < SR * MNU * (16 - MT * GU); t += 256) {
+      const int ub = t / (16 - MT * GU), i = MT * GU + t - ub * (16 - MT * GU);
+      xsum[ub * 16 + i] = 0.0f;
+    }
   }
   __syncthreads();
 

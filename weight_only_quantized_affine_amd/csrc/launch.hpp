@@ -81,7 +81,10 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 // and walks them in u-blocks of 128 codes (64 bytes of each row); GEMV_MF_NU u-blocks make one
 // pipeline step.  A 256-thread workgroup walks `batches` sets of 64 * GEMV_MF_RS rows.
 #ifndef GEMV_MF_NU
-#define GEMV_MF_NU 4
+#define GEMV_MF_NU 2
+#endif
+#ifndef GEMV_MF_WG_BYTES
+#define GEMV_MF_WG_BYTES 32768  // packed bytes per workgroup the batch count aims at
 #endif
 #ifndef GEMV_MF_RS
 #define GEMV_MF_RS 1
@@ -91,6 +94,9 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #endif
 #ifndef GEMV_MF_SCHED
 #define GEMV_MF_SCHED 1
+#endif
+#ifndef GEMV_MF_MINB
+#define GEMV_MF_MINB 1  // workgroups per CU the register allocation must allow
 #endif
 #ifndef GEMV_MF_AUX
 #define GEMV_MF_AUX 0  // cache policy bits of the weight-word loads
@@ -140,7 +146,7 @@ inline bool gemv_mf_eligible(int64_t m, int64_t k, int bits, int g, const void* 
   const int mt = gemv_mt(m);
   return mt * gemv_mf_gu(g) <= 16 && gemv_mf_lds(k, mt, g, 1).bytes <= 64 * 1024;
 }
-// Batches per workgroup: about GEMV_WG_BYTES of packed words, fewer when `min_tiles` workgroups
+// Batches per workgroup: about GEMV_MF_WG_BYTES of packed words, fewer when `min_tiles` workgroups
 // would otherwise not be reached or the LDS would pass 64 KiB.
 int gemv_mf_batches(int64_t n, int64_t k, int g, int mt, int64_t min_tiles);
 

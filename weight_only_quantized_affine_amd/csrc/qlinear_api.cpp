@@ -213,6 +213,10 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
                   fn);
 }
 
+#ifndef GEMV_TILES_BY_SIZE
+#define GEMV_TILES_BY_SIZE 1
+#endif
+
 namespace {
 // Device table of a problem list: descs (ordered by class), then the tiles of every class.
 struct BatchedPlan {
@@ -288,6 +292,17 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
     }
     c.n_tiles = plan.tiles.size() - c.first_tile;
+    // Largest tiles first: the workgroups that start last, and so end the launch, are short.
+    if (GEMV_TILES_BY_SIZE) {
+      auto tile_bytes = [&](const ql::GemvTile& t) {
+        const ql::GemvDesc& d = plan.descs[t.prob];
+        const int64_t rows = c.mf_g ? ql::gemv_mf_geometry(d.k, d.batches).rows_per_wg
+                                    : ql::gemv_geometry(d.k, d.bits, d.batches).rows_per_wg;
+        return std::min<int64_t>(rows, d.n - (int64_t)t.local * rows) * (d.k * d.bits / 8);
+      };
+      std::stable_sort(plan.tiles.begin() + c.first_tile, plan.tiles.end(),
+                       [&](const ql::GemvTile& a, const ql::GemvTile& b) { return tile_bytes(a) > tile_bytes(b); });
+    }
     c.xlds = fits ? 1 : 0;
     c.lds = (fits || c.mf_g) ? lds_x : lds_lb;
     plan.classes.push_back(c);
