@@ -50,7 +50,7 @@ def parse():
 # profiles/ is reported only while their contents hash to the value recorded with it.
 GEMV_SOURCES = ["device_common.hpp", "launch.hpp", "gemv_impl.hpp", "gemv_mfma.hpp", "gemv.hip", "gemv_m1.hip",
                 "qlinear_api.cpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_kernel_qwen3_0.6b_decode_4bit_g64.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_mf_kernel_qwen3_0.6b_decode_4bit_g64.txt")
 
 
 def gemv_source_hash() -> str:
