@@ -101,15 +101,19 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        ql_dtype param_dtype, int64_t n, int bits, int group_size,
                        const void* layer_bias, void* y, ql_dtype y_dtype, void* stream);
 
-/* Prefill GEMM: the same product as qlinear_gemv, for large m, on the matrix cores.  The codes
- * enter the bf16 MFMA as exact small integers and each group's scale is applied to that group's
- * fp32 partial sum (the block-scaled contraction of Nx_quant Products, apply); the additive
- * bias enters through the per-group sums of x.  Needs a device workspace of
+/* Prefill GEMM: the same product as qlinear_gemv (Nx_quant Products, apply: fp32 accumulation,
+ * one rounding to y_dtype), for large m, on the matrix cores.  Each weight is dequantized in
+ * registers and rounded once to fp16, and x enters as fp16 after an exact power-of-two scaling
+ * per row; the fp16 MFMA accumulates in fp32 (error ~1.5e-4 relative per output row, from the
+ * fp16 rounding of the weights).  Needs a device workspace of
  * qlinear_gemm_workspace_size(m, n, k, group_size) bytes (16-byte aligned), overwritten by the
- * call: the per-group sums of x (m * k/group_size words), per-group records of the weight's
- * scales and biases (n * k/group_size x 16 bytes), each padded to 256 bytes, then a copy of x
- * (m * k 16-bit values) rearranged for the matrix-core operand order.  x and the packed words must
- * each be smaller than 2 GiB (QL_ERR_UNSUPPORTED otherwise). */
+ * call: the fp16 copy of x (m rows of k rounded up to a multiple of 64 values), its m row factors
+ * (floats), per-group records of the weight's scales and biases (n * k/group_size pairs of
+ * floats) and n row factors, each padded to 256 bytes, and, when the output has too few 256 x 128
+ * tiles to fill the chip (fewer than 128), fp32 partial products of the k-ranges the call splits
+ * the sum into (2 to 4 ranges: that many m x n floats), summed by a second pass in a fixed order
+ * (results do not depend on timing).  The fp16 copy of x and the packed words must each be smaller
+ * than 2 GiB (QL_ERR_UNSUPPORTED otherwise). */
 size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int group_size);
 ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        const uint32_t* packed, const void* scales, const void* biases,

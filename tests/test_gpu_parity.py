@@ -258,6 +258,13 @@ GEMM_CASES = [
     (64, 129, 1024, 4, 64, "f16", "bf16"),
     (1, 100, 256, 4, 64, "bf16", "bf16"),
     (33, 64, 768, 8, 128, "bf16", "f16"),
+    # few output tiles: k split in 2 (17 k-tiles: 9 + 8) and in 4 (65 k-tiles: 17 + 17 + 17 + 14)
+    (70, 300, 1088, 4, 64, "bf16", "bf16"),
+    (100, 100, 4160, 4, 64, "f16", "f16"),
+    (90, 120, 2048, 8, 32, "bf16", "bf16"),
+    # at least two output tiles per compute unit: two workgroups per CU, two LDS stages
+    (4100, 4000, 256, 4, 64, "bf16", "bf16"),
+    (4097, 4096, 192, 4, 32, "bf16", "f16"),
 ]
 
 
@@ -267,7 +274,9 @@ def test_gemm_parity(m, n, k, bits, g, xdt, pdt):
     x, xf = _x_case(4000 + m + k, m, k, xdt)
     y = q.qlinear_gemm(x, pk, sc, bi, bits=bits, group_size=g, y_dtype=torch.float32)
     _sync()
-    _assert_rel(y, O.apply(xf, D), 1e-4, "gemm")
+    # the GEMM rounds each dequantized weight once to fp16 (2^-12 relative) before the fp32
+    # accumulation: ~1.5e-4 per row, inside the 2e-3 bound on products
+    _assert_rel(y, O.apply(xf, D), TOL, "gemm")
 
 
 def test_gemm_one_hot_and_bias_and_bf16_out():
@@ -280,7 +289,8 @@ def test_gemm_one_hot_and_bias_and_bf16_out():
     x = bits_to_dev(O.to_bits("bf16", xb), "bf16")
     y = q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y_dtype=torch.float32)
     _sync()
-    np.testing.assert_allclose(y.cpu().numpy(), D[:, js].T, rtol=2e-6, atol=1e-7)
+    # one-hot rows give the dequantized weights, each rounded once to fp16: within half an ulp
+    np.testing.assert_allclose(y.cpu().numpy(), D[:, js].T, rtol=2.0 ** -11, atol=3e-8)
     xr, xf = _x_case(52, 150, k, "bf16")
     lb_bits = synth.acts_bits(53, 1, n, "bf16")[0]
     yb = q.qlinear_gemm(xr, pk, sc, bi, bits=4, group_size=64, layer_bias=bits_to_dev(lb_bits, "bf16"))

@@ -108,8 +108,9 @@ def test_gemv_rejects_bad_arguments(lib):
 
 def test_gemm_rejects_missing_or_small_workspace(lib):
     need = lib.qlinear_gemm_workspace_size(2048, 4096, 4096, 64)
-    # group sums of x, group records of the weights (each padded to 256 bytes), permuted copy of x
-    assert need == 2048 * 64 * 4 + 4096 * 64 * 16 + 2048 * 4096 * 2
+    # fp16 copy of x, its row factors, the weight records (s, c) and row factors (each padded to
+    # 256 bytes)
+    assert need == 2048 * 4096 * 2 + 2048 * 4 + 4096 * 64 * 8 + 4096 * 4
     args = _gemv_args(m=2048, k=4096, n=4096)
     assert lib.qlinear_gemm(*args[:-1], None, 0, None) == QL_ERR_WORKSPACE
     assert lib.qlinear_gemm(*args[:-1], FAKE, need - 1, None) == QL_ERR_WORKSPACE

@@ -26,11 +26,12 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"),
 ]
-# Matrix-core kernels keep their accumulators in the architectural VGPRs (the VALU reads them
-# every group to apply the scales; accumulation registers would need a move per element).
+# Matrix-core kernels whose VALU reads the accumulators in the loop (to apply group scales) keep
+# them in the architectural VGPRs (accumulation registers would need a move per element); the
+# GEMM's accumulators are only read in its epilogue and may live in the accumulation registers.
 FILE_FLAGS = {
     f: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-    for f in ("gemm.hip", "experts.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip", "gemv_m8.hip")
+    for f in ("experts.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip", "gemv_m8.hip")
 }
 
 

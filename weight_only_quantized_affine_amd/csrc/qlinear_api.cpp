@@ -200,9 +200,11 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
   if (k == 0)  // no codes to read: the GEMV path writes the bias (or zeros)
     return qlinear_gemv(x, x_dtype, m, k, packed, scales, biases, param_dtype, n, bits, group_size, layer_bias, y,
                         y_dtype, stream);
-  // the kernel addresses x (and its copy) and the packed words with 32-bit buffer offsets
-  CHECK(m * k * 2 < (int64_t(1) << 31) && n * (k * bits / 8) < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
-        "%s: x (%lld x %lld) and the packed words must each be smaller than 2 GiB", fn, (long long)m, (long long)k);
+  // the kernel addresses the fp16 copy of x (rows padded to a multiple of 64) and the packed
+  // words with 32-bit buffer offsets
+  CHECK(m * ((k + 63) / 64 * 64) * 2 < (int64_t(1) << 31) && n * (k * bits / 8) < (int64_t(1) << 31),
+        QL_ERR_UNSUPPORTED, "%s: x (%lld x %lld) and the packed words must each be smaller than 2 GiB", fn,
+        (long long)m, (long long)k);
   const size_t need = qlinear_gemm_workspace_size(m, n, k, group_size);
   CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
   CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
