@@ -283,7 +283,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 64), dtype=torch.uint8, device=dev)
         avg, med = _time_launches(
-            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 10, 3, stream)
+            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 20, 60, stream)
         flop = 2.0 * m * n * k
         per[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
         tot_flop += flop
@@ -299,7 +299,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         "per_projection": per,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_kernel<4,64,bf16,bf16> + xsum pre-pass"},
+                     "kernel": "xprep16 + wprep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
     }
 
     # ---------------- routed experts, MXFP4 and Q8_0
@@ -332,7 +332,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
                 wb = blocks.numel()
         avg, med = _time_launches(
             lambda i: q.qlinear_apply_experts(fmt, copies[i % 3][0], copies[i % 3][1], ids, x, n=n, k=k,
-                                              pos_per_row=top, y=y, workspace=ws), 12, 3, stream)
+                                              pos_per_row=top, y=y, workspace=ws), 20, 20, stream)
         byts = wb + x.numel() * 2 + y.numel() * 2
         gbs = byts / (avg * 1e-3) / 1e9
         legs[f"experts_{fname}"] = {

@@ -202,6 +202,12 @@ GEMV_CASES = [
     (7, 1100, 3072, 4, 64, "f16", "bf16", "bf16"),
     # m = 5..8 with group size 32 needs 32 accumulator rows: the vector-ALU kernel
     (5, 100, 512, 4, 32, "bf16", "bf16", "f32"),
+    # 8-bit, k a multiple of 128: the matrix-core kernel with f16 products (bf16 x converted)
+    (1, 1000, 1024, 8, 64, "bf16", "bf16", "f32"),
+    (1, 300, 3072, 8, 128, "f16", "bf16", "bf16"),
+    (2, 257, 640, 8, 32, "bf16", "f16", "f32"),
+    (4, 190, 1280, 8, 64, "f16", "f16", "f32"),
+    (8, 500, 3072, 8, 64, "bf16", "bf16", "bf16"),
 ]
 
 
@@ -217,6 +223,27 @@ def test_gemv_parity(m, n, k, bits, g, xdt, pdt, ydt):
     else:
         want = O.bits_to_f64(ydt, O.to_bits(ydt, ref.astype(np.float32)))
         _assert_rel(y, want, TOL, "gemv 16-bit out vs rounded oracle")
+
+
+@pytest.mark.parametrize("bits,m", [(8, 3), (8, 8), (4, 3)])
+def test_gemv_x_row_magnitudes(bits, m):
+    """x rows from 1e-30 to 1e30 (bf16): the per-row power-of-two factor of the f16 conversion
+    keeps every row exact, so each row meets the same bound."""
+    n, k = 300, 1024
+    (pk, sc, bi), D = _affine_case(61, n, k, bits, 64, "bf16")
+    mags = np.array([1e-30, 1.0, 1e30, 3e-5, 7e4, 1e-12, 1e12, 0.0][:m], np.float32)
+    xb32 = synth.weights_f32(62, m, k, std=1.0) * mags[:, None]
+    xbits = O.to_bits("bf16", xb32)
+    y = q.qlinear_gemv(bits_to_dev(xbits, "bf16"), pk, sc, bi, bits=bits, group_size=64, y_dtype=torch.float32)
+    _sync()
+    ref = O.apply(O.bits_to_f64("bf16", xbits), D)
+    got = out_f64(y)
+    for r in range(m):
+        if mags[r] == 0.0:
+            assert np.all(got[r] == 0.0)
+            continue
+        err = np.linalg.norm(got[r] - ref[r]) / np.linalg.norm(ref[r])
+        assert err <= 1e-4, f"row {r} (|x| ~ {mags[r]:g}): rel-l2 {err:.3e}"
 
 
 def test_gemv_layer_bias_and_empty_k():
@@ -277,6 +304,18 @@ def test_gemm_parity(m, n, k, bits, g, xdt, pdt):
     # the GEMM rounds each dequantized weight once to fp16 (2^-12 relative) before the fp32
     # accumulation: ~1.5e-4 per row, inside the 2e-3 bound on products
     _assert_rel(y, O.apply(xf, D), TOL, "gemm")
+
+
+@pytest.mark.parametrize("std", [1e-7, 2e4])
+def test_gemm_weight_magnitudes(std):
+    """Rows far below and far above the fp16 range: the per-row power-of-two factor keeps each
+    dequantized weight an fp16 normal, so the error stays that of one fp16 rounding."""
+    m, n, k = 200, 300, 1024
+    (pk, sc, bi), D = _affine_case(71, n, k, 4, 64, "bf16", std=std)
+    x, xf = _x_case(72, m, k, "bf16")
+    y = q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y_dtype=torch.float32)
+    _sync()
+    _assert_rel(y, O.apply(xf, D), TOL, "gemm magnitudes")
 
 
 def test_gemm_one_hot_and_bias_and_bf16_out():
@@ -371,7 +410,7 @@ def test_gemv_batched_mixed_bits_small_list():
     _verify_decode(checks8, 8, "batched 8-bit")
 
 
-@pytest.mark.parametrize("bits,m", [(4, 1), (8, 1), (8, 8)])
+@pytest.mark.parametrize("bits,m", [(4, 1), (4, 8), (8, 1), (8, 8)])
 def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     """All 197 projections of the Qwen3-0.6B-shaped decode step in one problem-list launch (the
     bench's configuration), sampled rows of every projection against the oracle; a second launch

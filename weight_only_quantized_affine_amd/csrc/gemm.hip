@@ -12,8 +12,9 @@
 //   xprep16: per row of x, t = the exponent that brings max|x| into [2^14, 2^15); the copy
 //            x * 2^-t in fp16, permuted per 8 values to the order the code unpacking yields and
 //            zero-padded to a multiple of 64 values; the factor 2^t.
-//   wprep16: per weight row and group, the fp32 pair (s, b - 1024 s) times 2^-u, u > 0 only
-//            when a dequantized value of the row could reach 2^15 (fp16 range); the factor 2^u.
+//   wprep16: per weight row and group, the fp32 pair (s, b - 1024 s) times 2^-u, u chosen per
+//            row so that the largest possible dequantized value |b| + qmax |s| times 2^-u lies in
+//            [2^14, 2^15) (inside the fp16 range, above its subnormals); the factor 2^u.
 //   gemm16:  the product; y = acc * 2^t[m] * 2^u[n] + layer bias.
 // Dequantization: a code pair becomes the fp16 pair (1024 + q) by bit operations (magic
 // 0x6400 in each half), then one v_fma_mix per value computes fp16(fma(1024 + q, s', c'))
@@ -196,11 +197,14 @@ __global__ __launch_bounds__(256) void wprep16_kernel(const uint16_t* __restrict
     bound = fmaxf(bound, fabsf(param_to_f32<PT>(br[g])) + QMAX * fabsf(param_to_f32<PT>(sr[g])));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) bound = fmaxf(bound, __shfl_xor(bound, off));
+  // u: bound * 2^-u in [2^14, 2^15), so that every dequantized value of the row is below the fp16
+  // maximum and the row's large values are fp16 normals (small rows would otherwise fall into
+  // the fp16 subnormals and lose their relative precision)
   int u = 0;
-  if (bound >= 32768.0f) {
+  if (bound > 0.0f && bound <= 3.0e38f) {
     int e;
     (void)__builtin_frexpf(bound, &e);  // bound = f * 2^e, f in [0.5, 1)
-    u = e - 15;                         // bound * 2^-u < 2^15
+    u = e - 15;
   }
   const float f = __builtin_ldexpf(1.0f, -u);
   for (int g = lane; g < groups; g += 64) {

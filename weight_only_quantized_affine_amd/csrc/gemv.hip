@@ -15,31 +15,33 @@ hipError_t launch_gemv_m8(const GemvDesc&, const GemvDesc*, const GemvTile*, int
                           int, hipStream_t);
 
 hipError_t launch_gemv_mf_m1(const GemvDesc&, const GemvDesc*, const GemvTile*, int64_t, size_t, int, int, int, int,
-                             hipStream_t);
+                             int, hipStream_t);
 hipError_t launch_gemv_mf_m2(const GemvDesc&, const GemvDesc*, const GemvTile*, int64_t, size_t, int, int, int, int,
-                             hipStream_t);
+                             int, hipStream_t);
 hipError_t launch_gemv_mf_m4(const GemvDesc&, const GemvDesc*, const GemvTile*, int64_t, size_t, int, int, int, int,
-                             hipStream_t);
+                             int, hipStream_t);
 hipError_t launch_gemv_mf_m8(const GemvDesc&, const GemvDesc*, const GemvTile*, int64_t, size_t, int, int, int, int,
-                             hipStream_t);
+                             int, hipStream_t);
 
-int gemv_mf_batches(int64_t n, int64_t k, int g, int mt, int64_t min_tiles) {
+int gemv_mf_batches(int64_t n, int64_t k, int bits, int g, int mt, int64_t min_tiles) {
   const int64_t rows = gemv_mf_geometry(k, 1).rows_per_wg;
-  const int64_t set_bytes = rows * (k / 2);
-  int nb = set_bytes > 0 ? (int)((GEMV_MF_WG_BYTES + set_bytes / 2) / set_bytes) : 1;
+  const int64_t set_bytes = rows * (k * bits / 8);
+  const int64_t target = mt >= 8 ? GEMV_MF_WG_BYTES_M8 : GEMV_MF_WG_BYTES;
+  int nb = set_bytes > 0 ? (int)((target + set_bytes / 2) / set_bytes) : 1;
   nb = nb < 1 ? 1 : (nb > 32 ? 32 : nb);
-  while (nb > 1 && ((n + rows * nb - 1) / (rows * nb) < min_tiles || gemv_mf_lds(k, mt, g, nb).bytes > 64 * 1024))
+  while (nb > 1 &&
+         ((n + rows * nb - 1) / (rows * nb) < min_tiles || gemv_mf_lds(k, mt, g, nb).bytes > GEMV_MF_LDS_MAX))
     --nb;
   return nb;
 }
 
 hipError_t launch_gemv_mf(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m,
-                          int g, int xdt, int pdt, int ydt, size_t lds_bytes, hipStream_t s) {
+                          int bits, int g, int xdt, int pdt, int ydt, size_t lds_bytes, hipStream_t s) {
   switch (gemv_mt(m)) {
-    case 1: return launch_gemv_mf_m1(single, table, tiles, grid, lds_bytes, g, xdt, pdt, ydt, s);
-    case 2: return launch_gemv_mf_m2(single, table, tiles, grid, lds_bytes, g, xdt, pdt, ydt, s);
-    case 4: return launch_gemv_mf_m4(single, table, tiles, grid, lds_bytes, g, xdt, pdt, ydt, s);
-    default: return launch_gemv_mf_m8(single, table, tiles, grid, lds_bytes, g, xdt, pdt, ydt, s);
+    case 1: return launch_gemv_mf_m1(single, table, tiles, grid, lds_bytes, bits, g, xdt, pdt, ydt, s);
+    case 2: return launch_gemv_mf_m2(single, table, tiles, grid, lds_bytes, bits, g, xdt, pdt, ydt, s);
+    case 4: return launch_gemv_mf_m4(single, table, tiles, grid, lds_bytes, bits, g, xdt, pdt, ydt, s);
+    default: return launch_gemv_mf_m8(single, table, tiles, grid, lds_bytes, bits, g, xdt, pdt, ydt, s);
   }
 }
 

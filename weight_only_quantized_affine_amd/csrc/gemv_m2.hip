@@ -7,7 +7,7 @@ hipError_t launch_gemv_m2(const GemvDesc& single, const GemvDesc* table, const G
   return gemv_detail::launch_m<2>(single, table, tiles, grid, lds, xlds, g2, bits, xdt, pdt, ydt, s);
 }
 hipError_t launch_gemv_mf_m2(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid,
-                            size_t lds, int g, int xdt, int pdt, int ydt, hipStream_t s) {
-  return gemv_detail::launch_mf_m<2>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
+                            size_t lds, int bits, int g, int xdt, int pdt, int ydt, hipStream_t s) {
+  return gemv_detail::launch_mf_m<2>(single, table, tiles, grid, lds, bits, g, xdt, pdt, ydt, s);
 }
 }  // namespace ql

@@ -1,18 +1,21 @@
-// Decode GEMV on the matrix cores for 4-bit affine codes: y[m,n] = x[m,k] . (code*scale + bias)^T,
-// fp32 accumulation, one rounding to the output dtype -- the product of gemv_impl.hpp (Nx_quant
-// API docs, Products: apply; GPTQModel wiki "MLX Apple Silicon", Executing MLX qlinear kernels),
-// with the code-times-x sums done by v_mfma_f32_16x16x32 instead of v_dot2.
+// Decode GEMV on the matrix cores for 4- and 8-bit affine codes: y[m,n] = x[m,k] . (code*scale +
+// bias)^T, fp32 accumulation, one rounding to the output dtype -- the product of gemv_impl.hpp
+// (Nx_quant API docs, Products: apply; GPTQModel wiki "MLX Apple Silicon", Executing MLX qlinear
+// kernels), with the code-times-x sums done by v_mfma_f32_16x16x32 instead of v_dot2.
 //
 // One product D = A.B takes a 16x32 A and a 32x16 B (lane l: row or column l%16, k-slots
 // 8*(l/16)..+7; D: column l%16, rows 4*(l/16)..+3).  B is 16 weight rows, one per column: every
-// lane reads 16 bytes (32 codes) of its row, and word t of them is its k-slots in product t, so
-// four products cover a u-block of 128 codes of 16 rows.  A carries x: its row i serves one
+// lane reads 32 codes of its row (16 bytes at 4 bits, 32 at 8), and codes 8t..8t+7 of them are its
+// k-slots in product t, so four products cover a u-block of 128 codes of 16 rows.  A carries x: its row i serves one
 // (x row, group of the u-block) pair, with x in the k-slots of that group and zeros in the others,
 // so accumulator row i collects that group's sum of x*code for that x row.  Each u-block ends with
 // the fold of every accumulator element with its group's scale and bias,
 //   acc += s * (D - off*X) + b * X,   X = that group's sum of x,
-// the codes entering as 16-bit floats off + q (off = 128 for bf16 x, 1024 for f16 x; exact), so
-// that D - off*X is the group's sum of x*q.
+// the codes entering as 16-bit floats off + q (exact), so that D - off*X is the group's sum of
+// x*q: 4-bit codes as bf16 128 + q with bf16 x and as f16 1024 + q with f16 x; 8-bit codes always
+// as f16 1024 + q (bf16 has too few bits for 128 + q), with bf16 x converted to f16 after an exact
+// power-of-two scaling per x row that brings max |x| into [2^14, 2^15) (every bf16 value of that
+// row within 2^31 of the maximum converts exactly); the row's factor is applied at the end.
 //
 // x is staged once per workgroup in LDS, permuted to the order the code unpacking gives, with a
 // zero row that the lanes of non-matching (row, group) pairs read, and the table of group sums.
@@ -21,6 +24,8 @@
 // cache policy: a 128-byte line is consumed by two consecutive u-blocks.
 #pragma once
 #include "gemv_impl.hpp"
+
+#include <type_traits>
 
 namespace ql {
 namespace gemv_detail {
@@ -51,9 +56,9 @@ template <> __device__ __forceinline__ float half_param<F16>(uint32_t w, bool hi
 constexpr int MNU = GEMV_MF_NU;  // u-blocks per step
 constexpr int MRS = GEMV_MF_RS;  // 16-row sets per wave
 
-// Loads of one step: per row set and u-block, the lane's 16 bytes of codes.
-struct MfBuf {
-  u32x4_t w[MRS][MNU];
+// Loads of one step: per row set and u-block, the lane's 32 codes (WPB = 1 or 2 16-byte loads).
+template <int WPB> struct MfBuf {
+  u32x4_t w[MRS][MNU][WPB];
 };
 
 // The (scale | bias << 16) words of the u-block's groups for one row, from LDS (G = 32: four
@@ -78,10 +83,14 @@ template <> struct MfParams<128> {
   __device__ __forceinline__ void load(const uint8_t* p) { v[0] = *(const uint32_t*)p; }
 };
 
-template <int MT, int G, typename XT, typename PT>
+template <int MT, int G, typename XT, typename PT, int BITS>
 __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc single, const GemvDesc* __restrict__ table,
                                                       const GemvTile* __restrict__ tiles, int ydt) {
-  using U = Unpack<4, XT>;
+  // CT: the 16-bit type of the products' operands; x is converted (and scaled) to it when it differs
+  using CT = typename std::conditional<BITS == 8, F16, XT>::type;
+  constexpr bool kConvX = !std::is_same<CT, XT>::value;
+  constexpr int WPB = BITS / 4;  // 16-byte loads per row and u-block
+  using U = Unpack<BITS, CT>;
   constexpr int GU = gemv_mf_gu(G);                // groups per u-block
   constexpr int NR = MT * GU < 4 ? MT * GU : 4;    // accumulator registers a lane folds
   constexpr int GW = 128 / GU;                     // x values of one accumulator row per u-block
@@ -104,7 +113,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   const GemvMfGeom geo = gemv_mf_geometry(k, d.batches);
   const int UB = geo.ublocks, SR = geo.steps_per_row, KP = geo.kpad, XP = KP + 8;
   const int groups = (int)(k / G);
-  const int row_bytes = (int)(k / 2);
+  const int row_bytes = (int)(k * BITS / 8);
   const int steps = geo.batches * SR;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 15, h = lane >> 4;
@@ -120,24 +129,27 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   const int lrow0 = wave * 16 * MRS + j;  // this lane's weight row in row set 0 of batch 0
   constexpr int kSetRows = 64 * MRS;       // rows of one batch of the workgroup
 
-  auto issue = [&](int st, MfBuf& q) __attribute__((always_inline)) {
+  auto issue = [&](int st, MfBuf<WPB>& q) __attribute__((always_inline)) {
     const int b = st / SR, i = st - b * SR;
     const bool live = st < steps;
 #pragma unroll
     for (int rs = 0; rs < MRS; ++rs) {
       const int lr = lrow0 + b * kSetRows + rs * 16;
-      const int vw = live ? lr * row_bytes + 16 * h : kOOB;
+      const int vw = live ? lr * row_bytes + 16 * WPB * h : kOOB;
 #pragma unroll
       for (int u = 0; u < MNU; ++u) {
         const int ub = min(i * MNU + u, UB - 1);
-        q.w[rs][u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, ub * 64, GEMV_MF_AUX));
+#pragma unroll
+        for (int c = 0; c < WPB; ++c)
+          q.w[rs][u][c] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + 16 * c, ub * 64 * WPB, GEMV_MF_AUX));
       }
     }
   };
 
   // NB step buffers in rotation: the loads of step s + NB - 1 are issued before step s is computed.
   constexpr int NB = GEMV_MF_NB;
-  MfBuf buf[NB];
+  MfBuf<WPB> buf[NB];
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) issue(t, buf[t]);
 
@@ -146,6 +158,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   //    then the workgroup's scales and biases as (scale | bias << 16) words, `groups` per row.
   const GemvMfLds lay = gemv_mf_lds(k, MT, G, d.batches);
   float* xsum = (float*)((uint8_t*)sx + lay.xsum_off);
+  float* xscale = (float*)((uint8_t*)sx + lay.xscale_off);
   uint8_t* sp = (uint8_t*)sx + lay.param_off;
   {
     // rows of the workgroup that exist, times groups / 2 words of scales (and of biases); read
@@ -158,23 +171,62 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       *(u32x2_t*)(sp + 8 * t) = u32x2_t{perm(bw, sw, 0x05040100u), perm(bw, sw, 0x07060302u)};
     }
   }
+  gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
+  const int c8n = KP / 8;
+  // bf16 x into f16 products: per x row the factor 2^-t that brings max |x| into [2^14, 2^15)
+  // (t clamped to [-100, 100]; 2^t is kept for the end)
+  float xmul[MT];
+  if constexpr (kConvX) {
+    __shared__ uint32_t s_amax[MT];
+    if (threadIdx.x < MT) s_amax[threadIdx.x] = 0u;
+    __syncthreads();
+    for (int t = threadIdx.x; t < MT * c8n; t += 256) {
+      const int xr = t / c8n, c8 = t - xr * c8n;
+      if (xr < m && c8 * 8 < k) {
+        const u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+        uint32_t a = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a = max(a, max(raw[e] & 0x7fffu, (raw[e] >> 16) & 0x7fffu));
+        atomicMax(&s_amax[xr], a);  // |x| of bf16 bits orders as the integer bits
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < MT; ++r) {
+      const uint32_t a = s_amax[r];
+      const int e = (int)(a >> 7) - 127;  // a in [2^e, 2^(e+1)) for a normal value
+      const int t = a == 0u ? 0 : min(100, max(-100, e - 14));
+      xmul[r] = __builtin_ldexpf(1.0f, -t);
+      if (threadIdx.x == 0) xscale[r] = __builtin_ldexpf(1.0f, t);
+    }
+  }
   {
     // One thread per 8 values: stage them, and sum them with the GW/8 neighbours of the same
     // accumulator row and u-block (aligned lane groups; (MT+1) * KP/8 is a multiple of 16).
-    gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
-    const int c8n = KP / 8;
     constexpr int GL = GW / 8;  // lanes per x sum: 16, 8 or 4
     for (int t = threadIdx.x; t < (MT + 1) * c8n; t += 256) {
       const int xr = t / c8n, c8 = t - xr * c8n;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (xr < m && c8 * 8 < k) {
-        const u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+        u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+        if constexpr (kConvX) {
+          float f = 1.0f;
+#pragma unroll
+          for (int r = 0; r < MT; ++r)
+            if (xr == r) f = xmul[r];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const _Float16 lo = (_Float16)(__uint_as_float(raw[e] << 16) * f);
+            const _Float16 hi = (_Float16)(__uint_as_float(raw[e] & 0xffff0000u) * f);
+            raw[e] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+        }
         v = U::xperm(raw);
       }
       *(u32x4_t*)&sx[xr * XP + 8 * c8] = v;
       float sum = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sum = dot2(XT{}, v[e], XTraits<XT>::kOnes, sum);
+      for (int e = 0; e < 4; ++e) sum = dot2(CT{}, v[e], XTraits<CT>::kOnes, sum);
       sum = group_sum(sum, GL);
       const int ub = c8 >> 4, gp = (c8 & 15) / GL;
       if (xr < MT && (c8 & (GL - 1)) == 0) xsum[ub * 16 + xr * GU + gp] = sum;
@@ -213,10 +265,12 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       const float add = (lbg && rowok) ? x_to_f32<XT>(lbg[wg_row + lr]) : 0.0f;
 #pragma unroll
       for (int p = 0; p < NR / GU; ++p) {
-        float v = add;
+        const int xr = (4 * h) / GU + p;
+        float v = 0.0f;
 #pragma unroll
         for (int e = 0; e < GU; ++e) v += acc[rs][p * GU + e];
-        const int xr = (4 * h) / GU + p;
+        if constexpr (kConvX) v *= xscale[xr < MT ? xr : 0];
+        v += add;
         const int64_t el = (int64_t)xr * n + wg_row + lr;
         const int off = (rowok && xr < m) ? (int)(el * esz) : kOOB;
         if (esz == 4)
@@ -230,7 +284,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
     }
   };
 
-  auto compute = [&](int b, int i, const MfBuf& q) __attribute__((always_inline)) {
+  auto compute = [&](int b, int i, const MfBuf<WPB>& q) __attribute__((always_inline)) {
     // this lane's parameter words of u-block i * MNU, per row set
     const uint8_t* pb = sp + ((lrow0 + b * kSetRows) * groups + i * MNU * GU) * 4;
 #pragma unroll
@@ -242,11 +296,13 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       const f32x4_t X = *(const f32x4_t*)(xbase + ub * 64);
 #pragma unroll
       for (int rs = 0; rs < MRS; ++rs) {
+        // 16 operand words: product t takes words 4t .. 4t+3 (codes 8t .. 8t+7 of the lane's 32)
         uint32_t c[16];
-        U::codes(q.w[rs][u], c, mk, mg);
+#pragma unroll
+        for (int w = 0; w < WPB; ++w) U::codes(q.w[rs][u][w], c + (16 / WPB) * w, mk, mg);
         f32x4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) D = MfOp<XT>::mma(a[t], u32x4_t{c[4 * t], c[4 * t + 1], c[4 * t + 2], c[4 * t + 3]}, D);
+        for (int t = 0; t < 4; ++t) D = MfOp<CT>::mma(a[t], u32x4_t{c[4 * t], c[4 * t + 1], c[4 * t + 2], c[4 * t + 3]}, D);
         // past UB the words of the row's last u-block stand in (finite; they meet zeros)
         MfParams<G> pr;
         pr.load(pb + (rs * 16 * groups + min(u, UB - 1 - i * MNU) * GU) * 4);
@@ -265,7 +321,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
     }
   };
 
-  auto run = [&](int st, const MfBuf& q) __attribute__((always_inline)) {
+  auto run = [&](int st, const MfBuf<WPB>& q) __attribute__((always_inline)) {
     if (st < steps) {
       const int b = st / SR, i = st - b * SR;
       compute(b, i, q);
@@ -282,31 +338,39 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   }
 }
 
-template <int MT, int G, typename XT, typename PT>
+template <int MT, int G, typename XT, typename PT, int BITS>
 hipError_t launch_mf_t(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid,
                        size_t lds_bytes, int ydt, hipStream_t s) {
-  gemv_mf_kernel<MT, G, XT, PT><<<(unsigned)grid, 256, lds_bytes, s>>>(single, table, tiles, ydt);
+  gemv_mf_kernel<MT, G, XT, PT, BITS><<<(unsigned)grid, 256, lds_bytes, s>>>(single, table, tiles, ydt);
   return hipGetLastError();
 }
 
-template <int MT, int G>
+template <int MT, int G, int BITS>
 hipError_t launch_mf_g(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid,
                        size_t lds, int xdt, int pdt, int ydt, hipStream_t s) {
   const bool xb = xdt == DT_BF16, pb = pdt == DT_BF16;
-  if (xb && pb) return launch_mf_t<MT, G, BF16, BF16>(single, table, tiles, grid, lds, ydt, s);
-  if (xb) return launch_mf_t<MT, G, BF16, F16>(single, table, tiles, grid, lds, ydt, s);
-  if (pb) return launch_mf_t<MT, G, F16, BF16>(single, table, tiles, grid, lds, ydt, s);
-  return launch_mf_t<MT, G, F16, F16>(single, table, tiles, grid, lds, ydt, s);
+  if (xb && pb) return launch_mf_t<MT, G, BF16, BF16, BITS>(single, table, tiles, grid, lds, ydt, s);
+  if (xb) return launch_mf_t<MT, G, BF16, F16, BITS>(single, table, tiles, grid, lds, ydt, s);
+  if (pb) return launch_mf_t<MT, G, F16, BF16, BITS>(single, table, tiles, grid, lds, ydt, s);
+  return launch_mf_t<MT, G, F16, F16, BITS>(single, table, tiles, grid, lds, ydt, s);
+}
+
+template <int MT, int BITS>
+hipError_t launch_mf_b(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid,
+                       size_t lds, int g, int xdt, int pdt, int ydt, hipStream_t s) {
+  if (g == 128) return launch_mf_g<MT, 128, BITS>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
+  if (g == 64) return launch_mf_g<MT, 64, BITS>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
+  if constexpr (MT * gemv_mf_gu(32) <= 16) {
+    if (g == 32) return launch_mf_g<MT, 32, BITS>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int MT>
 hipError_t launch_mf_m(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid,
-                       size_t lds, int g, int xdt, int pdt, int ydt, hipStream_t s) {
-  if (g == 128) return launch_mf_g<MT, 128>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
-  if (g == 64) return launch_mf_g<MT, 64>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
-  if constexpr (MT * gemv_mf_gu(32) <= 16) {
-    if (g == 32) return launch_mf_g<MT, 32>(single, table, tiles, grid, lds, xdt, pdt, ydt, s);
-  }
+                       size_t lds, int bits, int g, int xdt, int pdt, int ydt, hipStream_t s) {
+  if (bits == 8) return launch_mf_b<MT, 8>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
+  if (bits == 4) return launch_mf_b<MT, 4>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
   return hipErrorInvalidValue;
 }
 

@@ -77,14 +77,20 @@ struct GemvLds {
 };
 GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 
-// Matrix-core GEMV (4-bit codes, k a multiple of 128): a wave owns 16 * GEMV_MF_RS weight rows
-// and walks them in u-blocks of 128 codes (64 bytes of each row); GEMV_MF_NU u-blocks make one
-// pipeline step.  A 256-thread workgroup walks `batches` sets of 64 * GEMV_MF_RS rows.
+// Matrix-core GEMV (4- or 8-bit codes, k a multiple of 128): a wave owns 16 * GEMV_MF_RS weight
+// rows and walks them in u-blocks of 128 codes (64 or 128 bytes of each row); GEMV_MF_NU u-blocks
+// make one pipeline step.  A 256-thread workgroup walks `batches` sets of 64 * GEMV_MF_RS rows.
 #ifndef GEMV_MF_NU
 #define GEMV_MF_NU 2
 #endif
 #ifndef GEMV_MF_WG_BYTES
-#define GEMV_MF_WG_BYTES 32768  // packed bytes per workgroup the batch count aims at
+#define GEMV_MF_WG_BYTES 32768  // packed bytes per workgroup the batch count aims at (one x row)
+#endif
+#ifndef GEMV_MF_WG_BYTES_M8
+#define GEMV_MF_WG_BYTES_M8 131072  // the same for 5 to 8 x rows (staging x costs more per workgroup)
+#endif
+#ifndef GEMV_MF_LDS_MAX
+#define GEMV_MF_LDS_MAX (80 * 1024)  // LDS of one workgroup (two fit a compute unit)
 #endif
 #ifndef GEMV_MF_RS
 #define GEMV_MF_RS 1
@@ -120,35 +126,39 @@ __host__ __device__ inline GemvMfGeom gemv_mf_geometry(int64_t k, int batches) {
 // Groups of a u-block (1 when the group spans it) and the x rows one matrix-core pass serves.
 __host__ __device__ constexpr int gemv_mf_gu(int g) { return g >= 128 ? 1 : 128 / g; }
 // LDS of a matrix-core GEMV launch, in this order: mt x rows and one zero row of kpad + 8
-// elements; the table of x sums (one float per u-block and accumulator row); the workgroup's
-// scales and biases, interleaved per group (scale | bias << 16, one word per row and group).
+// elements; the table of x sums (one float per u-block and accumulator row); the x row factors
+// (8 floats); the workgroup's scales and biases, interleaved per group (scale | bias << 16, one
+// word per row and group).
 struct GemvMfLds {
-  size_t xsum_off, param_off, bytes;
+  size_t xsum_off, xscale_off, param_off, bytes;
 };
 __host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int batches) {
   const GemvMfGeom geo = gemv_mf_geometry(k, batches);
   GemvMfLds r;
   r.xsum_off = ((size_t)(mt + 1) * (geo.kpad + 8) * 2 + 15) / 16 * 16;
-  r.param_off = r.xsum_off + (size_t)geo.steps_per_row * GEMV_MF_NU * 16 * 4;
+  r.xscale_off = r.xsum_off + (size_t)geo.steps_per_row * GEMV_MF_NU * 16 * 4;
+  r.param_off = r.xscale_off + 32;
   r.bytes = r.param_off + (size_t)geo.rows_per_wg * (k / g) * 4;
   return r;
 }
 #ifndef GEMV_MF_ENABLE
 #define GEMV_MF_ENABLE 1
 #endif
-// Whether a problem takes the matrix-core GEMV: 4-bit codes, group size 32, 64 or 128, k a
+// Whether a problem takes the matrix-core GEMV: 4- or 8-bit codes, group size 32, 64 or 128, k a
 // multiple of 128 with an even number of groups per row, scales and biases 4-byte aligned, at
 // most 16 accumulator rows (rows of x times groups per u-block) and the LDS of one batch within
-// 64 KiB.
+// GEMV_MF_LDS_MAX.
 inline bool gemv_mf_eligible(int64_t m, int64_t k, int bits, int g, const void* scales, const void* biases) {
-  if (!GEMV_MF_ENABLE || bits != 4 || k < 128 || k % 128 != 0 || (g != 32 && g != 64 && g != 128)) return false;
+  if (!GEMV_MF_ENABLE || (bits != 4 && bits != 8) || k < 128 || k % 128 != 0 || (g != 32 && g != 64 && g != 128))
+    return false;
   if ((k / g) % 2 != 0 || ((uintptr_t)scales | (uintptr_t)biases) % 4 != 0) return false;
   const int mt = gemv_mt(m);
-  return mt * gemv_mf_gu(g) <= 16 && gemv_mf_lds(k, mt, g, 1).bytes <= 64 * 1024;
+  return mt * gemv_mf_gu(g) <= 16 && gemv_mf_lds(k, mt, g, 1).bytes <= GEMV_MF_LDS_MAX;
 }
-// Batches per workgroup: about GEMV_MF_WG_BYTES of packed words, fewer when `min_tiles` workgroups
-// would otherwise not be reached or the LDS would pass 64 KiB.
-int gemv_mf_batches(int64_t n, int64_t k, int g, int mt, int64_t min_tiles);
+// Batches per workgroup: about GEMV_MF_WG_BYTES (GEMV_MF_WG_BYTES_M8 for mt = 8) of packed words,
+// fewer when `min_tiles` workgroups would otherwise not be reached or the LDS would pass
+// GEMV_MF_LDS_MAX.
+int gemv_mf_batches(int64_t n, int64_t k, int bits, int g, int mt, int64_t min_tiles);
 
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, int bits, int g, int pdt, uint32_t* packed,
                            void* scales, void* biases, hipStream_t s);
@@ -162,9 +172,9 @@ hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, v
 // (all problems of one launch share the row-count template of m and bits).
 hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m,
                        int bits, int xdt, int pdt, int ydt, size_t lds_bytes, int xlds, bool g2, hipStream_t s);
-// The same for the matrix-core GEMV; every problem of the launch has group size `g`.
+// The same for the matrix-core GEMV; every problem of the launch has `bits` and group size `g`.
 hipError_t launch_gemv_mf(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m,
-                          int g, int xdt, int pdt, int ydt, size_t lds_bytes, hipStream_t s);
+                          int bits, int g, int xdt, int pdt, int ydt, size_t lds_bytes, hipStream_t s);
 
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,

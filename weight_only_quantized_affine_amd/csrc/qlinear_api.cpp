@@ -165,10 +165,10 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
     hipError_t e;
     if (ql::gemv_mf_eligible(mm, k, bits, group_size, scales, biases)) {
       const int mt = ql::gemv_mt(mm);
-      d.batches = ql::gemv_mf_batches(n, k, group_size, mt, 1024);
+      d.batches = ql::gemv_mf_batches(n, k, bits, group_size, mt, 1024);
       const ql::GemvMfGeom g = ql::gemv_mf_geometry(k, d.batches);
       const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
-      e = ql::launch_gemv_mf(d, nullptr, nullptr, tiles, (int)mm, group_size, dt(x_dtype), dt(param_dtype),
+      e = ql::launch_gemv_mf(d, nullptr, nullptr, tiles, (int)mm, bits, group_size, dt(x_dtype), dt(param_dtype),
                              dt(y_dtype), ql::gemv_mf_lds(k, mt, group_size, d.batches).bytes, (hipStream_t)stream);
     } else {
       d.batches = ql::gemv_batches(n, k, bits, 1024);
@@ -242,7 +242,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
                                 probs[i].biases);
   };
   auto key = [&](int i) {
-    if (mf(i)) return (1 << 16) + ql::gemv_mt(probs[i].m) * 1024 + probs[i].group_size;
+    if (mf(i)) return (1 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256 + probs[i].group_size;
     const bool g2 = probs[i].bits == 4 && probs[i].group_size == 32;
     return ql::gemv_mt(probs[i].m) * 32 + probs[i].bits * 2 + (g2 ? 1 : 0);
   };
@@ -277,7 +277,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       d.group_size = p.group_size;
       c.m = std::max<int>(c.m, (int)p.m);
       if (c.mf_g) {
-        d.batches = ql::gemv_mf_batches(p.n, p.k, p.group_size, ql::gemv_mt(p.m), 1);
+        d.batches = ql::gemv_mf_batches(p.n, p.k, p.bits, p.group_size, ql::gemv_mt(p.m), 1);
         const ql::GemvMfGeom g = ql::gemv_mf_geometry(p.k, d.batches);
         lds_x = std::max(lds_x, ql::gemv_mf_lds(p.k, ql::gemv_mt(p.m), p.group_size, d.batches).bytes);
         const int64_t t = (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
@@ -363,7 +363,7 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
   for (const BatchedPlan::Cls& c : plan.classes) {
     ql::GemvDesc none{};
     hipError_t e =
-        c.mf_g ? ql::launch_gemv_mf(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.mf_g,
+        c.mf_g ? ql::launch_gemv_mf(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits, c.mf_g,
                                     dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s)
                : ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
                                  dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, c.xlds, c.g2, s);
