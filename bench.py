@@ -259,7 +259,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
     for bits, m in ((8, 1), (8, 8), (4, 8)):
         log(f"leg: {bits}-bit decode m={m}")
         sets_b, wb, io = build_decode(bits, m, 2, 30_000 + 100 * bits + m)
-        wall, avg = time_decode(sets_b, 100, 10)
+        wall, avg = time_decode(sets_b, 200, 300)
         legs[f"decode_{bits}bit_m{m}"] = {
             "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 2),
             "kernel_ms": round(avg, 5),

@@ -152,7 +152,8 @@ ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
  * x_dtype must be QL_BF16 (MXFP4 values are exact in bf16, and so are int8 codes); y is
  * [n_pos, n] in y_dtype.  k % 32 == 0; 0 <= e <= 4096.  Needs a workspace of
  * qlinear_apply_experts_workspace_size(n_pos, e) bytes (routing scratch: offsets then perm,
- * as qlinear_route writes them). */
+ * as qlinear_route writes them, each padded to 16 bytes, then the e experts in decreasing order
+ * of their position counts). */
 size_t qlinear_apply_experts_workspace_size(int64_t n_pos, int64_t e);
 ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, int64_t e,
                                 int64_t n, int64_t k, const int64_t* ids, int64_t n_pos,

@@ -514,6 +514,36 @@ def test_apply_experts_small(fmt, ydt):
 
 
 @pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
+@pytest.mark.parametrize("e,n,k,tokens,top,skew", [
+    (3, 300, 288, 100, 2, True),    # one expert with ~150 positions (two chunks), k % 64 == 32
+    (300, 64, 64, 50, 4, False),    # most experts empty; the expert order spans two workgroups
+    (4, 520, 1024, 70, 4, False),   # weight-row tiles of 384 and 136 rows
+    (2, 100, 4160, 20, 2, False),   # k too long for staging the scale bytes in LDS
+])
+def test_apply_experts_chunks_and_shapes(fmt, e, n, k, tokens, top, skew):
+    seed = 700 + e + n
+    if fmt == q.QL_MXFP4:
+        codes, scales = synth.mxfp4_codes_scales(seed, e, n, k)
+        W = O.mxfp4_dequant_f32(codes, scales)
+        w0, w1 = u8_to_dev(codes), u8_to_dev(scales)
+    else:
+        blocks = O.q8_0_quantize(synth.weights_f32(seed, e * n, k).reshape(e, n, k))
+        W = O.q8_0_dequant_f32(blocks)
+        w0, w1 = u8_to_dev(blocks), None
+    g = np.random.default_rng(seed)
+    ids = g.integers(0, e, size=(tokens, top)).astype(np.int64)
+    if skew:
+        ids[:, 0] = 0
+        ids[: tokens // 2, 1] = 0
+    xb = synth.acts_bits(seed + 1, tokens, k, "bf16")
+    y = q.qlinear_apply_experts(fmt, w0, w1, torch.from_numpy(ids.reshape(-1)).to(DEV), bits_to_dev(xb, "bf16"), n=n,
+                                k=k, pos_per_row=top, y_dtype=torch.float32)
+    _sync()
+    ref = O.apply_experts(W, ids.reshape(-1), O.bits_to_f64("bf16", xb), pos_per_row=top)
+    _assert_rel(y, ref, 1e-4, "experts shapes")
+
+
+@pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
 def test_apply_experts_full_size_sampled_and_row_independent(fmt):
     """32 experts of 5760x2880, 512 tokens x top-4 (the routed-experts workload): 64 sampled
     positions x 96 sampled output rows against the oracle; a position's row keeps its bits when

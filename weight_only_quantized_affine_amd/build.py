@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqlinear.so")
 SOURCES = ["qlinear_api.cpp", "quantize.hip", "dequant.hip", "gemv.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip",
-           "gemv_m8.hip", "gemm.hip", "experts.hip"]
+           "gemv_m8.hip", "gemm.hip", "experts.hip", "experts_mx.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

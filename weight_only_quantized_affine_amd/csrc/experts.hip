@@ -15,11 +15,11 @@
 //   MXFP4: a byte of codes becomes a bf16 pair with the scaled conversion of CDNA4, which applies
 //          the block scale 2^(s-127) exactly (NaN for s == 255).
 //   Q8_0:  int8 codes become exact bf16; each 32-block's fp32 partial sum is scaled by its d.
-#include "device_common.hpp"
-#include "launch.hpp"
+#include "experts_common.hpp"
 
 namespace ql {
 namespace {
+using namespace ex_detail;
 
 // ---------------------------------------------------------------- routing
 
@@ -79,6 +79,21 @@ __global__ __launch_bounds__(256) void zero_unrouted_kernel(const int64_t* __res
   for (int64_t i = threadIdx.x; i < n * esz / 2; i += 256) ((uint16_t*)row)[i] = 0;
 }
 
+// Experts in decreasing order of their position counts (ties by index): order[rank] = expert.
+// The apply launch walks them in this order, so that the largest tasks start first.
+__global__ __launch_bounds__(256) void expert_order_kernel(const int32_t* __restrict__ offsets, int64_t e,
+                                                           int32_t* __restrict__ order) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= e) return;
+  const int32_t cj = offsets[j + 1] - offsets[j];
+  int32_t rank = 0;
+  for (int64_t i = 0; i < e; ++i) {
+    const int32_t ci = offsets[i + 1] - offsets[i];
+    rank += (ci > cj || (ci == cj && i < j)) ? 1 : 0;
+  }
+  order[rank] = (int32_t)j;
+}
+
 // ---------------------------------------------------------------- routed apply
 
 constexpr int EBK = 64, EMC = 96;  // k / positions per chunk (up to 3 m-subtiles of 32)
@@ -93,43 +108,14 @@ enum : int { FMT_MXFP4 = 1, FMT_Q8_0 = 2 };
 template <int FMT> constexpr int ex_ct() { return FMT == FMT_MXFP4 ? EX_MXFP4_CT : 1; }
 template <int FMT> constexpr int ex_bn() { return 128 * ex_ct<FMT>(); }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 __device__ __forceinline__ f32x16_t mfma_bf16(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
                                                  0, 0, 0);
 }
 
-// Raw buffer resource over `bytes` bytes at `base` (bytes < 2^31, checked by the host): loads
-// past the end return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t ex_rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-constexpr uint32_t kExOOB = 0x7ffffff0u;  // a buffer offset past every resource
-
-template <int N> __device__ __forceinline__ void ex_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // x tile swizzle: chunk c (8 values) of row r sits at 16-byte slot r*8 + (c ^ xswz(r)); keeps the
 // fragment reads of 8 and of 16 consecutive rows on distinct banks.
 __device__ __forceinline__ int ex_xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// 8 MXFP4 codes (one word: byte i holds values 2i, 2i+1 in its low/high nibble) -> bf16 operand
-// registers (v0,v1),(v2,v3),(v4,v5),(v6,v7) with the CDNA4 scaled conversion
-// (v_cvt_scalef32_pk_bf16_fp4: one byte = two E2M1 codes, low nibble into the low half, times an
-// fp32 scale, rounded to bf16).  With scale = 2^(s-127) the products have at most two
-// significant bits, so they are exact for every scale byte s <= 254 (s = 0 gives bf16
-// subnormals), overflow to inf where the format does, and a NaN scale (s = 255) gives NaN.
-__device__ __forceinline__ u32x4_t decode_mxfp4(uint32_t w, float scale) {
-  u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
-  return r;
-}
 
 // Two int8 values (low bytes of a and b) -> packed bf16 pair, exact.
 __device__ __forceinline__ uint32_t pack2_bf16_i8(uint32_t a, uint32_t b) {
@@ -443,7 +429,7 @@ hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
 
 hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
-                                void* y, int ydt, int32_t* offsets, int32_t* perm, hipStream_t s) {
+                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, hipStream_t s) {
   (void)xdt;
   zero_unrouted_kernel<<<(unsigned)n_pos, 256, 0, s>>>(ids, n_pos, e, n, y, ydt, k == 0 ? 1 : 0);
   hipError_t err = hipGetLastError();
@@ -451,6 +437,13 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
   err = launch_route(ids, n_pos, e, offsets, perm, s);
   if (err != hipSuccess) return err;
   const int64_t x_rows = n_pos / pos_per_row;
+  if (fmt == FMT_MXFP4) {
+    expert_order_kernel<<<(unsigned)((e + 255) / 256), 256, 0, s>>>(offsets, e, order);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_experts_mx((const uint8_t*)w0, (const uint8_t*)w1, e, n, k, offsets, perm, order,
+                             (const uint16_t*)x, x_rows, pos_per_row, y, ydt, s);
+  }
   const int64_t bn = fmt == FMT_MXFP4 ? ex_bn<FMT_MXFP4>() : ex_bn<FMT_Q8_0>();
   const int64_t grid = e * ((n + bn - 1) / bn);
   if (fmt == FMT_MXFP4)

@@ -1,0 +1,272 @@
+// Routed apply for MXFP4 experts (Nx_quant API docs, Products: apply_experts; Nx_quant Weights:
+// MXFP4): y[p, :] = x[p / pos_per_row, :] . W_{ids[p]}^T in fp32, the codes decoded while summing.
+// The routing (offsets, permutation and expert order) is computed by experts.hip.
+#include "experts_common.hpp"
+
+namespace ql {
+namespace {
+using namespace ex_detail;
+
+// ---------------------------------------------------------------- MXFP4, 48 weight rows per wave
+//
+// One workgroup of 8 waves per (expert, 384 weight rows), taken in decreasing order of the experts'
+// position counts; wave w owns three column tiles of 16 weight rows and all the chunk's positions
+// (up to 96: MS m-subtiles of 16), and multiplies with v_mfma_f32_16x16x32_bf16 (lane l: row or
+// column l%16, k-slots 8*(l/16)..+7; D: column l%16, rows 4*(l/16)..+3), so that every x fragment
+// read from LDS feeds three products and every decoded code fragment MS.  k-tiles are 128 wide: a
+// lane reads 16 bytes (one 32-value block) of its row per tile, and the four lanes of a row read 64
+// consecutive bytes, half a cache line, in one instruction.  The gathered x rows go straight into
+// XNS LDS stages, XNS - 1 k-tiles ahead, shared by the 8 waves; each lane's code words go into a
+// ring of XNS register buffers, XNS k-tiles ahead (one in-order counter, as in experts_kernel).
+// The workgroup's scale bytes (all k) are read once into LDS, coalesced, when they fit
+// (SCL_LDS); otherwise each lane loads its block's byte with its codes.
+constexpr int XBK = 128, XMC = 96, XCT = 3, XW = 8, XBN = XW * 16 * XCT, XNS = 3;
+constexpr int XSCL_MAX = 48 * 1024;  // LDS bytes for the staged scale bytes
+
+struct MxBuf {
+  u32x4_t c[XCT];   // this lane's 32 codes (block 4 kt + q of its row), per column tile
+  uint32_t s[XCT];  // that block's scale byte (per-lane loads only)
+};
+
+__device__ __forceinline__ f32x4_t mfma16_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// x stage: row r holds 16 chunks of 8 values (k-tile 128), chunk c at slot c ^ (r % 16), so that the
+// 16 rows of one fragment read hit 16 distinct bank groups.
+template <int MS, bool SCL_LDS>
+__device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
+                                         const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
+                                         __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K, int64_t N,
+                                         int64_t ncol0, const uint32_t* wo, const uint32_t* so, int64_t pos_per_row,
+                                         void* __restrict__ y, int ydt) {
+  constexpr int CPW = (MS + 1) / 2;                // x copies per wave and k-tile (32 rows per copy round)
+  constexpr int NW = SCL_LDS ? XCT : 2 * XCT;     // weight loads per lane and k-tile
+  constexpr int L = NW + (XNS - 2) * (CPW + NW);  // loads issued after x(kt) when kt is due
+  static_assert(L < 64, "vmcnt range");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j16 = lane & 15, q = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int KT = (int)((K + XBK - 1) / XBK);
+  const int kint = (int)K;
+
+  // x copies: copy i (0..CPW-1) of wave w covers chunk rows (8i + w)*4 .. +3; lane l -> row + l/16,
+  // slot l%16 (chunk (l%16) ^ (row % 16)).  Rows past the chunk copy its first position (never
+  // stored).
+  uint32_t xoff[CPW];
+  int xc[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = (XW * i + wave) * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const int32_t pos = sPos[r < rows ? r : 0];
+    xoff[i] = (uint32_t)(((int64_t)(pos / pos_per_row) * K + 8 * c) * 2);
+    xc[i] = c;
+  }
+  auto copy_x = [&](int kt, uint8_t* stage) __attribute__((always_inline)) {
+    const int k0 = kt * XBK;
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const uint32_t v = k0 + 8 * xc[i] < kint ? xoff[i] : kExOOB;  // zeros past K
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX, (lds_void*)(stage + (XW * i + wave_u) * 1024), 16, v,
+                                               (uint32_t)(k0 * 2), 0, 0);
+    }
+  };
+  auto load_w = [&](int kt, MxBuf& wb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < XCT; ++ct) {
+      wb.c[ct] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsW, wo[ct], (uint32_t)(kt * 64), 0));
+      if constexpr (!SCL_LDS) wb.s[ct] = __builtin_amdgcn_raw_buffer_load_b8(rsS, so[ct], (uint32_t)(kt * 4), 0);
+    }
+  };
+
+  f32x4_t acc[XCT][MS];
+#pragma unroll
+  for (int ct = 0; ct < XCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < MS; ++i) acc[ct][i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // k-slots: MFMA slot s of lane quadrant q at k-step t reads k = 32q + 8t + s of the tile, i.e.
+  // x chunk 4q + t and code word t of the lane's 16 bytes.
+  auto compute = [&](int kt, const uint8_t* stage, const MxBuf& wb) __attribute__((always_inline)) {
+    // the block scale 2^(s-127) as fp32 (s = 0: the subnormal 2^-127), NaN for s = 255, 0 past K
+    const bool kin = kt * XBK + 32 * q < kint;
+    float scl[XCT];
+#pragma unroll
+    for (int ct = 0; ct < XCT; ++ct) {
+      uint32_t sb;
+      if constexpr (SCL_LDS)
+        sb = sScl[so[ct] + 4 * kt];
+      else
+        sb = wb.s[ct] & 0xffu;
+      scl[ct] = !kin ? 0.0f : __uint_as_float(sb == 255u ? 0x7fc00000u : (sb == 0u ? 0x00400000u : sb << 23));
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4_t af[MS];
+#pragma unroll
+      for (int rt = 0; rt < MS; ++rt) {
+        const int r = rt * 16 + j16;
+        af[rt] = *(const u32x4_t*)(stage + (r * 16 + ((4 * q + t) ^ j16)) * 16);
+      }
+#pragma unroll
+      for (int ct = 0; ct < XCT; ++ct) {
+        const u32x4_t bf = decode_mxfp4(wb.c[ct][t], scl[ct]);
+#pragma unroll
+        for (int rt = 0; rt < MS; ++rt) acc[ct][rt] = mfma16_bf16(af[rt], bf, acc[ct][rt]);
+      }
+    }
+  };
+
+  MxBuf wbr[XNS];
+  // One k-tile: wait for its x copies and weights, barrier (every wave is done with the stage the
+  // copies below refill), copy x of kt + XNS - 1, compute, load the weights of kt + XNS into the
+  // ring slot just consumed.  Steps past the last tile (completing a round) load clamped tiles and
+  // compute nothing.
+  auto step = [&](int kt, const uint8_t* cur, uint8_t* refill, MxBuf& wb) __attribute__((always_inline)) {
+    ex_wait_vmcnt<L>();
+    __builtin_amdgcn_s_barrier();
+    copy_x(kt + XNS - 1 < KT ? kt + XNS - 1 : KT - 1, refill);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt < KT) compute(kt, cur, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(kt + XNS < KT ? kt + XNS : KT - 1, wb);
+    asm volatile("" ::: "memory");
+  };
+
+#pragma unroll
+  for (int t = 0; t < XNS - 1; ++t) {
+    copy_x(t < KT ? t : KT - 1, stg[t]);
+    asm volatile("" ::: "memory");
+    load_w(t < KT ? t : KT - 1, wbr[t]);
+    asm volatile("" ::: "memory");
+  }
+  load_w(XNS - 1 < KT ? XNS - 1 : KT - 1, wbr[XNS - 1]);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < XNS; ++j) step(j, stg[j], stg[(j + XNS - 1) % XNS], wbr[j]);
+  for (int kt = XNS; kt < KT; kt += XNS) {
+#pragma unroll
+    for (int j = 0; j < XNS; ++j) step(kt + j, stg[j], stg[(j + XNS - 1) % XNS], wbr[j]);
+  }
+  ex_wait_vmcnt<0>();  // no copy may still be writing LDS
+  __syncthreads();     // every wave is done with the stages before the next chunk refills them
+
+  // store: lane holds weight row ncol0 + 16 ct (column j16 of its tile) for positions 4q + r of
+  // each m-subtile
+#pragma unroll
+  for (int ct = 0; ct < XCT; ++ct) {
+    const int64_t ncol = ncol0 + 16 * ct;
+    if (ncol >= N) continue;
+#pragma unroll
+    for (int rt = 0; rt < MS; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = rt * 16 + 4 * q + r;
+        if (rr < rows) store_out(y, (int64_t)sPos[rr] * N + ncol, acc[ct][rt][r], ydt);
+      }
+  }
+}
+
+template <bool SCL_LDS>
+__device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
+                                          const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
+                                          __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K,
+                                          int64_t N, int64_t ncol0, const uint32_t* wo, const uint32_t* so,
+                                          int64_t pos_per_row, void* __restrict__ y, int ydt) {
+  switch ((rows + 15) >> 4) {
+#define QL_MX_CASE(ms)                                                                                             \
+  case ms:                                                                                                         \
+    mx_chunk<ms, SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);          \
+    break;
+    QL_MX_CASE(1)
+    QL_MX_CASE(2)
+    QL_MX_CASE(3)
+    QL_MX_CASE(4)
+    QL_MX_CASE(5)
+    default:
+      mx_chunk<6, SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+      break;
+#undef QL_MX_CASE
+  }
+}
+
+template <bool SCL_LDS>
+__global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales, int64_t e, int64_t N,
+                                                            int64_t K, const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ perm_pos,
+                                                            const int32_t* __restrict__ order,
+                                                            const uint16_t* __restrict__ x, int64_t x_rows,
+                                                            int64_t pos_per_row, void* __restrict__ y, int ydt) {
+  static_assert(XNS == 3, "the stage arrays below");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[XMC * XBK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[XMC * XBK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[XMC * XBK * 2];
+  __shared__ int32_t sPos[XMC];
+  extern __shared__ uint32_t sScl32[];  // the scale bytes of the workgroup's rows (SCL_LDS)
+  uint8_t* const stg[XNS] = {st0, st1, st2};
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j16 = lane & 15;
+  const int64_t n_tiles = (N + XBN - 1) / XBN;
+  const int64_t rank = blockIdx.x / n_tiles;
+  const int64_t nt = blockIdx.x - rank * n_tiles;
+  const int64_t ex = order[rank];
+  const int32_t off = offsets[ex];
+  const int32_t cnt = offsets[ex + 1] - off;
+  if (cnt <= 0) return;
+
+  const __amdgpu_buffer_rsrc_t rsX = ex_rsrc(x, x_rows * K * 2);
+  const __amdgpu_buffer_rsrc_t rsW = ex_rsrc(codes, e * N * (K / 2));
+  const __amdgpu_buffer_rsrc_t rsS = ex_rsrc(scales, e * N * (K / 32));
+  // this lane's weight rows of the expert, one per column tile (ncol0 + 16 ct; past N the last row
+  // stands in): byte offsets of its 16 code bytes in the first k-tile, and of its block's scale
+  // byte (in the staged LDS copy, or in the scales array)
+  const int64_t ncol0 = nt * XBN + wave * (16 * XCT) + j16;
+  const int64_t sbase = (ex * N + nt * XBN) * (K / 32);  // first scale byte of the workgroup's rows
+  const int ssh = (int)(sbase & 3);
+  uint32_t wo[XCT], so[XCT];
+#pragma unroll
+  for (int ct = 0; ct < XCT; ++ct) {
+    const int64_t wrow = ex * N + min(ncol0 + 16 * ct, N - 1);
+    wo[ct] = (uint32_t)(wrow * (K / 2) + 16 * (lane >> 4));
+    so[ct] = SCL_LDS ? (uint32_t)(ssh + (wrow - ex * N - nt * XBN) * (K / 32) + (lane >> 4))
+                     : (uint32_t)(wrow * (K / 32) + (lane >> 4));
+  }
+  if constexpr (SCL_LDS) {
+    // rows of the tile that exist, K/32 bytes each, from the aligned word at or below the first
+    const int64_t live = min((int64_t)XBN, N - nt * XBN);
+    const int nd = (int)((ssh + live * (K / 32) + 3) / 4);
+    const uint32_t a0 = (uint32_t)(sbase - ssh);
+    for (int i = tid; i < nd; i += XW * 64) sScl32[i] = __builtin_amdgcn_raw_buffer_load_b32(rsS, a0 + 4u * i, 0, 0);
+  }
+  const uint8_t* sScl = (const uint8_t*)sScl32;
+  for (int32_t mc = 0; mc < cnt; mc += XMC) {
+    const int rows = min(XMC, cnt - mc);
+    __syncthreads();  // previous chunk's readers of sPos are done (and the scale bytes are staged)
+    if (tid < XMC) sPos[tid] = tid < rows ? perm_pos[off + mc + tid] : -1;
+    __syncthreads();
+    mx_chunks<SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_t e, int64_t n, int64_t k,
+                             const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
+                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
+  const int64_t grid = e * ((n + XBN - 1) / XBN);
+  const size_t scl = (size_t)((3 + XBN * (k / 32) + 3) / 4 * 4);
+  if (scl <= (size_t)XSCL_MAX)
+    experts_mx_kernel<true><<<(unsigned)grid, XW * 64, scl, s>>>(codes, scales, e, n, k, offsets, perm, order, x,
+                                                                 x_rows, pos_per_row, y, ydt);
+  else
+    experts_mx_kernel<false><<<(unsigned)grid, XW * 64, 0, s>>>(codes, scales, e, n, k, offsets, perm, order, x,
+                                                                x_rows, pos_per_row, y, ydt);
+  return hipGetLastError();
+}
+
+}  // namespace ql

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   };
 
   // NB step buffers in rotation: the loads of step s + NB - 1 are issued before step s is computed.
-  constexpr int NB = GEMV_MF_NB;
+  constexpr int NB = MT >= 8 ? GEMV_MF_NB_M8 : GEMV_MF_NB;
   MfBuf<WPB> buf[NB];
 #pragma unroll
   for (int t = 0; t < NB - 1; ++t) issue(t, buf[t]);

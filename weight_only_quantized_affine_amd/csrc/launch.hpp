@@ -87,7 +87,7 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #define GEMV_MF_WG_BYTES 32768  // packed bytes per workgroup the batch count aims at (one x row)
 #endif
 #ifndef GEMV_MF_WG_BYTES_M8
-#define GEMV_MF_WG_BYTES_M8 131072  // the same for 5 to 8 x rows (staging x costs more per workgroup)
+#define GEMV_MF_WG_BYTES_M8 262144  // the same for 5 to 8 x rows (staging x costs more per workgroup)
 #endif
 #ifndef GEMV_MF_LDS_MAX
 #define GEMV_MF_LDS_MAX (80 * 1024)  // LDS of one workgroup (two fit a compute unit)
@@ -97,6 +97,9 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #endif
 #ifndef GEMV_MF_NB
 #define GEMV_MF_NB 2  // step buffers of the load pipeline
+#endif
+#ifndef GEMV_MF_NB_M8
+#define GEMV_MF_NB_M8 3  // the same for 5 to 8 x rows
 #endif
 #ifndef GEMV_MF_SCHED
 #define GEMV_MF_SCHED 1
@@ -183,8 +186,13 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int g);
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm,
                         hipStream_t s);
+// The MXFP4 routed apply, after routing: offsets, permutation and expert order as launch_apply_experts
+// computes them.
+hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_t e, int64_t n, int64_t k,
+                             const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
+                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
 hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
-                                void* y, int ydt, int32_t* offsets, int32_t* perm, hipStream_t s);
+                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, hipStream_t s);
 
 }  // namespace ql
