@@ -494,7 +494,7 @@ def _experts_small(fmt, seed):
 
 
 @pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
-@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+@pytest.mark.parametrize("ydt", ["f32", "bf16", "f16"])
 def test_apply_experts_small(fmt, ydt):
     (w0, w1), W, ids, xb, n, k, top = _experts_small(fmt, 61 + fmt)
     y = q.qlinear_apply_experts(fmt, w0, w1, torch.from_numpy(ids.reshape(-1)).to(DEV), bits_to_dev(xb, "bf16"), n=n,

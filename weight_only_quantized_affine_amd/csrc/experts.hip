@@ -3,9 +3,9 @@
 // other positions' experts.  Weights in MXFP4 (codes + E8M0 scales apart) or Q8_0 blocks
 // (Nx_quant Weights), decoded while summing (no stored decoded weight).
 //
-// route_kernel: workgroup j scans all ids twice: counts ids below j (its offset) then writes the
-// positions with id j in increasing order (wave ballots + an LDS prefix over the 4 waves), so the
-// permutation is a stable counting sort, identical on every run.
+// route_kernel: workgroup j counts all ids in LDS (its offset and the experts' order by count),
+// then writes the positions with id j in increasing order: a stable counting sort, identical on
+// every run.
 //
 // experts_kernel: one workgroup per (expert, 128 weight rows); its 4 waves own 32 weight rows
 // each and loop over the expert's positions in chunks of up to 96 (m-subtiles of 32) and over k
@@ -23,75 +23,102 @@ using namespace ex_detail;
 
 // ---------------------------------------------------------------- routing
 
-__global__ __launch_bounds__(256) void route_kernel(const int64_t* __restrict__ ids, int64_t n_pos, int64_t e,
-                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out) {
-  __shared__ int32_t s_wave[4];
-  __shared__ int32_t s_tot[2];
+// Workgroup j: an LDS histogram of all ids gives expert j's offset (the counts below j) and its
+// rank among the experts by count (larger counts first, ties by index); then the positions with
+// id j are written in increasing order (wave ballots + an LDS prefix over the 16 waves), so the
+// permutation is a stable counting sort, identical on every run.  With `order`, order[rank] = j.
+// With `y`, the workgroup also zeroes the output rows of the positions of its share
+// [j n_pos / e, (j+1) n_pos / e) whose id is out of [0, e).  1024 threads: one pass per 1024 ids.
+__global__ __launch_bounds__(1024) void route_kernel(const int64_t* __restrict__ ids, int64_t n_pos, int64_t e,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out,
+                                                     int32_t* __restrict__ order, void* __restrict__ y, int64_t n,
+                                                     int ydt) {
+  extern __shared__ int32_t s_hist[];  // e counts
+  __shared__ int32_t s_wave[16];
+  __shared__ int32_t s_red[2][16];
   const int64_t j = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t below = 0, mine = 0;
-  for (int64_t p = tid; p < n_pos; p += 256) {
+  for (int64_t i = tid; i < e; i += 1024) s_hist[i] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < n_pos; p += 1024) {
     const int64_t v = ids[p];
-    below += (v >= 0 && v < j) ? 1 : 0;
-    mine += (v == j) ? 1 : 0;
+    if (v >= 0 && v < e) atomicAdd(&s_hist[v], 1);
   }
-  // block sums of `below` and `mine`
+  __syncthreads();
+  const int32_t cj = s_hist[j];
+  int32_t below = 0, ahead = 0;
+  for (int64_t i = tid; i < e; i += 1024) {
+    const int32_t ci = s_hist[i];
+    below += i < j ? ci : 0;
+    ahead += (ci > cj || (ci == cj && i < j)) ? 1 : 0;
+  }
   for (int off = 32; off >= 1; off >>= 1) {
     below += __shfl_xor(below, off);
-    mine += __shfl_xor(mine, off);
+    ahead += __shfl_xor(ahead, off);
   }
-  if (tid < 2) s_tot[tid] = 0;
-  __syncthreads();
   if (lane == 0) {
-    atomicAdd(&s_tot[0], below);
-    atomicAdd(&s_tot[1], mine);
+    s_red[0][wave] = below;
+    s_red[1][wave] = ahead;
   }
   __syncthreads();
-  const int32_t base = s_tot[0];
+  int32_t base = 0, rank = 0;
+  for (int w = 0; w < 16; ++w) {
+    base += s_red[0][w];
+    rank += s_red[1][w];
+  }
   if (tid == 0) {
     offsets[j] = base;
-    if (j == e - 1) offsets[e] = base + s_tot[1];
+    if (j == e - 1) offsets[e] = base + cj;
+    if (order) order[rank] = (int32_t)j;
   }
   int32_t running = 0;
-  for (int64_t p0 = 0; p0 < n_pos; p0 += 256) {
+  for (int64_t p0 = 0; p0 < n_pos; p0 += 1024) {
     const int64_t p = p0 + tid;
     const bool hit = p < n_pos && ids[p] == j;
     const uint64_t bal = __ballot(hit);
     const int32_t in_wave = __popcll(bal & ((1ull << lane) - 1ull));
     if (lane == 0) s_wave[wave] = __popcll(bal);
     __syncthreads();
-    int32_t before = running;
-    for (int w = 0; w < wave; ++w) before += s_wave[w];
+    int32_t before = running, total = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int32_t c = s_wave[w];
+      before += w < wave ? c : 0;
+      total += c;
+    }
     if (hit) perm_out[base + before + in_wave] = (int32_t)p;
-    running += s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+    running += total;
     __syncthreads();
+  }
+  if (y) {
+    // positions of this workgroup's share whose id is out of range, 1024 at a time: listed in LDS
+    // (in any order), then their rows zeroed by all threads
+    const int64_t esz = ydt == DT_F32 ? 4 : 2;
+    int32_t* s_dead = s_hist;  // the histogram is no longer read
+    for (int64_t pb = j * n_pos / e; pb < (j + 1) * n_pos / e; pb += 1024) {
+      if (tid == 0) s_red[0][0] = 0;
+      __syncthreads();
+      const int64_t p = pb + tid;
+      if (p < (j + 1) * n_pos / e) {
+        const int64_t v = ids[p];
+        if (v < 0 || v >= e) s_dead[atomicAdd(&s_red[0][0], 1)] = tid;
+      }
+      __syncthreads();
+      const int nd = s_red[0][0];
+      for (int d = 0; d < nd; ++d) {
+        uint16_t* row = (uint16_t*)((uint8_t*)y + (pb + s_dead[d]) * n * esz);
+        for (int64_t i = tid; i < n * esz / 2; i += 1024) row[i] = 0;
+      }
+      __syncthreads();
+    }
   }
 }
 
-// Zero the output rows of positions whose id is out of [0, e) (of every position when k == 0).
-__global__ __launch_bounds__(256) void zero_unrouted_kernel(const int64_t* __restrict__ ids, int64_t n_pos, int64_t e,
-                                                            int64_t n, void* __restrict__ y, int ydt, int all_rows) {
+// Zero every output row (no expert, or k == 0: every product is empty).
+__global__ __launch_bounds__(256) void zero_rows_kernel(int64_t n, void* __restrict__ y, int ydt) {
   const int64_t p = blockIdx.x;
-  const int64_t v = ids[p];
-  if (!all_rows && v >= 0 && v < e) return;
   const int64_t esz = ydt == DT_F32 ? 4 : 2;
   uint8_t* row = (uint8_t*)y + p * n * esz;
   for (int64_t i = threadIdx.x; i < n * esz / 2; i += 256) ((uint16_t*)row)[i] = 0;
-}
-
-// Experts in decreasing order of their position counts (ties by index): order[rank] = expert.
-// The apply launch walks them in this order, so that the largest tasks start first.
-__global__ __launch_bounds__(256) void expert_order_kernel(const int32_t* __restrict__ offsets, int64_t e,
-                                                           int32_t* __restrict__ order) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= e) return;
-  const int32_t cj = offsets[j + 1] - offsets[j];
-  int32_t rank = 0;
-  for (int64_t i = 0; i < e; ++i) {
-    const int32_t ci = offsets[i + 1] - offsets[i];
-    rank += (ci > cj || (ci == cj && i < j)) ? 1 : 0;
-  }
-  order[rank] = (int32_t)j;
 }
 
 // ---------------------------------------------------------------- routed apply
@@ -423,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void experts_kernel(const uint8_t* __restri
 }  // namespace
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm, hipStream_t s) {
-  route_kernel<<<(unsigned)e, 256, 0, s>>>(ids, n_pos, e, offsets, perm);
+  route_kernel<<<(unsigned)e, 1024, (size_t)e * 4, s>>>(ids, n_pos, e, offsets, perm, nullptr, nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -431,16 +458,17 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
                                 void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, hipStream_t s) {
   (void)xdt;
-  zero_unrouted_kernel<<<(unsigned)n_pos, 256, 0, s>>>(ids, n_pos, e, n, y, ydt, k == 0 ? 1 : 0);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || e == 0 || k == 0) return err;
-  err = launch_route(ids, n_pos, e, offsets, perm, s);
+  hipError_t err;
+  if (e == 0 || k == 0) {  // no expert, or empty products: every row is zero
+    zero_rows_kernel<<<(unsigned)n_pos, 256, 0, s>>>(n, y, ydt);
+    return hipGetLastError();
+  }
+  // routing, expert order, and zero rows for the positions routed nowhere
+  route_kernel<<<(unsigned)e, 1024, (size_t)(e > 1024 ? e : 1024) * 4, s>>>(ids, n_pos, e, offsets, perm, order, y, n, ydt);
+  err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t x_rows = n_pos / pos_per_row;
   if (fmt == FMT_MXFP4) {
-    expert_order_kernel<<<(unsigned)((e + 255) / 256), 256, 0, s>>>(offsets, e, order);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     return launch_experts_mx((const uint8_t*)w0, (const uint8_t*)w1, e, n, k, offsets, perm, order,
                              (const uint16_t*)x, x_rows, pos_per_row, y, ydt, s);
   }

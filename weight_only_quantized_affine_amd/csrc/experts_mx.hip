@@ -152,21 +152,58 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     for (int j = 0; j < XNS; ++j) step(kt + j, stg[j], stg[(j + XNS - 1) % XNS], wbr[j]);
   }
   ex_wait_vmcnt<0>();  // no copy may still be writing LDS
-  __syncthreads();     // every wave is done with the stages before the next chunk refills them
+  __syncthreads();     // every wave is done with the stages: stage 0 now holds the output blocks
 
   // store: lane holds weight row ncol0 + 16 ct (column j16 of its tile) for positions 4q + r of
-  // each m-subtile
+  // each m-subtile.  When every y row is 16-byte aligned (N a multiple of 8), each m-subtile goes
+  // through this wave's 3 KB of stage 0 (16 positions x 48 columns) so that every lane writes 16
+  // contiguous bytes of one y row (y 16-byte aligned); otherwise element by element.
+  const int esz = ydt == DT_F32 ? 4 : 2;
+  if (N % 8 == 0 && ((uintptr_t)y & 15) == 0) {
+    uint8_t* wbuf = stg[0] + wave * 3072;
+    const int rb = 48 * esz;              // bytes of a staged row
+    const int nch = 16 * rb / 16;         // 16-byte chunks of a block: 96 or 192
+    const int64_t col0 = ncol0 - j16;     // the wave's first column
 #pragma unroll
-  for (int ct = 0; ct < XCT; ++ct) {
-    const int64_t ncol = ncol0 + 16 * ct;
-    if (ncol >= N) continue;
+    for (int rt = 0; rt < MS; ++rt) {
 #pragma unroll
-    for (int rt = 0; rt < MS; ++rt)
+      for (int ct = 0; ct < XCT; ++ct)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = rt * 16 + 4 * q + r;
-        if (rr < rows) store_out(y, (int64_t)sPos[rr] * N + ncol, acc[ct][rt][r], ydt);
+        for (int r = 0; r < 4; ++r) {
+          uint8_t* dst = wbuf + (4 * q + r) * rb + (16 * ct + j16) * esz;
+          const float v = acc[ct][rt][r];
+          if (esz == 4)
+            *(float*)dst = v;
+          else
+            *(uint16_t*)dst = (uint16_t)(ydt == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
+        }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS for every lane
+      asm volatile("" ::: "memory");
+      for (int i = lane; i < nch; i += 64) {
+        const int row = i / (rb / 16), c = i - row * (rb / 16);
+        const int rr = rt * 16 + row;
+        const int64_t col = col0 + c * (16 / esz);
+        if (rr < rows && col < N)
+          *(u32x4_t*)((uint8_t*)y + ((int64_t)sPos[rr] * N + col) * esz) = *(const u32x4_t*)(wbuf + i * 16);
       }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next block is written
+      asm volatile("" ::: "memory");
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < XCT; ++ct) {
+      const int64_t ncol = ncol0 + 16 * ct;
+      if (ncol >= N) continue;
+#pragma unroll
+      for (int rt = 0; rt < MS; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rt * 16 + 4 * q + r;
+          if (rr < rows) store_out(y, (int64_t)sPos[rr] * N + ncol, acc[ct][rt][r], ydt);
+        }
+    }
   }
 }
 
