@@ -153,7 +153,8 @@ ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
  * [n_pos, n] in y_dtype.  k % 32 == 0; 0 <= e <= 4096.  Needs a workspace of
  * qlinear_apply_experts_workspace_size(n_pos, e) bytes (routing scratch: offsets then perm,
  * as qlinear_route writes them, each padded to 16 bytes, then the e experts in decreasing order
- * of their position counts). */
+ * of their position counts, padded to 16 bytes, then two floats per x row: the power-of-two
+ * factors of its f16 conversion for Q8_0). */
 size_t qlinear_apply_experts_workspace_size(int64_t n_pos, int64_t e);
 ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, int64_t e,
                                 int64_t n, int64_t k, const int64_t* ids, int64_t n_pos,

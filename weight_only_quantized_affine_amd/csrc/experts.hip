@@ -28,11 +28,13 @@ using namespace ex_detail;
 // id j are written in increasing order (wave ballots + an LDS prefix over the 16 waves), so the
 // permutation is a stable counting sort, identical on every run.  With `order`, order[rank] = j.
 // With `y`, the workgroup also zeroes the output rows of the positions of its share
-// [j n_pos / e, (j+1) n_pos / e) whose id is out of [0, e).  1024 threads: one pass per 1024 ids.
+// [j n_pos / e, (j+1) n_pos / e) whose id is out of [0, e); with `xfac`, it writes the power-of-two
+// factors of its share of the x rows (for f16 products).  1024 threads: one pass per 1024 ids.
 __global__ __launch_bounds__(1024) void route_kernel(const int64_t* __restrict__ ids, int64_t n_pos, int64_t e,
                                                      int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out,
                                                      int32_t* __restrict__ order, void* __restrict__ y, int64_t n,
-                                                     int ydt) {
+                                                     int ydt, const uint16_t* __restrict__ x, int64_t x_rows,
+                                                     int64_t K, float* __restrict__ xfac) {
   extern __shared__ int32_t s_hist[];  // e counts
   __shared__ int32_t s_wave[16];
   __shared__ int32_t s_red[2][16];
@@ -109,6 +111,25 @@ __global__ __launch_bounds__(1024) void route_kernel(const int64_t* __restrict__
         for (int64_t i = tid; i < n * esz / 2; i += 1024) row[i] = 0;
       }
       __syncthreads();
+    }
+  }
+  if (xfac) {
+    // bf16 x rows: the factors 2^-t and 2^t with max |x| 2^-t in [2^14, 2^15) (t = 0 for a zero
+    // row, clamped to [-100, 100]); one wave per row, rows spread over all workgroups' waves
+    for (int64_t r = j * 16 + wave; r < x_rows; r += e * 16) {
+      uint32_t a = 0u;
+      const uint16_t* xr = x + r * K;
+      for (int64_t i = 8 * lane; i < K; i += 512) {
+        const u32x4_t v = *(const u32x4_t*)(xr + i);  // K % 32 == 0 and x 16-byte aligned
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a = max(a, max(v[c] & 0x7fffu, (v[c] >> 16) & 0x7fffu));
+      }
+      for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off));
+      if (lane == 0) {
+        const int t = a == 0u ? 0 : min(100, max(-100, (int)(a >> 7) - 127 - 14));
+        xfac[2 * r] = __builtin_ldexpf(1.0f, -t);
+        xfac[2 * r + 1] = __builtin_ldexpf(1.0f, t);
+      }
     }
   }
 }
@@ -450,13 +471,15 @@ __global__ __launch_bounds__(256, 2) void experts_kernel(const uint8_t* __restri
 }  // namespace
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm, hipStream_t s) {
-  route_kernel<<<(unsigned)e, 1024, (size_t)e * 4, s>>>(ids, n_pos, e, offsets, perm, nullptr, nullptr, 0, 0);
+  route_kernel<<<(unsigned)e, 1024, (size_t)e * 4, s>>>(ids, n_pos, e, offsets, perm, nullptr, nullptr, 0, 0,
+                                                        nullptr, 0, 0, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
-                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, hipStream_t s) {
+                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, float* xfac,
+                                hipStream_t s) {
   (void)xdt;
   hipError_t err;
   if (e == 0 || k == 0) {  // no expert, or empty products: every row is zero
@@ -464,10 +487,14 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
     return hipGetLastError();
   }
   // routing, expert order, and zero rows for the positions routed nowhere
-  route_kernel<<<(unsigned)e, 1024, (size_t)(e > 1024 ? e : 1024) * 4, s>>>(ids, n_pos, e, offsets, perm, order, y, n, ydt);
+  const int64_t x_rows = n_pos / pos_per_row;
+  route_kernel<<<(unsigned)e, 1024, (size_t)(e > 1024 ? e : 1024) * 4, s>>>(
+      ids, n_pos, e, offsets, perm, order, y, n, ydt, (const uint16_t*)x, x_rows, k, fmt == FMT_Q8_0 ? xfac : nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t x_rows = n_pos / pos_per_row;
+  if (fmt == FMT_Q8_0)
+    return launch_experts_q8((const uint8_t*)w0, e, n, k, offsets, perm, order, xfac, (const uint16_t*)x, x_rows,
+                             pos_per_row, y, ydt, s);
   if (fmt == FMT_MXFP4) {
     return launch_experts_mx((const uint8_t*)w0, (const uint8_t*)w1, e, n, k, offsets, perm, order,
                              (const uint16_t*)x, x_rows, pos_per_row, y, ydt, s);

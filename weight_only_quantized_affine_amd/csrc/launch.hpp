@@ -191,8 +191,12 @@ hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
 hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_t e, int64_t n, int64_t k,
                              const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
                              int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
+hipError_t launch_experts_q8(const uint8_t* blocks, int64_t e, int64_t n, int64_t k, const int32_t* offsets,
+                             const int32_t* perm, const int32_t* order, const float* xfac, const uint16_t* x,
+                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
 hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
-                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, hipStream_t s);
+                                void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, float* xfac,
+                                hipStream_t s);
 
 }  // namespace ql

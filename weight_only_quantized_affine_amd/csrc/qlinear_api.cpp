@@ -387,7 +387,8 @@ ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
 
 size_t qlinear_apply_experts_workspace_size(int64_t n_pos, int64_t e) {
   if (n_pos < 0 || e < 0) return 0;
-  return (size_t)(((e + 1) * 4 + 15) / 16 * 16) + (size_t)((n_pos * 4 + 15) / 16 * 16) + (size_t)e * 4;
+  return (size_t)(((e + 1) * 4 + 15) / 16 * 16) + (size_t)((n_pos * 4 + 15) / 16 * 16) +
+         (size_t)((e * 4 + 15) / 16 * 16) + (size_t)n_pos * 8;
 }
 
 ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
@@ -411,7 +412,7 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
   hipStream_t s = (hipStream_t)stream;
   if (e == 0) {  // every position is out of range: zeros
     hipError_t err = ql::launch_apply_experts((int)fmt, nullptr, nullptr, 0, n, 0, ids, n_pos, nullptr, 0,
-                                              pos_per_row, y, dt(y_dtype), nullptr, nullptr, nullptr, s);
+                                              pos_per_row, y, dt(y_dtype), nullptr, nullptr, nullptr, nullptr, s);
     return launched(err, fn);
   }
   CHECK(w0 && x, QL_ERR_NULL, "%s: w0 and x must not be NULL", fn);
@@ -435,8 +436,9 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
   int32_t* offsets = (int32_t*)workspace;
   int32_t* perm = (int32_t*)((uint8_t*)workspace + ((e + 1) * 4 + 15) / 16 * 16);
   int32_t* order = (int32_t*)((uint8_t*)perm + (n_pos * 4 + 15) / 16 * 16);
+  float* xfac = (float*)((uint8_t*)order + (e * 4 + 15) / 16 * 16);
   return launched(ql::launch_apply_experts((int)fmt, w0, w1, e, n, k, ids, n_pos, x, dt(x_dtype), pos_per_row, y,
-                                           dt(y_dtype), offsets, perm, order, s),
+                                           dt(y_dtype), offsets, perm, order, xfac, s),
                   fn);
 }
 
