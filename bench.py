@@ -342,7 +342,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
             "weights_bytes": wb,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": f"route + experts_kernel<{fname}>"},
+                         "kernel": "route_kernel + " + ("experts_mx_kernel" if fname == "mxfp4" else "experts_q8_kernel")},
         }
         del copies
         torch.cuda.empty_cache()

@@ -32,7 +32,7 @@ FLAGS = [
 # GEMM's accumulators are only read in its epilogue and may live in the accumulation registers.
 FILE_FLAGS = {
     f: ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-    for f in ("experts.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip", "gemv_m8.hip")
+    for f in ("gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip", "gemv_m8.hip")
 }
 
 
