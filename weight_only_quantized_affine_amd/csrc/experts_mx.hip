@@ -45,6 +45,10 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
   constexpr int NW = SCL_LDS ? XCT : 2 * XCT;     // weight loads per lane and k-tile
   constexpr int L = NW + (XNS - 2) * (CPW + NW);  // loads issued after x(kt) when kt is due
   static_assert(L < 64, "vmcnt range");
+  // the copies of a k-tile (1 KB each, at (XW i + w) KB) and the output blocks (3 KB per wave)
+  // stay inside one stage
+  static_assert(XW * CPW * 1024 <= XMC * XBK * 2, "x copies past the stage");
+  static_assert(XW * 3072 <= XMC * XBK * 2, "output blocks past the stage");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j16 = lane & 15, q = lane >> 4;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);

@@ -58,6 +58,11 @@ __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const
   constexpr int NW = 3 * QCT;                      // weight loads per lane and k-tile
   constexpr int L = NW + (QNS - 2) * (CPW + NW);  // loads issued after x(kt) when kt is due
   static_assert(L < 64, "vmcnt range");
+  // the copies of a k-tile (1 KB each, at (QW i + w) KB), the converted chunks and the output
+  // blocks (2 KB per wave) stay inside one stage
+  static_assert(QW * CPW * 1024 <= QMC * QBK * 2, "x copies past the stage");
+  static_assert(16 * 16 * MS * 16 <= QMC * QBK * 2, "converted chunks past the stage");
+  static_assert(QW * 2048 <= QMC * QBK * 2, "output blocks past the stage");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j16 = lane & 15, q = lane >> 4;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
