@@ -292,6 +292,10 @@ GEMM_CASES = [
     # at least two output tiles per compute unit: two workgroups per CU, two LDS stages
     (4100, 4000, 256, 4, 64, "bf16", "bf16"),
     (4097, 4096, 192, 4, 32, "bf16", "f16"),
+    # two tiles per compute unit only with 128-row tiles (ragged m, odd k-tile count)
+    (2100, 4000, 320, 4, 64, "bf16", "bf16"),
+    (2000, 4100, 192, 4, 32, "f16", "bf16"),
+    (2050, 4096, 256, 8, 64, "bf16", "bf16"),
 ]
 
 
