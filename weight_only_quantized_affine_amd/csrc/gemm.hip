@@ -12,26 +12,27 @@
 //   xprep16: per row of x, t = the exponent that brings max|x| into [2^14, 2^15); the copy
 //            x * 2^-t in fp16, permuted per 8 values to the order the code unpacking yields and
 //            zero-padded to a multiple of 64 values; the factor 2^t.
-//   wprep16: per weight row and group, the fp32 pair (s, b - 1024 s) times 2^-u, u chosen per
-//            row so that the largest possible dequantized value |b| + qmax |s| times 2^-u lies in
-//            [2^14, 2^15) (inside the fp16 range, above its subnormals); the factor 2^u.
-//   gemm16:  the product; y = acc * 2^t[m] * 2^u[n] + layer bias.
-// Dequantization: a code pair becomes the fp16 pair (1024 + q) by bit operations (magic
-// 0x6400 in each half), then one v_fma_mix per value computes fp16(fma(1024 + q, s', c'))
-// = fp16((q*s + b) * 2^-u) in fp32 with one rounding to fp16.
+//   wprep16: per weight row a power of two 2^v with every S = s 2^(24-v) and B = b 2^-v of the
+//            row below 2^15 (the largest in [2^14, 2^15)), so that S and B are exact fp16 values;
+//            per group the fp16 pair (S, B); the factor 2^v.
+//   gemm16:  the product; y = acc * 2^t[m] * 2^v[n] + layer bias.
+// Dequantization: the bits of a code pair, masked into the two halves of a word, are the fp16
+// subnormals q 2^-24 (exact); one v_pk_fma_f16 per pair computes fp16(q 2^-24 S + B) =
+// fp16((q*s + b) * 2^-v) with one rounding.
 //
 // Tiling: 256 threads (4 waves, 2 x 2), workgroup tile 256 (m) x 128 (n) x 64 (k), each wave a
 // 128 x 64 block of 4 x 2 v_mfma_f32_32x32x16_f16 tiles: one dequantized code fragment feeds four
 // products.  x, packed code and record tiles go straight from HBM into three LDS stages (up to
 // three tiles ahead of the compute); codes stay packed in LDS; each wave reads the fragments of
 // the next tile into registers while it dequantizes and multiplies the current one (one wave
-// per SIMD: the overlap has to come from within the wave).  Workgroup w takes m-tile w % m_tiles: the workgroups of one m-tile share an XCD
-// (dispatch is round-robin over the 8 XCDs) and so its L2 copy of the x rows.
+// per SIMD: the overlap has to come from within the wave).  Workgroup w takes m-tile
+// w % m_tiles: the workgroups of one m-tile share an XCD (dispatch is round-robin over the 8
+// XCDs) and so its L2 copy of the x rows.
 // MFMA operand layout (32x32x16): lane l supplies row/column l%32 and k-slots 8*(l/32)..+7; the
 // result register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 // k-slots: lane half h at k-step t (0..3) of a 64-wide k-tile takes the 8-value chunk 4h + t, so
 // a lane's codes for the whole tile are 16 (4-bit) or 32 (8-bit) consecutive bytes of its row and
-// lie in one group (g >= 32); its (s, c) pair is the record of that group.
+// lie in one group (g >= 32); its (S, B) pair is the record of that group.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -89,31 +90,28 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c) {
   return r;
 }
 
-// fp16 pair (1024 + a, 1024 + b) -> fp16 pair (fma(1024 + a, s, c), fma(1024 + b, s, c)), each
-// computed in fp32 and rounded once (v_fma_mixlo_f16 / v_fma_mixhi_f16).
-__device__ __forceinline__ uint32_t deq2(uint32_t p, float s, float c) {
-  const f16x2_t v = __builtin_bit_cast(f16x2_t, p);
-  const f16x2_t r = {(_Float16)__builtin_fmaf((float)v[0], s, c), (_Float16)__builtin_fmaf((float)v[1], s, c)};
-  return __builtin_bit_cast(uint32_t, r);
+// A code pair in the two halves of a word as fp16 subnormals (bits q: value q 2^-24, exact) ->
+// fp16(q S 2^-24 + B) per half, one v_pk_fma_f16 and one rounding: with S = s 2^(24-v) and
+// B = b 2^-v exact in fp16, the value is fp16((q s + b) 2^-v).
+__device__ __forceinline__ uint32_t deq2p(uint32_t p, f16x2_t S2, f16x2_t B2) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(f16x2_t, p), S2, B2));
 }
 
 template <int BITS> struct Deq;
 // 4-bit word (codes 0..7) -> operand pairs (0,4), (1,5), (2,6), (3,7).
 template <> struct Deq<4> {
-  __device__ __forceinline__ static void run(const uint32_t* w, uint32_t* r, float s, float c, uint32_t mk,
-                                             uint32_t mg) {
+  __device__ __forceinline__ static void runp(const uint32_t* w, uint32_t* r, f16x2_t S2, f16x2_t B2, uint32_t mk) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = deq2(((w[0] >> (4 * j)) & mk) | mg, s, c);
+    for (int j = 0; j < 4; ++j) r[j] = deq2p((w[0] >> (4 * j)) & mk, S2, B2);
   }
 };
 // Two 8-bit words (codes 0..7) -> operand pairs (0,2), (1,3), (4,6), (5,7).
 template <> struct Deq<8> {
-  __device__ __forceinline__ static void run(const uint32_t* w, uint32_t* r, float s, float c, uint32_t mk,
-                                             uint32_t mg) {
-    r[0] = deq2((w[0] & mk) | mg, s, c);
-    r[1] = deq2(((w[0] >> 8) & mk) | mg, s, c);
-    r[2] = deq2((w[1] & mk) | mg, s, c);
-    r[3] = deq2(((w[1] >> 8) & mk) | mg, s, c);
+  __device__ __forceinline__ static void runp(const uint32_t* w, uint32_t* r, f16x2_t S2, f16x2_t B2, uint32_t mk) {
+    r[0] = deq2p(w[0] & mk, S2, B2);
+    r[1] = deq2p((w[0] >> 8) & mk, S2, B2);
+    r[2] = deq2p(w[1] & mk, S2, B2);
+    r[3] = deq2p((w[1] >> 8) & mk, S2, B2);
   }
 };
 
@@ -181,7 +179,7 @@ __global__ __launch_bounds__(256) void xprep16_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- pre-pass over the weights
-// One wave per weight row: the bound of its dequantized values, then the records.
+// One wave per weight row: the largest scale and bias magnitudes, then the records.
 template <typename PT, int BITS>
 __global__ __launch_bounds__(256) void wprep16_kernel(const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ biases, int64_t N, int groups,
@@ -191,27 +189,39 @@ __global__ __launch_bounds__(256) void wprep16_kernel(const uint16_t* __restrict
   if (n >= N) return;
   const uint16_t* sr = scales + n * groups;
   const uint16_t* br = biases + n * groups;
-  constexpr float QMAX = BITS == 4 ? 15.0f : 255.0f;
-  float bound = 0.0f;
-  for (int g = lane; g < groups; g += 64)
-    bound = fmaxf(bound, fabsf(param_to_f32<PT>(br[g])) + QMAX * fabsf(param_to_f32<PT>(sr[g])));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) bound = fmaxf(bound, __shfl_xor(bound, off));
-  // u: bound * 2^-u in [2^14, 2^15), so that every dequantized value of the row is below the fp16
-  // maximum and the row's large values are fp16 normals (small rows would otherwise fall into
-  // the fp16 subnormals and lose their relative precision)
-  int u = 0;
-  if (bound > 0.0f && bound <= 3.0e38f) {
-    int e;
-    (void)__builtin_frexpf(bound, &e);  // bound = f * 2^e, f in [0.5, 1)
-    u = e - 15;
+  // v: S = s 2^(24-v) and B = b 2^-v below 2^15 for every group of the row (the largest S, or
+  // the largest B when the biases bind, in [2^14, 2^15)), so both are exact fp16 values (down to
+  // 2^-24 below the row's largest; v is clamped to [-126, 127]); the record holds (S, B)
+  float smax = 0.0f, bmax = 0.0f;
+  for (int g = lane; g < groups; g += 64) {
+    smax = fmaxf(smax, fabsf(param_to_f32<PT>(sr[g])));
+    bmax = fmaxf(bmax, fabsf(param_to_f32<PT>(br[g])));
   }
-  const float f = __builtin_ldexpf(1.0f, -u);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    smax = fmaxf(smax, __shfl_xor(smax, off));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+  }
+  int v = -126;
+  if (smax > 0.0f) {
+    int e;
+    (void)__builtin_frexpf(smax, &e);  // smax < 2^e
+    v = max(v, e + 9);
+  }
+  if (bmax > 0.0f) {
+    int e;
+    (void)__builtin_frexpf(bmax, &e);
+    v = max(v, e - 15);
+  }
+  if (smax == 0.0f && bmax == 0.0f) v = 0;
+  v = min(v, 127);
   for (int g = lane; g < groups; g += 64) {
     const float s = param_to_f32<PT>(sr[g]), b = param_to_f32<PT>(br[g]);
-    rec[n * groups + g] = make_float2(s * f, (b - 1024.0f * s) * f);
+    const uint32_t S = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(s, 24 - v));
+    const uint32_t B = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(b, -v));
+    rec[n * groups + g] = make_float2(__uint_as_float(S | (B << 16)), 0.0f);
   }
-  if (lane == 0) wsc[n] = __builtin_ldexpf(1.0f, u);
+  if (lane == 0) wsc[n] = __builtin_ldexpf(1.0f, v);
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -263,7 +273,7 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   const int KT = max(0, min(per, KT_all - kb));
   const int64_t row_bytes = K * BITS / 8;
 
-  const uint32_t mk = vconst(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu), mg = vconst(0x64006400u);
+  const uint32_t mk = vconst(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
   const int gshift = __builtin_ctz((unsigned)g);
 
   // ---- copies of one tile into a stage (every lane, every tile)
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   struct Frag {
     u32x4_t a[4][4];
     uint32_t cw[2][2 * BCH];
-    float sc[2], cc[2];
+    uint32_t sb[2];  // the fp16 pair (S, B) of each col-tile's group
   };
   auto load_frag = [&](const uint8_t* stage, Frag& f) __attribute__((always_inline)) {
     const uint8_t* sA = stage;
@@ -344,8 +354,7 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
         f.cw[ct][4 * q + 3] = v[3];
       }
       const u32x2_t rr = *(const u32x2_t*)(sR + n * RD + (G32 ? 2 * h : 0));
-      f.sc[ct] = __uint_as_float(rr[0]);
-      f.cc[ct] = __uint_as_float(rr[1]);
+      f.sb[ct] = rr[0];
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -360,7 +369,8 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       uint32_t r[4];
-      Deq<BITS>::run(&f.cw[ct][t * (BITS / 4)], r, f.sc[ct], f.cc[ct], mk, mg);
+      const f16x2_t sb = __builtin_bit_cast(f16x2_t, f.sb[ct]);
+      Deq<BITS>::runp(&f.cw[ct][t * (BITS / 4)], r, f16x2_t{sb[0], sb[0]}, f16x2_t{sb[1], sb[1]}, mk);
       bf[ct] = u32x4_t{r[0], r[1], r[2], r[3]};
     }
   };
