@@ -71,6 +71,14 @@ def test_quantize_lm_head_full_size_sampled_rows():
     np.testing.assert_array_equal(dev_to_bits(biases[rows]), obb)
 
 
+def test_quantize_deterministic():
+    w = torch.from_numpy(synth.weights_f32(91, 1000, 1024)).to(DEV)
+    a = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
+    b = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
+    _sync()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+
+
 # ============================================================ dequant
 
 
@@ -368,6 +376,10 @@ def test_gemm_prefill_9b_full_size_sampled(name, k, n):
     err = O.rel_l2_per_row(got, ref)
     print(f"{name}: max rel-l2 over sampled rows {err.max():.3e}")
     assert err.max() <= TOL
+    # a second call (its split-over-k partial sums are added in a fixed order) gives the same bits
+    y2 = q.qlinear_gemm(bits_to_dev(xb, "bf16"), pk, sc, bi, bits=4, group_size=64, y_dtype=torch.float32)
+    _sync()
+    assert torch.equal(y, y2)
 
 
 # ============================================================ batched GEMV
