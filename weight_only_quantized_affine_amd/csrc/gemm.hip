@@ -42,7 +42,6 @@ namespace ql {
 namespace {
 
 constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int kInterleave = 4;  // vector instructions scheduled after each product in the compute
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -238,6 +237,9 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
                                                                   int g, const uint16_t* __restrict__ layer_bias,
                                                                   int lb_bf16, void* __restrict__ y, int ydt,
                                                                   int splits, float* __restrict__ part) {
+  // vector instructions scheduled after each product in the compute (measured best: 4 with one
+  // workgroup per CU, 3 with two)
+  constexpr int kInterleave = TWO ? 3 : 4;
   constexpr int B_ROW = BK * BITS / 8;             // bytes of codes per weight row and tile: 32 or 64
   constexpr int BCH = B_ROW / 16;                  // 16-byte chunks per row: 2 or 4
   constexpr int A_BYTES = BM * BK * 2;             // 32 KiB
