@@ -299,7 +299,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         "per_projection": per,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "xprep16 + wprep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
+                     "kernel": "prep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
     }
 
     # ---------------- routed experts, MXFP4 and Q8_0

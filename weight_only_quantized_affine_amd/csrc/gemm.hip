@@ -8,7 +8,7 @@
 // 2^-12 relative) is the only error beyond fp32 accumulation: about 1.5e-4 relative per output
 // row for unstructured weights.  (A bf16 copy of w, 2^-9, would cost ~1.7e-3.)
 //
-// Three launches:
+// Three launches (the two pre-passes share one, prep16_kernel):
 //   xprep16: per row of x, t = the exponent that brings max|x| into [2^14, 2^15); the copy
 //            x * 2^-t in fp16, permuted per 8 values to the order the code unpacking yields and
 //            zero-padded to a multiple of 64 values; the factor 2^t.
@@ -122,10 +122,9 @@ __device__ __forceinline__ f32x16_t mfma16(const u32x4_t& a, const u32x4_t& b, c
 // ---------------------------------------------------------------- pre-pass over x
 // One workgroup per row: the row's largest magnitude, then the scaled, permuted fp16 copy.
 template <typename XT, int BITS>
-__global__ __launch_bounds__(256) void xprep16_kernel(const uint16_t* __restrict__ x, int64_t K, int64_t Kp,
-                                                      uint16_t* __restrict__ x16, float* __restrict__ xsc) {
+__device__ __forceinline__ void xprep16_row(int64_t m, const uint16_t* __restrict__ x, int64_t K, int64_t Kp,
+                                            uint16_t* __restrict__ x16, float* __restrict__ xsc) {
   __shared__ uint32_t s_max[4];
-  const int64_t m = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = (int)(K / 8), ncp = (int)(Kp / 8);
   typedef __attribute__((address_space(1))) const u32x4_t gu32x4;
@@ -178,13 +177,14 @@ __global__ __launch_bounds__(256) void xprep16_kernel(const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- pre-pass over the weights
-// One wave per weight row: the largest scale and bias magnitudes, then the records.
-template <typename PT, int BITS>
-__global__ __launch_bounds__(256) void wprep16_kernel(const uint16_t* __restrict__ scales,
-                                                      const uint16_t* __restrict__ biases, int64_t N, int groups,
-                                                      float2* __restrict__ rec, float* __restrict__ wsc) {
+// One wave per weight row (four per workgroup): the largest scale and bias magnitudes, then the
+// records.
+template <typename PT>
+__device__ __forceinline__ void wprep16_rows(int64_t blk, const uint16_t* __restrict__ scales,
+                                             const uint16_t* __restrict__ biases, int64_t N, int groups,
+                                             float2* __restrict__ rec, float* __restrict__ wsc) {
   const int lane = threadIdx.x & 63;
-  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t n = blk * 4 + (threadIdx.x >> 6);
   if (n >= N) return;
   const uint16_t* sr = scales + n * groups;
   const uint16_t* br = biases + n * groups;
@@ -221,6 +221,21 @@ __global__ __launch_bounds__(256) void wprep16_kernel(const uint16_t* __restrict
     rec[n * groups + g] = make_float2(__uint_as_float(S | (B << 16)), 0.0f);
   }
   if (lane == 0) wsc[n] = __builtin_ldexpf(1.0f, v);
+}
+
+// Both pre-passes in one launch: workgroups 0 .. M-1 take the x rows, the rest four weight rows
+// each.
+template <typename XT, typename PT, int BITS>
+__global__ __launch_bounds__(256) void prep16_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t Kp,
+                                                     uint16_t* __restrict__ x16, float* __restrict__ xsc,
+                                                     const uint16_t* __restrict__ scales,
+                                                     const uint16_t* __restrict__ biases, int64_t N, int groups,
+                                                     float2* __restrict__ rec, float* __restrict__ wsc) {
+  const int64_t b = blockIdx.x;
+  if (b < M)
+    xprep16_row<XT, BITS>(b, x, K, Kp, x16, xsc);
+  else
+    wprep16_rows<PT>(b - M, scales, biases, N, groups, rec, wsc);
 }
 
 // ---------------------------------------------------------------- main kernel
@@ -552,12 +567,9 @@ hipError_t launch_t(const void* x, int64_t m, int64_t k, const uint32_t* packed,
   float* wsc = (float*)p;
   p += pad256((size_t)n * 4u);
   float* part = splits > 1 ? (float*)p : nullptr;
-  xprep16_kernel<XT, BITS><<<(unsigned)m, 256, 0, s>>>((const uint16_t*)x, k, kp, x16, xsc);
+  prep16_kernel<XT, PT, BITS><<<(unsigned)(m + (n + 3) / 4), 256, 0, s>>>(
+      (const uint16_t*)x, m, k, kp, x16, xsc, (const uint16_t*)scales, (const uint16_t*)biases, n, groups, rec, wsc);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  wprep16_kernel<PT, BITS><<<(unsigned)((n + 3) / 4), 256, 0, s>>>((const uint16_t*)scales, (const uint16_t*)biases,
-                                                                   n, groups, rec, wsc);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int lb_bf16 = std::is_same<XT, BF16>::value ? 1 : 0;
   const uint16_t* lb = (const uint16_t*)layer_bias;
