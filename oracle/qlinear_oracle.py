@@ -8,9 +8,9 @@ Sources (cited by page title and section):
 
 * GPTQModel wiki, "MLX Apple Silicon": the Concepts table (MLX affine storage: packed uint32
   codes, scales and additive biases, value = code*scale + bias) and "Packed layouts and exact
-  transcoding" (scales/biases laid out [out, groups]; whole codes per uint32 for 2/4/8 bits,
-  little-endian bit order; GGUF Q8_0 maps to 8-bit group-32 affine with the signed byte
-  plus 128).
+  transcoding" (scales/biases laid out [out, groups]; each row one continuous little-endian
+  bitstream of codes: whole codes per uint32 for 2/4/8 bits, codes crossing words for 3/5/6
+  bits; GGUF Q8_0 maps to 8-bit group-32 affine with the signed byte plus 128).
 * tinygpt PRD "Quantized inference ... QuantizedLinear", section "Problem": 8 four-bit values
   per uint32 with per-weight ``.scales`` and ``.biases`` companions.
 * gguf2mlx-stream, section "01 Tensor-bounded streaming": MLX affine quantization into packed
@@ -44,6 +44,7 @@ __all__ = [
     "to_bits",
     "bits_to_f64",
     "round_f32_to",
+    "AFFINE_BITS",
     "pack_codes",
     "unpack_codes",
     "group_min_max",
@@ -120,33 +121,55 @@ def round_f32_to(dtype: str, a_f32):
 # --------------------------------------------------------------------------------------
 
 
+AFFINE_BITS = (2, 3, 4, 5, 6, 8)
+
+
+def _stream_unit(bits: int):
+    """(codes, words) of the repeating unit of a row's bitstream: the fewest codes that fill
+    whole uint32 words (8 codes in 1 word at 4 bits; 32 codes in 3 words at 3 bits)."""
+    d = int(np.gcd(bits, 32))
+    return 32 // d, bits // d
+
+
 def pack_codes(q, bits: int) -> np.ndarray:
     """Pack integer codes [rows, k] into uint32 words [rows, k*bits/32], low bits first.
 
-    Code c of a word sits at bit positions [bits*c, bits*(c+1)), c ascending along k
-    (whole codes per word for 2/4/8 bits, little-endian order)."""
+    GPTQModel wiki "MLX Apple Silicon", "Packed layouts and exact transcoding": each row is one
+    continuous little-endian bitstream; code i of the row occupies stream bits
+    [bits*i, bits*(i+1)) and stream bit j is bit j % 32 of word j // 32.  At 2, 4 and 8 bits
+    whole codes sit in each word; at 3, 5 and 6 bits codes cross word boundaries."""
     q = np.asarray(q, dtype=np.int64)
     rows, k = q.shape
-    per = 32 // bits
-    assert bits in (2, 4, 8) and k % per == 0
+    assert bits in AFFINE_BITS
+    uc, uw = _stream_unit(bits)
+    assert k % uc == 0, "a row must fill whole words"
     assert q.min(initial=0) >= 0 and q.max(initial=0) < (1 << bits)
-    qq = q.reshape(rows, k // per, per).astype(np.uint64)
-    words = np.zeros((rows, k // per), dtype=np.uint64)
-    for c in range(per):
-        words |= qq[:, :, c] << np.uint64(bits * c)
-    return words.astype(np.uint32)
+    qq = q.reshape(rows, k // uc, uc).astype(np.uint64)
+    words = np.zeros((rows, k // uc, uw), dtype=np.uint64)
+    for i in range(uc):
+        w, sh = divmod(bits * i, 32)
+        words[:, :, w] |= (qq[:, :, i] << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:  # the code's high bits start the next word
+            words[:, :, w + 1] |= qq[:, :, i] >> np.uint64(32 - sh)
+    return words.reshape(rows, (k // uc) * uw).astype(np.uint32)
 
 
 def unpack_codes(packed, bits: int, k: int) -> np.ndarray:
     """Inverse of :func:`pack_codes`: words [rows, k*bits/32] -> codes [rows, k] (int64)."""
     packed = np.asarray(packed, dtype=np.uint32)
-    per = 32 // bits
+    assert bits in AFFINE_BITS
+    uc, uw = _stream_unit(bits)
     rows = packed.shape[0]
-    assert packed.shape[1] * per == k
-    mask = np.uint32((1 << bits) - 1)
-    out = np.empty((rows, k // per, per), dtype=np.int64)
-    for c in range(per):
-        out[:, :, c] = (packed >> np.uint32(bits * c)) & mask
+    assert k % uc == 0 and packed.shape[1] * uc == k * uw
+    ww = packed.reshape(rows, k // uc, uw).astype(np.uint64)
+    mask = np.uint64((1 << bits) - 1)
+    out = np.empty((rows, k // uc, uc), dtype=np.int64)
+    for i in range(uc):
+        w, sh = divmod(bits * i, 32)
+        v = ww[:, :, w] >> np.uint64(sh)
+        if sh + bits > 32:
+            v = v | (ww[:, :, w + 1] << np.uint64(32 - sh))
+        out[:, :, i] = (v & mask).astype(np.int64)
     return out.reshape(rows, k)
 
 

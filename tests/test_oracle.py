@@ -64,11 +64,46 @@ def test_pack_low_bits_first_8bit_and_2bit():
     assert O.pack_codes(np.array([[1, 2, 3, 0] * 4]), 2)[0, 0] == int("".join(["00", "11", "10", "01"] * 4), 2)
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
 def test_unpack_inverts_pack(bits):
     g = np.random.default_rng(bits)
     q = g.integers(0, 1 << bits, size=(5, 128))
     np.testing.assert_array_equal(O.unpack_codes(O.pack_codes(q, bits), bits, 128), q)
+
+
+def _stream_words_from_digits(codes, bits):
+    """The row's bitstream read as one integer is the number whose base-2^bits digits (most
+    significant first) are the codes in reverse order; written out as a digit string and parsed
+    with Python's int(), then cut into little-endian 32-bit words (no shifts or masks)."""
+    digits = "0123456789abcdefghijklmnopqrstuv"
+    if bits in (2, 3, 4, 5):
+        text, base = "".join(digits[c] for c in reversed(codes)), 1 << bits
+    elif bits == 6:  # two octal digits per code
+        text, base = "".join(f"{c >> 3}{c & 7}" for c in reversed(codes)), 8
+    else:  # bits == 8: two hex digits per code
+        text, base = "".join(f"{c:02x}" for c in reversed(codes)), 16
+    raw = int(text, base).to_bytes(len(codes) * bits // 8, "little")
+    return np.frombuffer(raw, dtype="<u4")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+def test_pack_is_one_little_endian_stream_per_row(bits):
+    """Every row is one continuous little-endian bitstream (GPTQModel wiki, "Packed layouts and
+    exact transcoding"): compared with the digit-string construction on random rows."""
+    g = np.random.default_rng(100 + bits)
+    q = g.integers(0, 1 << bits, size=(4, 256))
+    packed = O.pack_codes(q, bits)
+    for r in range(q.shape[0]):
+        np.testing.assert_array_equal(packed[r], _stream_words_from_digits([int(c) for c in q[r]], bits))
+
+
+def test_pack_bitstream_golden_3_5_6bit():
+    fx = _golden("affine_bitstream_3_5_6.json")
+    for case in fx["cases"]:
+        q = np.array([case["codes"]])
+        words = np.array([int(w, 16) for w in case["words"]], dtype=np.uint32)
+        np.testing.assert_array_equal(O.pack_codes(q, case["bits"])[0], words)
+        np.testing.assert_array_equal(O.unpack_codes(words[None, :], case["bits"], q.shape[1]), q)
 
 
 # ---------------------------------------------------------------- quantizer
@@ -103,7 +138,8 @@ def _brute_codes(w, s, b, bits):
     return idx, gap
 
 
-@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "f16"), (4, 32, "bf16"), (8, 64, "bf16"), (8, 128, "f16"), (4, 128, "bf16")])
+@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "f16"), (4, 32, "bf16"), (8, 64, "bf16"), (8, 128, "f16"), (4, 128, "bf16"),
+                                        (2, 64, "bf16"), (3, 32, "f16"), (5, 128, "bf16"), (6, 64, "f16")])
 def test_quantize_codes_equal_brute_force_nearest_level(bits, g, pdt):
     n, k = 6, 256
     w = synth.weights_f32(11 + bits + g, n, k)
@@ -119,7 +155,7 @@ def test_quantize_codes_equal_brute_force_nearest_level(bits, g, pdt):
     assert diff.sum() <= 2
 
 
-@pytest.mark.parametrize("bits,pdt", [(4, "f16"), (4, "bf16"), (8, "bf16"), (8, "f16")])
+@pytest.mark.parametrize("bits,pdt", [(4, "f16"), (4, "bf16"), (8, "bf16"), (8, "f16"), (3, "bf16"), (6, "f16")])
 def test_quantize_scale_is_range_over_levels_and_bias_is_min(bits, pdt):
     """scale = RNE((max-min)/(2^bits-1)) and bias = RNE(min), with max/min found by a loop."""
     w = synth.weights_f32(5, 3, 128)
@@ -139,7 +175,8 @@ def test_quantize_scale_is_range_over_levels_and_bias_is_min(bits, pdt):
             assert bb[r, j] == want_b.view(torch.int16).numpy().view(np.uint16)[0]
 
 
-@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "bf16"), (4, 64, "f16"), (8, 32, "bf16"), (8, 64, "f16")])
+@pytest.mark.parametrize("bits,g,pdt", [(4, 64, "bf16"), (4, 64, "f16"), (8, 32, "bf16"), (8, 64, "f16"), (2, 32, "bf16"),
+                                        (5, 64, "f16"), (6, 128, "bf16")])
 def test_quantize_round_trip_bound(bits, g, pdt):
     """|w - dequant| <= s/2 inside [b, b + L*s]; outside, only by the clamp distance, which is
     bounded by the storage rounding of the min and of the scale."""
