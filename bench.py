@@ -281,7 +281,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         del w
         x = torch.randn((m, k), generator=gen(41_000 + i), device=dev).to(torch.bfloat16)
         y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 64), dtype=torch.uint8, device=dev)
+        ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 4, 64), dtype=torch.uint8, device=dev)
         avg, med = _time_launches(
             lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 20, 60, stream)
         flop = 2.0 * m * n * k

@@ -5,9 +5,11 @@
  *   - MLX affine storage: packed uint32 codes plus one scale and one ADDITIVE bias per group of
  *     k-values, value = code*scale + bias (GPTQModel wiki "MLX Apple Silicon", Concepts table;
  *     tinygpt PRD "Quantized inference ... QuantizedLinear", Problem; gguf2mlx-stream, section 01).
- *   - Packing: whole codes per uint32 for 4 and 8 bits, code c of a word at bits
- *     [bits*c, bits*(c+1)), ascending along k; scales/biases laid out [out, groups]
- *     (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact transcoding).
+ *   - Packing: each row of codes is one little-endian bitstream, code i of the row at stream
+ *     bits [bits*i, bits*(i+1)) and stream bit j in bit j % 32 of word j / 32: whole codes per
+ *     uint32 at 2, 4 and 8 bits (code c of a word at bits [bits*c, bits*(c+1))), codes crossing
+ *     words at 3, 5 and 6 bits; scales/biases laid out [out, groups] (GPTQModel wiki "MLX Apple
+ *     Silicon", Packed layouts and exact transcoding).
  *   - dequant / apply / apply_experts and the MXFP4 and Q8_0 block formats
  *     (Nx_quant API docs, Weights and Products).
  *
@@ -70,7 +72,8 @@ typedef struct {
  * order (-0 < +0); scale = RNE(fl32(mx - mn) / (2^bits - 1)); bias = RNE(mn);
  * code = clamp(round-half-even(fl32(v - bias) / scale), 0, 2^bits - 1), 0 where scale == 0.
  * IEEE fp32 arithmetic, correctly rounded division.  w must be finite (otherwise the
- * outputs are unspecified).  bits in {4, 8}; group_size in {32, 64, 128} dividing k; k % 32 == 0. */
+ * outputs are unspecified).  bits in {2, 3, 4, 5, 6, 8}; group_size in {32, 64, 128} dividing k;
+ * k % 32 == 0. */
 ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int group_size,
                            ql_dtype param_dtype, uint32_t* packed, void* scales, void* biases,
                            void* stream);
@@ -95,7 +98,7 @@ ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const v
  * y[m,n] = RNE_y( sum_k x[m,k]*(code*scale + bias) [+ layer_bias[n]] ), summed in fp32 straight
  * from the packed words (no stored decoded weight).  Built for small m (1..8); any m >= 0 works
  * (m > 8 runs in slices of 8).  x_dtype in {QL_F16, QL_BF16}; layer_bias (nullable) has x_dtype;
- * y_dtype in {QL_F32, QL_F16, QL_BF16}.  bits in {4, 8}; group_size in {32, 64, 128}. */
+ * y_dtype in {QL_F32, QL_F16, QL_BF16}.  bits in {2, 3, 4, 5, 6, 8}; group_size in {32, 64, 128}. */
 ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        const uint32_t* packed, const void* scales, const void* biases,
                        ql_dtype param_dtype, int64_t n, int bits, int group_size,
@@ -106,15 +109,17 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
  * registers and rounded once to fp16, and x enters as fp16 after an exact power-of-two scaling
  * per row; the fp16 MFMA accumulates in fp32 (error ~1.5e-4 relative per output row, from the
  * fp16 rounding of the weights).  Needs a device workspace of
- * qlinear_gemm_workspace_size(m, n, k, group_size) bytes (16-byte aligned), overwritten by the
+ * qlinear_gemm_workspace_size(m, n, k, bits, group_size) bytes (16-byte aligned), overwritten by the
  * call: the fp16 copy of x (m rows of k rounded up to a multiple of 64 values), its m row factors
  * (floats), per-group records of the weight's scales and biases (n * k/group_size pairs of
  * floats) and n row factors, each padded to 256 bytes, and, when the output has too few 256 x 128
  * tiles to fill the chip (fewer than 128), fp32 partial products of the k-ranges the call splits
  * the sum into (2 to 4 ranges: that many m x n floats), summed by a second pass in a fixed order
- * (results do not depend on timing).  The fp16 copy of x and the packed words must each be smaller
- * than 2 GiB (QL_ERR_UNSUPPORTED otherwise). */
-size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int group_size);
+ * (results do not depend on timing).  At 2, 3, 5 and 6 bits the workspace also holds the codes
+ * re-packed as one byte each (n * k bytes, the 8-bit layout), which the 8-bit kernel then reads.
+ * The fp16 copy of x, the packed words and those bytes must each be smaller than 2 GiB
+ * (QL_ERR_UNSUPPORTED otherwise).  bits in {2, 3, 4, 5, 6, 8}; group_size in {32, 64, 128}. */
+size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int bits, int group_size);
 ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        const uint32_t* packed, const void* scales, const void* biases,
                        ql_dtype param_dtype, int64_t n, int bits, int group_size,
@@ -122,7 +127,7 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        size_t ws_bytes, void* stream);
 
 /* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
- * 1/2/4/8, bits); bits and group_size may differ between problems.  `probs` is HOST memory
+ * 1/2/4/8, bits); bits (4 or 8 here) and group_size may differ between problems.  `probs` is HOST memory
  * (count entries), validated on the host like qlinear_gemv; the device table built from it (the
  * problems and their row tiles) is written to `workspace` (device memory of at least
  * qlinear_gemv_batched_workspace_size(probs, count) bytes, which depends on the shapes).

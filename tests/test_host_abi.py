@@ -57,8 +57,9 @@ def _err(lib):
 def test_quantize_rejects_bad_arguments(lib):
     assert lib.qlinear_quantize(None, 4, 64, 4, 64, BF16, None, None, None, None) == QL_ERR_NULL
     assert "must not be NULL" in _err(lib)
-    assert lib.qlinear_quantize(FAKE, 4, 64, 3, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
-    assert "bits=3" in _err(lib)
+    assert lib.qlinear_quantize(FAKE, 4, 64, 7, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
+    assert "bits=7" in _err(lib)
+    assert lib.qlinear_quantize(FAKE, 4, 64, 1, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
     assert lib.qlinear_quantize(FAKE, 4, 64, 4, 48, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_UNSUPPORTED
     assert lib.qlinear_quantize(FAKE, 4, 96, 4, 64, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_SHAPE
     assert lib.qlinear_quantize(FAKE, 4, 48, 4, 32, BF16, FAKE, FAKE, FAKE, None) == QL_ERR_SHAPE  # k % 32
@@ -96,7 +97,8 @@ def test_gemv_rejects_bad_arguments(lib):
     assert lib.qlinear_gemv(*_gemv_args(y=None)) == QL_ERR_NULL
     assert lib.qlinear_gemv(*_gemv_args(xdt=F32)) == QL_ERR_DTYPE
     assert lib.qlinear_gemv(*_gemv_args(ydt=5)) == QL_ERR_DTYPE
-    assert lib.qlinear_gemv(*_gemv_args(bits=2)) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_gemv(*_gemv_args(bits=7)) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_gemv(*_gemv_args(bits=3, x=None)) == QL_ERR_NULL  # 3 bits passes the width check
     assert lib.qlinear_gemv(*_gemv_args(k=1000)) == QL_ERR_SHAPE
     assert lib.qlinear_gemv(*_gemv_args(m=-2)) == QL_ERR_SHAPE
     assert lib.qlinear_gemv(*_gemv_args(x=FAKE + 2)) == QL_ERR_ALIGN
@@ -107,7 +109,7 @@ def test_gemv_rejects_bad_arguments(lib):
 
 
 def test_gemm_rejects_missing_or_small_workspace(lib):
-    need = lib.qlinear_gemm_workspace_size(2048, 4096, 4096, 64)
+    need = lib.qlinear_gemm_workspace_size(2048, 4096, 4096, 4, 64)
     # fp16 copy of x, its row factors, the weight records (s, c) and row factors (each padded to
     # 256 bytes)
     assert need == 2048 * 4096 * 2 + 2048 * 4 + 4096 * 64 * 8 + 4096 * 4
@@ -116,7 +118,12 @@ def test_gemm_rejects_missing_or_small_workspace(lib):
     assert lib.qlinear_gemm(*args[:-1], FAKE, need - 1, None) == QL_ERR_WORKSPACE
     assert "smaller" in _err(lib)
     assert lib.qlinear_gemm(*args[:-1], FAKE + 4, need, None) == QL_ERR_ALIGN
-    assert lib.qlinear_gemm(*_gemv_args(bits=5)[:-1], FAKE, need, None) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_gemm(*_gemv_args(bits=7)[:-1], FAKE, need, None) == QL_ERR_UNSUPPORTED
+    # bitstream widths also hold the codes as bytes: the 4-bit workspace is too small (checked
+    # before any launch)
+    need5 = lib.qlinear_gemm_workspace_size(2048, 4096, 4096, 5, 64)
+    assert need5 == need + 4096 * 4096
+    assert lib.qlinear_gemm(*_gemv_args(m=2048, k=4096, n=4096, bits=5)[:-1], FAKE, need, None) == QL_ERR_WORKSPACE
 
 
 def test_gemv_batched_validates_every_problem(lib):
@@ -131,6 +138,10 @@ def test_gemv_batched_validates_every_problem(lib):
     big_m = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 9, 256, 1024, 4, 64)
     arr = (P * 2)(good, big_m)
     assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_UNSUPPORTED
+    stream_bits = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1024, 3, 64)
+    arr = (P * 2)(good, stream_bits)
+    assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_UNSUPPORTED
+    assert "bits=3" in _err(lib)
     arr = (P * 2)(good, good)
     assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need - 1, 1, None) == QL_ERR_WORKSPACE
     assert lib.qlinear_gemv_batched(arr, 0, BF16, BF16, F32, None, 0, 1, None) == QL_OK

@@ -72,7 +72,7 @@ _SIGNATURES = {
     "qlinear_quantize": (_INT, [_P, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P]),
     "qlinear_dequant": (_INT, [_INT, _P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P]),
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
-    "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT]),
+    "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
     "qlinear_gemv_batched_workspace_size": (_SZ, [ctypes.POINTER(_Problem), _INT]),
     "qlinear_gemv_batched": (_INT, [ctypes.POINTER(_Problem), _INT, _INT, _INT, _INT, _P, _SZ, _INT, _P]),
@@ -180,8 +180,8 @@ def qlinear_gemv(x, packed, scales, biases, *, bits: int, group_size: int, layer
     return y
 
 
-def qlinear_gemm_workspace_size(m: int, n: int, k: int, group_size: int) -> int:
-    return int(load_library().qlinear_gemm_workspace_size(m, n, k, group_size))
+def qlinear_gemm_workspace_size(m: int, n: int, k: int, bits: int, group_size: int) -> int:
+    return int(load_library().qlinear_gemm_workspace_size(m, n, k, bits, group_size))
 
 
 def qlinear_gemm(x, packed, scales, biases, *, bits: int, group_size: int, layer_bias=None, y_dtype=None, y=None,
@@ -193,7 +193,7 @@ def qlinear_gemm(x, packed, scales, biases, *, bits: int, group_size: int, layer
     n = packed.shape[0]
     if y is None:
         y = torch.empty((m, n), dtype=y_dtype or x.dtype, device=x.device)
-    need = qlinear_gemm_workspace_size(m, n, k, group_size)
+    need = qlinear_gemm_workspace_size(m, n, k, bits, group_size)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _check(lib.qlinear_gemm(_ptr(x), _dt(x), m, k, _ptr(packed), _ptr(scales), _ptr(biases), _dt(scales), n, bits,

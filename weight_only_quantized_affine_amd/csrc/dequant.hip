@@ -58,6 +58,43 @@ __global__ __launch_bounds__(256) void dequant_affine_kernel(const uint32_t* __r
   for (int j = 0; j < PER / 8; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
 }
 
+// Bitstream widths (2, 3, 5, 6): each lane turns one 32-code chunk (BITS words) into 32 values.
+template <int BITS, typename PT>
+__global__ __launch_bounds__(256) void dequant_stream_kernel(const uint32_t* __restrict__ packed,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases, int64_t rows,
+                                                             int64_t k, int g, void* __restrict__ out, int odt) {
+  const int64_t chunks_per_row = k / 32;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * chunks_per_row) return;
+  const int64_t row = t / chunks_per_row;
+  const int64_t c = t - row * chunks_per_row;
+  const int64_t k0 = c * 32;
+  const int64_t gi = row * (k / g) + k0 / g;  // a chunk never straddles a group (g >= 32)
+  const float s = param_to_f32<PT>(scales[gi]);
+  const float b = param_to_f32<PT>(biases[gi]);
+  const uint32_t* src = packed + row * (k / 32 * BITS) + c * BITS;
+  uint32_t w[BITS];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) w[j] = src[j];
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf((float)stream_code<BITS>(w, i), s, b);  // one rounding
+  const int64_t o = row * k + k0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
+}
+
+template <int BITS>
+void launch_dequant_stream(const uint32_t* packed, const uint16_t* sc, const uint16_t* bi, int pdt, int64_t rows,
+                           int64_t k, int g, void* out, int odt, hipStream_t s) {
+  const unsigned nb = (unsigned)((rows * (k / 32) + 255) / 256);
+  if (pdt == DT_BF16)
+    dequant_stream_kernel<BITS, BF16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+  else
+    dequant_stream_kernel<BITS, F16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
+}
+
 // 2^(s-127) as an fp32 value (s = 0 gives the subnormal 2^-127); s == 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   if (s == 0) return __uint_as_float(0x00400000u);
@@ -123,7 +160,15 @@ hipError_t launch_dequant_affine(const uint32_t* packed, const void* scales, con
   const unsigned nb = (unsigned)((total + 255) / 256);
   const uint16_t* sc = (const uint16_t*)scales;
   const uint16_t* bi = (const uint16_t*)biases;
-  if (bits == 4 && pdt == DT_BF16)
+  if (bits == 2)
+    launch_dequant_stream<2>(packed, sc, bi, pdt, rows, k, g, out, odt, s);
+  else if (bits == 3)
+    launch_dequant_stream<3>(packed, sc, bi, pdt, rows, k, g, out, odt, s);
+  else if (bits == 5)
+    launch_dequant_stream<5>(packed, sc, bi, pdt, rows, k, g, out, odt, s);
+  else if (bits == 6)
+    launch_dequant_stream<6>(packed, sc, bi, pdt, rows, k, g, out, odt, s);
+  else if (bits == 4 && pdt == DT_BF16)
     dequant_affine_kernel<4, BF16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);
   else if (bits == 4)
     dequant_affine_kernel<4, F16><<<nb, 256, 0, s>>>(packed, sc, bi, rows, k, g, out, odt);

@@ -72,4 +72,16 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *(const u32x4_t*)p; }
 
+// Affine rows at 2, 3, 5 or 6 bits (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact
+// transcoding): each row is one little-endian bitstream, code i at stream bits [BITS i, BITS i +
+// BITS), stream bit j in bit j % 32 of word j / 32.  k is a multiple of 32, so a row is made of
+// 32-code chunks of exactly BITS words each.
+// Code i (0..31, a constant after unrolling) of a chunk held in w[0 .. BITS-1].
+template <int BITS> __device__ __forceinline__ uint32_t stream_code(const uint32_t* w, int i) {
+  const int pos = BITS * i, wi = pos >> 5, sh = pos & 31;
+  uint32_t v = w[wi] >> sh;
+  if (sh + BITS > 32) v |= w[wi + 1] << (32 - sh);  // the code continues in the next word
+  return v & ((1u << BITS) - 1u);
+}
+
 }  // namespace ql

@@ -10,8 +10,10 @@
 //
 // Three launches (the two pre-passes share one, prep16_kernel):
 //   xprep16: per row of x, t = the exponent that brings max|x| into [2^14, 2^15); the copy
-//            x * 2^-t in fp16, permuted per 8 values to the order the code unpacking yields and
-//            zero-padded to a multiple of 64 values; the factor 2^t.
+//            x * 2^-t in fp16, permuted per 8 values to the order the code unpacking yields,
+//            zero-padded to a multiple of 64 values and stored k-tile-major ([k/64][m][64]: the
+//            x tile of a workgroup is one contiguous 32 KiB block, spread over every L2
+//            channel, where rows of a row-major copy would fall on a few); the factor 2^t.
 //   wprep16: per weight row a power of two 2^v with every S = s 2^(24-v) and B = b 2^-v of the
 //            row below 2^15 (the largest in [2^14, 2^15)), so that S and B are exact fp16 values;
 //            per group the fp16 pair (S, B); the factor 2^v.
@@ -41,7 +43,16 @@
 namespace ql {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
+#ifndef GEMM_BM
+#define GEMM_BM 256
+#endif
+#ifndef GEMM_BN
+#define GEMM_BN 128
+#endif
+constexpr int BM = GEMM_BM, BN = GEMM_BN, BK = 64;
+// four waves, each a 128 x 64 block: WGN of them along n, BM / 128 along m
+constexpr int WGN = BN / 64;
+static_assert(BM % 128 == 0 && BN % 64 == 0 && (BM / 128) * WGN == 4, "four waves of 128 x 64");
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -122,8 +133,8 @@ __device__ __forceinline__ f32x16_t mfma16(const u32x4_t& a, const u32x4_t& b, c
 // ---------------------------------------------------------------- pre-pass over x
 // One workgroup per row: the row's largest magnitude, then the scaled, permuted fp16 copy.
 template <typename XT, int BITS>
-__device__ __forceinline__ void xprep16_row(int64_t m, const uint16_t* __restrict__ x, int64_t K, int64_t Kp,
-                                            uint16_t* __restrict__ x16, float* __restrict__ xsc) {
+__device__ __forceinline__ void xprep16_row(int64_t m, const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                            int64_t Kp, uint16_t* __restrict__ x16, float* __restrict__ xsc) {
   __shared__ uint32_t s_max[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nc = (int)(K / 8), ncp = (int)(Kp / 8);
@@ -151,7 +162,8 @@ __device__ __forceinline__ void xprep16_row(int64_t m, const uint16_t* __restric
     }
   }
   const float f = __builtin_ldexpf(1.0f, -t);
-  u32x4_t* out = (u32x4_t*)(x16 + m * Kp);
+  // k-tile-major: the 64 values of row m in k-tile kt sit at x16[(kt * M + m) * 64]
+  u32x4_t* out = (u32x4_t*)x16 + m * 8;
   for (int c = tid; c < ncp; c += 256) {
     u32x4_t o = {0u, 0u, 0u, 0u};
     if (c < nc) {
@@ -171,7 +183,7 @@ __device__ __forceinline__ void xprep16_row(int64_t m, const uint16_t* __restric
         o[e] = __builtin_bit_cast(uint32_t, hv);
       }
     }
-    out[c] = o;
+    out[(int64_t)(c >> 3) * M * 8 + (c & 7)] = o;
   }
   if (tid == 0) xsc[m] = __builtin_ldexpf(1.0f, t);
 }
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(256) void prep16_kernel(const uint16_t* __restrict_
                                                      float2* __restrict__ rec, float* __restrict__ wsc) {
   const int64_t b = blockIdx.x;
   if (b < M)
-    xprep16_row<XT, BITS>(b, x, K, Kp, x16, xsc);
+    xprep16_row<XT, BITS>(b, x, M, K, Kp, x16, xsc);
   else
     wprep16_rows<PT>(b - M, scales, biases, N, groups, rec, wsc);
 }
@@ -262,9 +274,11 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   constexpr int RD = G32 ? 4 : 2;                  // record words per weight row and tile
   constexpr int R_BYTES = BN * RD * 4;             // 2 or 1 KiB
   constexpr int STAGE = A_BYTES + B_BYTES + R_BYTES;
-  constexpr int NB = B_BYTES / (256 * 16);         // code copies per thread and tile: 1 or 2
-  constexpr int NR = BN * RD / 256;                // record copies per thread and tile: 2 or 1
-  constexpr int L = 8 + NB + NR;                   // copies per thread and tile
+  constexpr int NA = A_BYTES / (256 * 16);         // x copies per thread and tile
+  constexpr int NB = B_BYTES / (256 * 16);         // code copies per thread and tile
+  constexpr int NR = BN * RD / 256;                // record copies per thread and tile
+  constexpr int L = NA + NB + NR;                  // copies per thread and tile
+  static_assert(NA * 256 * 16 == A_BYTES && NB * 256 * 16 == B_BYTES && NR * 256 == BN * RD, "copy shares");
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[TWO ? 16 : STAGE];
@@ -272,7 +286,7 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, h = lane >> 5;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
@@ -294,19 +308,20 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   const int gshift = __builtin_ctz((unsigned)g);
 
   // ---- copies of one tile into a stage (every lane, every tile)
-  // x: copy i (0..7) of wave w covers rows 64w + 8i .. +7; lane l -> row + l/8, slot l%8.
-  uint32_t a_off[8];
+  // x: copy i (0..NA-1) of wave w covers rows (BM/4)w + 8i .. +7; lane l -> row + l/8, slot l%8.
+  uint32_t a_off[NA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < NA; ++i) {
+    const int r = (BM / 4) * wave + 8 * i + (lane >> 3);
     const int c = (lane & 7) ^ xswz(r);
-    a_off[i] = m0 + r < M ? (uint32_t)(((m0 + r) * Kp + 8 * c) * 2) : kOOB;
+    a_off[i] = m0 + r < M ? (uint32_t)(((m0 + r) * BK + 8 * c) * 2) : kOOB;
   }
-  // codes: copy i (0..NB-1) of wave w covers rows 32w + (32/NB)i ..; lane l -> row + l/BCH, slot l%BCH.
+  // codes: copy i (0..NB-1) of wave w covers rows (BN/4)w + (64/BCH)i ..; lane l -> row + l/BCH,
+  // slot l%BCH.
   uint32_t b_off[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int n = 32 * wave + (32 / NB) * i + lane / BCH;
+    const int n = (BN / 4) * wave + (64 / BCH) * i + lane / BCH;
     const int c = (lane % BCH) ^ bswz<BCH>(n);
     b_off[i] = n0 + n < N ? (uint32_t)((n0 + n) * row_bytes + 16 * c) : kOOB;
   }
@@ -325,10 +340,12 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   auto copy_tile = [&](int kt, uint8_t* stage) __attribute__((always_inline)) {
     const int k0 = (kb + kt) * BK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy_to_lds<16>(rsA, a_off[i], (uint32_t)(k0 * 2), stage + (64 * wave_u + 8 * i) * 128);
+    for (int i = 0; i < NA; ++i)
+      copy_to_lds<16>(rsA, a_off[i], (uint32_t)(k0 * M * 2), stage + ((BM / 4) * wave_u + 8 * i) * 128);
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      copy_to_lds<16>(rsB, b_off[i], (uint32_t)(k0 * BITS / 8), stage + A_BYTES + (32 * wave_u + (32 / NB) * i) * B_ROW);
+      copy_to_lds<16>(rsB, b_off[i], (uint32_t)(k0 * BITS / 8),
+                      stage + A_BYTES + ((BN / 4) * wave_u + (64 / BCH) * i) * B_ROW);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const int gi = G32 ? (k0 >> 5) + (r_word[i] >> 1) : k0 >> gshift;
@@ -436,7 +453,7 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   };
 
   // x row scales of the tile (read in the epilogue; the first barrier publishes them)
-  sXs[tid] = m0 + tid < M ? xsc[m0 + tid] : 0.0f;
+  for (int i = tid; i < BM; i += 256) sXs[i] = m0 + i < M ? xsc[m0 + i] : 0.0f;
   if constexpr (TWO) {
     // two stages: tile kt+1 is copied while tile kt is computed
     auto step2 = [&](int kt, const uint8_t* cur, uint8_t* other) __attribute__((always_inline)) {
@@ -520,8 +537,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // Workspace: the fp16 copy of x (m * kp values), its row factors (m floats), the weight records
-// (n * k/g pairs of floats) and row factors (n floats), and, for a launch split over k, the fp32
-// partial products (splits * m * n), each padded to 256 bytes.
+// (n * k/g pairs of floats) and row factors (n floats), for a launch split over k the fp32
+// partial products (splits * m * n), and at the bitstream widths the codes as bytes (n * k), each
+// padded to 256 bytes.
 inline size_t pad256(size_t b) { return (b + 255u) & ~(size_t)255u; }
 inline int64_t kpad(int64_t k) { return (k + BK - 1) / BK * BK; }
 constexpr int64_t kCUs = 256;  // compute units of the gfx950 parts this library is built for
@@ -583,18 +601,61 @@ hipError_t launch_t(const void* x, int64_t m, int64_t k, const uint32_t* packed,
   return hipGetLastError();
 }
 
-}  // namespace
+// Bitstream widths (2, 3, 5, 6 bits): each lane turns one 32-code chunk of a row (BITS words) into
+// its 32 codes as bytes, so that the 8-bit kernel reads them (byte i of a row: code i, the 8-bit
+// affine layout).
+template <int BITS>
+__global__ __launch_bounds__(256) void stream_to_bytes_kernel(const uint32_t* __restrict__ packed, int64_t n,
+                                                              int64_t k, uint8_t* __restrict__ codes8) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n * (k / 32)) return;
+  const uint32_t* src = packed + t * BITS;  // chunks are consecutive: row r, chunk c at r * k/32 + c
+  uint32_t w[BITS];
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) w[i] = src[i];
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    o[j] = stream_code<BITS>(w, 4 * j) | (stream_code<BITS>(w, 4 * j + 1) << 8) |
+           (stream_code<BITS>(w, 4 * j + 2) << 16) | (stream_code<BITS>(w, 4 * j + 3) << 24);
+  u32x4_t* dst = (u32x4_t*)(codes8 + t * 32);
+  dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+}
 
-size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int g) {
+size_t gemm_base_bytes(int64_t m, int64_t n, int64_t k, int g) {
   const int splits = gemm_splits(m, n, k);
   return pad256((size_t)(m * kpad(k)) * 2u) + pad256((size_t)m * 4u) + pad256((size_t)(n * (k / g)) * 8u) +
          pad256((size_t)n * 4u) + (splits > 1 ? pad256((size_t)(splits * m * n) * 4u) : 0u);
+}
+
+}  // namespace
+
+// The regions above, then (bitstream widths) the codes as bytes, n * k.
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g) {
+  return gemm_base_bytes(m, n, k, g) + (is_stream_bits(bits) ? pad256((size_t)(n * k)) : 0u);
 }
 
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,
                        int ydt, void* ws, hipStream_t s) {
   const bool xb = xdt == DT_BF16, pb = pdt == DT_BF16;
+  if (is_stream_bits(bits)) {
+    uint8_t* codes8 = (uint8_t*)ws + gemm_base_bytes(m, n, k, g);
+    const unsigned nb = (unsigned)((n * (k / 32) + 255) / 256);
+    if (bits == 2)
+      stream_to_bytes_kernel<2><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+    else if (bits == 3)
+      stream_to_bytes_kernel<3><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+    else if (bits == 5)
+      stream_to_bytes_kernel<5><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+    else
+      stream_to_bytes_kernel<6><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    packed = (const uint32_t*)codes8;
+    bits = 8;
+  }
   if (bits == 4) {
     if (xb && pb) return launch_t<4, BF16, BF16>(x, m, k, packed, scales, biases, n, g, layer_bias, y, ydt, ws, s);
     if (xb) return launch_t<4, BF16, F16>(x, m, k, packed, scales, biases, n, g, layer_bias, y, ydt, ws, s);

@@ -182,7 +182,27 @@ hipError_t launch_gemv_mf(const GemvDesc& single, const GemvDesc* table, const G
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,
                        int ydt, void* ws, hipStream_t s);
-size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int g);
+size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g);
+
+// Affine widths whose rows are read as a bitstream of 32-code chunks (BITS words each) rather
+// than by whole codes per word: 2, 3, 5 and 6 bits.
+constexpr bool is_stream_bits(int bits) { return bits == 2 || bits == 3 || bits == 5 || bits == 6; }
+
+// GEMV at the bitstream widths, m <= 8 rows of x.
+struct GemvStreamArgs {
+  const void* x;  // [m, k], x dtype; 16-byte aligned
+  int m;
+  int64_t k;
+  const uint32_t* packed;
+  const void* scales;
+  const void* biases;
+  int64_t n;
+  int g;
+  const void* layer_bias;  // [n] in x's dtype, or NULL
+  void* y;                 // [m, n]
+  int ydt, bits, xdt, pdt;
+};
+hipError_t launch_gemv_stream(const GemvStreamArgs& a, hipStream_t s);
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm,
                         hipStream_t s);

@@ -48,7 +48,8 @@ size_t esize(ql_dtype d) { return d == QL_F32 ? 4 : 2; }
 // Shared checks of the affine layout: bits, group size, k.
 ql_status check_affine(const char* fn, int64_t n, int64_t k, int bits, int g, ql_dtype pdt) {
   CHECK(n >= 0 && k >= 0, QL_ERR_SHAPE, "%s: n=%lld and k=%lld must be >= 0", fn, (long long)n, (long long)k);
-  CHECK(bits == 4 || bits == 8, QL_ERR_UNSUPPORTED, "%s: bits=%d not supported (4 or 8)", fn, bits);
+  CHECK(bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8, QL_ERR_UNSUPPORTED,
+        "%s: bits=%d not supported (2, 3, 4, 5, 6 or 8)", fn, bits);
   CHECK(g == 32 || g == 64 || g == 128, QL_ERR_UNSUPPORTED, "%s: group_size=%d not supported (32, 64 or 128)", fn,
         g);
   CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
@@ -150,6 +151,26 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
   CHECK(n * k * bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: packed weights of 2 GiB or more", fn);
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int64_t mm = std::min<int64_t>(8, m - m0);
+    if (ql::is_stream_bits(bits)) {
+      ql::GemvStreamArgs a{};
+      a.x = (const uint8_t*)x + m0 * k * 2;
+      a.m = (int)mm;
+      a.k = k;
+      a.packed = packed;
+      a.scales = scales;
+      a.biases = biases;
+      a.n = n;
+      a.g = group_size;
+      a.layer_bias = layer_bias;
+      a.y = (uint8_t*)y + m0 * n * esize(y_dtype);
+      a.ydt = dt(y_dtype);
+      a.bits = bits;
+      a.xdt = dt(x_dtype);
+      a.pdt = dt(param_dtype);
+      const hipError_t e = ql::launch_gemv_stream(a, (hipStream_t)stream);
+      if (e != hipSuccess) return launched(e, fn);
+      continue;
+    }
     ql::GemvDesc d{};
     d.x = (const uint8_t*)x + m0 * k * 2;
     d.packed = packed;
@@ -183,9 +204,9 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
   return ok();
 }
 
-size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int group_size) {
-  if (m <= 0 || n <= 0 || k <= 0 || group_size <= 0) return 0;
-  return ql::gemm_workspace_bytes(m, n, k, group_size);
+size_t qlinear_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int bits, int group_size) {
+  if (m <= 0 || n <= 0 || k <= 0 || group_size <= 0 || bits <= 0) return 0;
+  return ql::gemm_workspace_bytes(m, n, k, bits, group_size);
 }
 
 ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, const uint32_t* packed,
@@ -205,7 +226,9 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
   CHECK(m * ((k + 63) / 64 * 64) * 2 < (int64_t(1) << 31) && n * (k * bits / 8) < (int64_t(1) << 31),
         QL_ERR_UNSUPPORTED, "%s: x (%lld x %lld) and the packed words must each be smaller than 2 GiB", fn,
         (long long)m, (long long)k);
-  const size_t need = qlinear_gemm_workspace_size(m, n, k, group_size);
+  CHECK(!ql::is_stream_bits(bits) || n * k < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+        "%s: at %d bits the codes as bytes (n * k) must be smaller than 2 GiB", fn, bits);
+  const size_t need = qlinear_gemm_workspace_size(m, n, k, bits, group_size);
   CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
   CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
         need);
@@ -337,6 +360,8 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
     if (st != QL_OK) return st;
     CHECK(p.m <= 8, QL_ERR_UNSUPPORTED, "%s: problem %d has m=%lld > 8 (use qlinear_gemv or qlinear_gemm)", fn, i,
           (long long)p.m);
+    CHECK(p.bits == 4 || p.bits == 8, QL_ERR_UNSUPPORTED,
+          "%s: problem %d has bits=%d (lists take 4 or 8 bits; use qlinear_gemv)", fn, i, p.bits);
     CHECK(p.n * p.k * p.bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
           "%s: problem %d has packed weights of 2 GiB or more", fn, i);
   }

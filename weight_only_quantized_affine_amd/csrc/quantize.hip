@@ -2,7 +2,8 @@
 // low bits first into uint32 words, scales/biases [n, k/g]; GPTQModel wiki "MLX Apple
 // Silicon", Concepts and Packed layouts; gguf2mlx-stream section 01).
 //
-// One lane owns 8 consecutive weights of a row: one packed word at 4 bits, two at 8 bits.
+// One lane owns 8 consecutive weights of a row: one packed word at 4 bits, two at 8 bits, and at
+// the bitstream widths (2, 3, 5, 6 bits) a quarter of a 32-code chunk of BITS words.
 // The g/8 lanes of a group are consecutive in the wave, so the group min/max is a butterfly
 // over g/8 lanes.  HBM traffic per weight: 4 B read, bits/8 B + 4/g B written.
 #include "device_common.hpp"
@@ -64,8 +65,41 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
     r = r > 0.0f ? r : 0.0f;  // also maps NaN to 0
     q[i] = (s == 0.0f) ? 0u : (uint32_t)r;
   }
+  if constexpr (is_stream_bits(BITS)) {
+    // Bitstream widths: the 4 lanes of a 32-code chunk (consecutive lanes, c8 % 4 = 0..3) hold
+    // 8 * BITS consecutive bits of the chunk's stream each; every lane gathers all four parts
+    // and writes the chunk's words w with w % 4 == c8 % 4.
+    uint64_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mine |= (uint64_t)q[i] << (BITS * i);
+    const int base = (int)(threadIdx.x & 63) & ~3;
+    uint64_t part[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)mine, base + j);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(mine >> 32), base + j);
+      part[j] = (uint64_t)lo | ((uint64_t)hi << 32);
+    }
+    if (!live) return;
+    const int j0 = (int)(c8 & 3);
+    uint32_t* dst = packed + row * (k / 32 * BITS) + (c8 >> 2) * BITS;
+#pragma unroll
+    for (int wi = 0; wi < BITS; ++wi) {
+      if (wi % 4 != j0) continue;
+      // stream bits [32 wi, 32 wi + 32): part j covers [8 BITS j, 8 BITS (j + 1))
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 8 * BITS * j - 32 * wi;  // where part j starts relative to the word
+        if (d >= 32 || d + 8 * BITS <= 0) continue;
+        word |= d >= 0 ? (uint32_t)(part[j] << d) : (uint32_t)(part[j] >> (-d));
+      }
+      dst[wi] = word;
+    }
+  }
   if (!live) return;
-  if (BITS == 4) {
+  if constexpr (is_stream_bits(BITS)) {
+  } else if (BITS == 4) {
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) word |= q[i] << (4 * i);
@@ -91,6 +125,19 @@ hipError_t launch_quantize(const float* w, int64_t n, int64_t k, int bits, int g
   const unsigned blocks = (unsigned)((total + 255) / 256);
   uint16_t* sc = (uint16_t*)scales;
   uint16_t* bi = (uint16_t*)biases;
+#define QL_QUANT_STREAM(B)                                                              \
+  if (bits == B) {                                                                      \
+    if (pdt == DT_BF16)                                                                 \
+      quantize_kernel<B, BF16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);      \
+    else                                                                                \
+      quantize_kernel<B, F16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);       \
+    return hipGetLastError();                                                           \
+  }
+  QL_QUANT_STREAM(2)
+  QL_QUANT_STREAM(3)
+  QL_QUANT_STREAM(5)
+  QL_QUANT_STREAM(6)
+#undef QL_QUANT_STREAM
   if (bits == 4 && pdt == DT_BF16)
     quantize_kernel<4, BF16><<<blocks, 256, 0, s>>>(w, n, k, g, packed, sc, bi);
   else if (bits == 4)
