@@ -347,6 +347,22 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         del copies
         torch.cuda.empty_cache()
 
+    # ---------------- bitstream widths (2, 3, 6 bits): the decode step at batch 1, one problem-list
+    # launch per step as above
+    for bits in (2, 3, 6):
+        log(f"leg: {bits}-bit decode m=1 (bitstream GEMV)")
+        sets_b, wb, io = build_decode(bits, 1, 2, 70_000 + 100 * bits)
+        wall, avg = time_decode(sets_b, 200, 300)
+        legs[f"decode_{bits}bit_m1"] = {
+            "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 2),
+            "kernel_ms": round(avg, 5),
+            "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "weights_bytes": wb,
+            "kernel": "gemv_quad_kernel (one problem-list launch per step)",
+        }
+        del sets_b
+        torch.cuda.empty_cache()
+
     # ---------------- quantizer on the lm_head-sized matrix (151936 x 1024)
     log("leg: quantize")
     w = torch.randn((151936, 1024), generator=gen(60_000), device=dev) * 0.02

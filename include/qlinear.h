@@ -127,7 +127,8 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        size_t ws_bytes, void* stream);
 
 /* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
- * 1/2/4/8, bits); bits (4 or 8 here) and group_size may differ between problems.  `probs` is HOST memory
+ * 1/2/4/8, bits); bits and group_size may differ between problems (at 2, 3, 5 and 6 bits a
+ * problem's k must be a positive multiple of 128, else QL_ERR_UNSUPPORTED).  `probs` is HOST memory
  * (count entries), validated on the host like qlinear_gemv; the device table built from it (the
  * problems and their row tiles) is written to `workspace` (device memory of at least
  * qlinear_gemv_batched_workspace_size(probs, count) bytes, which depends on the shapes).

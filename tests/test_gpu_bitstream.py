@@ -116,10 +116,10 @@ GEMV_STREAM_CASES = [
     (3, 300, 1024, 2, 32, "f16", "f16", "f16"),
     (4, 129, 384, 5, 64, "bf16", "bf16", "f32"),
     (5, 64, 3072, 3, 32, "bf16", "bf16", "f32"),
-    (8, 250, 8192, 6, 64, "bf16", "bf16", "f32"),  # x in two LDS slices of 4096 values
+    (8, 250, 8192, 6, 64, "bf16", "bf16", "f32"),  # x through LDS in 3 slices
     (8, 1024, 1024, 3, 64, "f16", "bf16", "f32"),
     (11, 90, 512, 5, 64, "bf16", "bf16", "f32"),  # 8 + 3 rows of x
-    (1, 40, 33792, 2, 64, "bf16", "bf16", "f32"),  # one x row in two slices of 32768 values
+    (1, 40, 33792, 2, 64, "bf16", "bf16", "f32"),  # one x row through LDS in 2 slices
 ]
 
 
@@ -193,3 +193,54 @@ def test_gemm_bitstream_equals_its_8bit_transcode():
     y8 = q.qlinear_gemm(x, u32_to_dev(pk8), sc, bi, bits=8, group_size=g, y_dtype=torch.float32)
     _sync()
     assert torch.equal(y5, y8)
+
+
+def test_gemv_bitstream_graph_replay_matches_eager():
+    """Three bitstream GEMVs captured in one HIP graph: every replay (with eager work and the
+    outputs cleared in between) equals the eager results bit for bit."""
+    cases = []
+    for bits, (n, k) in zip((2, 3, 6), ((300, 1024), (1000, 3072), (4096, 1024))):
+        (pk, sc, bi), _ = _affine_case(1300 + bits, n, k, bits, 64, "bf16")
+        x, _ = _x_case(1400 + bits, 1, k, "bf16")
+        y = torch.empty((1, n), dtype=torch.float32, device=DEV)
+        cases.append((bits, x, pk, sc, bi, y))
+    eager = [q.qlinear_gemv(x, pk, sc, bi, bits=b, group_size=64, y_dtype=torch.float32).clone()
+             for (b, x, pk, sc, bi, _) in cases]
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for (b, x, pk, sc, bi, y) in cases:
+            q.qlinear_gemv(x, pk, sc, bi, bits=b, group_size=64, y=y)
+    _sync()
+    for rep in range(3):
+        for c in cases:
+            c[5].zero_()
+        _ = q.qlinear_gemv(cases[0][1], cases[0][2], cases[0][3], cases[0][4], bits=2, group_size=64)  # eager work
+        _sync()
+        g.replay()
+        _sync()
+        for c, want in zip(cases, eager):
+            assert torch.equal(c[5], want), f"replay {rep}, {c[0]} bits"
+
+
+def test_gemv_batched_with_bitstream_widths():
+    """One problem list mixing 2, 3, 4, 5, 6 and 8 bits, 1 to 8 rows of x and every group size:
+    each y against the oracle (fp32 output); the bitstream problems run as one class of the list."""
+    specs = [  # bits, m, n, k, g
+        (2, 1, 300, 1024, 64), (3, 1, 1000, 3072, 64), (6, 1, 2048, 1024, 128), (5, 3, 129, 384, 32),
+        (2, 8, 250, 2048, 64), (6, 2, 517, 2048, 64), (4, 1, 400, 1024, 64), (8, 1, 300, 1024, 64),
+        (3, 8, 64, 8192, 64), (2, 1, 7, 128, 32)]
+    probs, refs = [], []
+    for i, (bits, m, n, k, g) in enumerate(specs):
+        (pk, sc, bi), D = _affine_case(1500 + i, n, k, bits, g, "bf16")
+        x, xf = _x_case(1600 + i, m, k, "bf16")
+        y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        probs.append(dict(x=x, packed=pk, scales=sc, biases=bi, y=y, bits=bits, group_size=g))
+        refs.append(O.apply(xf, D))
+    arr = q.qlinear_problem_list(probs)
+    ws = torch.empty(q.qlinear_gemv_batched_workspace_size(arr), dtype=torch.uint8, device=DEV)
+    q.qlinear_gemv_batched(arr, x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.float32,
+                           workspace=ws, upload=True)
+    _sync()
+    for p, ref, spec in zip(probs, refs, specs):
+        _assert_rel(p["y"], ref, 1e-4, f"batched {spec}")

@@ -138,7 +138,7 @@ def test_gemv_batched_validates_every_problem(lib):
     big_m = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 9, 256, 1024, 4, 64)
     arr = (P * 2)(good, big_m)
     assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_UNSUPPORTED
-    stream_bits = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1024, 3, 64)
+    stream_bits = P(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 256, 1056, 3, 32)  # 3 bits: k % 128 != 0
     arr = (P * 2)(good, stream_bits)
     assert lib.qlinear_gemv_batched(arr, 2, BF16, BF16, F32, FAKE, need, 1, None) == QL_ERR_UNSUPPORTED
     assert "bits=3" in _err(lib)

@@ -23,7 +23,6 @@
 namespace ql {
 namespace {
 
-constexpr int kStreamLdsBytes = 65536;  // x slice: MT rows of ks 16-bit values
 
 template <typename XT> __device__ __forceinline__ float xval(uint32_t b);
 template <> __device__ __forceinline__ float xval<BF16>(uint32_t b) { return bf16_bits_to_f32(b); }
@@ -156,13 +155,39 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(const uint16_t* __rest
 // k a multiple of 128: each lane takes 4 consecutive chunks of a row (128 codes, BITS 16-byte
 // loads) per step, R rows at a time (up to 4 x BITS loads of 16 bytes in flight per lane); the
 // scale and bias of each group the 4 chunks meet are loaded once.  Same arithmetic as above.
+// table != NULL: a problem list; workgroup b takes tile tiles[b] (problem, row tile): the
+// problem's arguments come from its descriptor (lane group width in `batches`), one pass of
+// 4 (64 / lg) R rows, ks = min(k, ks) for that problem.
 template <int BITS, typename XT, int MT, int R>
 __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restrict__ x, int m, int64_t k,
                                                         const uint32_t* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint16_t* __restrict__ biases, int pbf16, int64_t n,
                                                         int g, const uint16_t* __restrict__ layer_bias,
-                                                        void* __restrict__ y, int ydt, int ks, int lg, int passes) {
+                                                        void* __restrict__ y, int ydt, int ks, int lg, int passes,
+                                                        const GemvDesc* __restrict__ table,
+                                                        const GemvTile* __restrict__ tiles) {
+  int64_t first_row;
+  if (table) {
+    const GemvTile t = tiles[blockIdx.x];
+    const GemvDesc& d = table[t.prob];
+    x = (const uint16_t*)d.x;
+    m = (int)d.m;
+    k = d.k;
+    packed = d.packed;
+    scales = (const uint16_t*)d.scales;
+    biases = (const uint16_t*)d.biases;
+    n = d.n;
+    g = d.group_size;
+    layer_bias = (const uint16_t*)d.layer_bias;
+    y = d.y;
+    lg = d.batches;
+    passes = 1;
+    ks = (int)max((int64_t)128, min(k, (int64_t)ks));
+    first_row = (int64_t)t.local * (4 * (64 / lg) * R);
+  } else {
+    first_row = (int64_t)blockIdx.x * passes * (4 * (64 / lg) * R);
+  }
   constexpr bool BX = std::is_same<XT, BF16>::value;
   constexpr uint32_t MAGIC = BX ? 0x43004300u : 0u;
   constexpr uint32_t ONES = BX ? 0x3F803F80u : 0x3C003C00u;
@@ -192,7 +217,7 @@ __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restri
   }
 
   for (int pass = 0; pass < passes; ++pass) {
-    const int64_t base = ((int64_t)blockIdx.x * passes + pass) * rpp;
+    const int64_t base = first_row + (int64_t)pass * rpp;
     if (base >= n) break;  // uniform over the workgroup
     const int64_t row0 = base + (int64_t)(wave * (64 / lg) + sub) * R;
     int64_t wrow[R];
@@ -305,21 +330,17 @@ void launch_quad_r(const GemvStreamArgs& a, int ks, size_t lds, int lg, int64_t 
   const int64_t grid = (row_groups + passes - 1) / passes;
   gemv_quad_kernel<BITS, XT, MT, R><<<(unsigned)grid, 256, lds, s>>>(
       (const uint16_t*)a.x, a.m, a.k, a.packed, (const uint16_t*)a.scales, (const uint16_t*)a.biases,
-      a.pdt == DT_BF16, a.n, a.g, (const uint16_t*)a.layer_bias, a.y, a.ydt, ks, lg, passes);
+      a.pdt == DT_BF16, a.n, a.g, (const uint16_t*)a.layer_bias, a.y, a.ydt, ks, lg, passes, nullptr, nullptr);
 }
 
 template <int BITS, typename XT, int MT>
 hipError_t launch_quad(const GemvStreamArgs& a, hipStream_t s) {
-  // slice: MT rows of ks values plus their padding (ks / 16) in kStreamLdsBytes
-  const int ks = (int)std::max<int64_t>(128, std::min<int64_t>(a.k, kStreamLdsBytes / 2 / MT * 16 / 17 / 128 * 128));
-  const size_t lds = (size_t)MT * (size_t)(ks + ks / 16) * 2;
-  const int64_t nq = std::max<int64_t>(1, std::min<int64_t>(a.k, ks) / 128);
-  int lg = 8;
-  for (int cand = 16; cand <= 64; cand *= 2)
-    if (nq % cand == 0 || nq >= 4 * cand) lg = cand;
+  const int ks = stream_quad_ks(a.k, MT);
+  const size_t lds = stream_quad_lds(a.k, MT);
+  int lg = stream_quad_lg(a.k, MT);
   // rows per lane group: at most 8 partial sums; while the chip would get fewer than 512
   // workgroups, fewer rows per group, then wider groups
-  constexpr int rmax = MT >= 8 ? 1 : (MT >= 4 ? 2 : 4);
+  constexpr int rmax = stream_quad_rows(MT);
   int r = rmax;
   auto wgs = [&](int rr, int l) { return (a.n + 4 * (64 / l) * rr - 1) / (4 * (64 / l) * rr); };
   while (wgs(r, lg) < 512) {
@@ -376,7 +397,49 @@ hipError_t launch_bits(const GemvStreamArgs& a, hipStream_t s) {
   return a.xdt == DT_BF16 ? launch_b<BITS, BF16>(a, s) : launch_b<BITS, F16>(a, s);
 }
 
+template <int BITS, typename XT, int MT>
+hipError_t launch_table_mt(const GemvDesc* table, const GemvTile* tiles, int64_t grid, int pbf16, int ydt,
+                           size_t lds, hipStream_t s) {
+  constexpr int R = stream_quad_rows(MT);
+  gemv_quad_kernel<BITS, XT, MT, R><<<(unsigned)grid, 256, lds, s>>>(
+      nullptr, 0, 0, nullptr, nullptr, nullptr, pbf16, 0, 32, nullptr, nullptr, ydt,
+      stream_quad_ks(int64_t(1) << 40, MT), 8, 1, table, tiles);
+  return hipGetLastError();
+}
+
+template <int BITS, typename XT>
+hipError_t launch_table_b(const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m, int pbf16, int ydt,
+                          size_t lds, hipStream_t s) {
+  if (m <= 1) return launch_table_mt<BITS, XT, 1>(table, tiles, grid, pbf16, ydt, lds, s);
+  if (m <= 2) return launch_table_mt<BITS, XT, 2>(table, tiles, grid, pbf16, ydt, lds, s);
+  if (m <= 4) return launch_table_mt<BITS, XT, 4>(table, tiles, grid, pbf16, ydt, lds, s);
+  return launch_table_mt<BITS, XT, 8>(table, tiles, grid, pbf16, ydt, lds, s);
+}
+
+template <int BITS>
+hipError_t launch_table_bits(const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m, int xdt, int pdt,
+                             int ydt, size_t lds, hipStream_t s) {
+  return xdt == DT_BF16 ? launch_table_b<BITS, BF16>(table, tiles, grid, m, pdt == DT_BF16, ydt, lds, s)
+                        : launch_table_b<BITS, F16>(table, tiles, grid, m, pdt == DT_BF16, ydt, lds, s);
+}
+
 }  // namespace
+
+hipError_t launch_gemv_stream_table(const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m, int bits,
+                                    int xdt, int pdt, int ydt, size_t lds, hipStream_t s) {
+  switch (bits) {
+    case 2:
+      return launch_table_bits<2>(table, tiles, grid, m, xdt, pdt, ydt, lds, s);
+    case 3:
+      return launch_table_bits<3>(table, tiles, grid, m, xdt, pdt, ydt, lds, s);
+    case 5:
+      return launch_table_bits<5>(table, tiles, grid, m, xdt, pdt, ydt, lds, s);
+    case 6:
+      return launch_table_bits<6>(table, tiles, grid, m, xdt, pdt, ydt, lds, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemv_stream(const GemvStreamArgs& a, hipStream_t s) {
   switch (a.bits) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace ql {
 
 // Device problem descriptor of one GEMV (mirrors ql_problem plus the host-chosen batch count).
@@ -203,6 +205,34 @@ struct GemvStreamArgs {
   int ydt, bits, xdt, pdt;
 };
 hipError_t launch_gemv_stream(const GemvStreamArgs& a, hipStream_t s);
+// A problem list of bitstream GEMVs (every problem: `bits`, k % 128 == 0, m <= 8); tiles as
+// stream_quad_tile_rows gives them; lds from stream_quad_lds (the largest over the list).
+hipError_t launch_gemv_stream_table(const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m, int bits,
+                                    int xdt, int pdt, int ydt, size_t lds, hipStream_t s);
+
+// Geometry of the bitstream GEMV for k % 128 == 0 (shared by the host plan and the kernels):
+// x slices of ks values (plus 16 bytes of padding per 128) in at most 64 KiB of LDS; lanes per
+// row group from the 128-code quads of a row; weight rows per lane group by x rows (mt).
+constexpr int kStreamLdsBytes = 65536;
+inline int stream_quad_ks(int64_t k, int mt) {
+  const int64_t cap = kStreamLdsBytes / 2 / mt * 16 / 17 / 128 * 128;
+  return (int)(k < 128 ? 128 : (k < cap ? k : cap));
+}
+inline size_t stream_quad_lds(int64_t k, int mt) {
+  const int ks = stream_quad_ks(k, mt);
+  return (size_t)mt * (size_t)(ks + ks / 16) * 2;
+}
+inline int stream_quad_lg(int64_t k, int mt) {
+  const int64_t nq = std::max<int64_t>(1, std::min<int64_t>(k, stream_quad_ks(k, mt)) / 128);
+  int lg = 8;
+  for (int cand = 16; cand <= 64; cand *= 2)
+    if (nq % cand == 0 || nq >= 4 * cand) lg = cand;
+  return lg;
+}
+constexpr int stream_quad_rows(int mt) { return mt >= 8 ? 1 : (mt >= 4 ? 2 : 4); }
+inline int64_t stream_quad_tile_rows(int64_t k, int mt) {
+  return 4 * (64 / stream_quad_lg(k, mt)) * stream_quad_rows(mt);
+}
 
 hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* offsets, int32_t* perm,
                         hipStream_t s);

@@ -250,6 +250,7 @@ struct BatchedPlan {
   struct Cls {
     int m, bits, xlds, mf_g;  // mf_g: group size of a matrix-core class, 0 for the vector-ALU kernel
     bool g2;
+    bool stream;  // bitstream widths (2, 3, 5, 6 bits)
     size_t first_tile, n_tiles, lds;
   };
   std::vector<Cls> classes;
@@ -265,6 +266,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
                                 probs[i].biases);
   };
   auto key = [&](int i) {
+    if (ql::is_stream_bits(probs[i].bits)) return (2 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256;
     if (mf(i)) return (1 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256 + probs[i].group_size;
     const bool g2 = probs[i].bits == 4 && probs[i].group_size == 32;
     return ql::gemv_mt(probs[i].m) * 32 + probs[i].bits * 2 + (g2 ? 1 : 0);
@@ -279,7 +281,8 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     c.m = 0;
     c.bits = probs[order[j]].bits;
     c.g2 = c.bits == 4 && probs[order[j]].group_size == 32;
-    c.mf_g = mf(order[j]) ? probs[order[j]].group_size : 0;
+    c.stream = ql::is_stream_bits(c.bits);
+    c.mf_g = !c.stream && mf(order[j]) ? probs[order[j]].group_size : 0;
     c.first_tile = plan.tiles.size();
     bool fits = true;
     size_t lds_x = 0, lds_lb = 0;
@@ -299,6 +302,15 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       d.bits = p.bits;
       d.group_size = p.group_size;
       c.m = std::max<int>(c.m, (int)p.m);
+      if (c.stream) {
+        const int mt = ql::gemv_mt(p.m);  // the class's row-count template (part of its key)
+        d.batches = ql::stream_quad_lg(p.k, mt);
+        lds_x = std::max(lds_x, ql::stream_quad_lds(p.k, mt));
+        const int64_t rows = ql::stream_quad_tile_rows(p.k, mt);
+        const int64_t t = (p.n + rows - 1) / rows;
+        for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
+        continue;
+      }
       if (c.mf_g) {
         d.batches = ql::gemv_mf_batches(p.n, p.k, p.bits, p.group_size, ql::gemv_mt(p.m), 1);
         const ql::GemvMfGeom g = ql::gemv_mf_geometry(p.k, d.batches);
@@ -321,15 +333,16 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     if (GEMV_TILES_BY_SIZE) {
       auto tile_bytes = [&](const ql::GemvTile& t) {
         const ql::GemvDesc& d = plan.descs[t.prob];
-        const int64_t rows = c.mf_g ? ql::gemv_mf_geometry(d.k, d.batches).rows_per_wg
-                                    : ql::gemv_geometry(d.k, d.bits, d.batches).rows_per_wg;
+        const int64_t rows = c.stream ? ql::stream_quad_tile_rows(d.k, ql::gemv_mt(d.m))
+                             : c.mf_g ? ql::gemv_mf_geometry(d.k, d.batches).rows_per_wg
+                                      : ql::gemv_geometry(d.k, d.bits, d.batches).rows_per_wg;
         return std::min<int64_t>(rows, d.n - (int64_t)t.local * rows) * (d.k * d.bits / 8);
       };
       std::stable_sort(plan.tiles.begin() + c.first_tile, plan.tiles.end(),
                        [&](const ql::GemvTile& a, const ql::GemvTile& b) { return tile_bytes(a) > tile_bytes(b); });
     }
     c.xlds = fits ? 1 : 0;
-    c.lds = (fits || c.mf_g) ? lds_x : lds_lb;
+    c.lds = (fits || c.mf_g || c.stream) ? lds_x : lds_lb;
     plan.classes.push_back(c);
     j = e;
   }
@@ -360,8 +373,9 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
     if (st != QL_OK) return st;
     CHECK(p.m <= 8, QL_ERR_UNSUPPORTED, "%s: problem %d has m=%lld > 8 (use qlinear_gemv or qlinear_gemm)", fn, i,
           (long long)p.m);
-    CHECK(p.bits == 4 || p.bits == 8, QL_ERR_UNSUPPORTED,
-          "%s: problem %d has bits=%d (lists take 4 or 8 bits; use qlinear_gemv)", fn, i, p.bits);
+    CHECK(!ql::is_stream_bits(p.bits) || (p.k > 0 && p.k % 128 == 0), QL_ERR_UNSUPPORTED,
+          "%s: problem %d has bits=%d and k=%lld (lists take 2, 3, 5 and 6 bits when k is a positive multiple "
+          "of 128; use qlinear_gemv)", fn, i, p.bits, (long long)p.k);
     CHECK(p.n * p.k * p.bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
           "%s: problem %d has packed weights of 2 GiB or more", fn, i);
   }
@@ -388,8 +402,10 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
   for (const BatchedPlan::Cls& c : plan.classes) {
     ql::GemvDesc none{};
     hipError_t e =
-        c.mf_g ? ql::launch_gemv_mf(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits, c.mf_g,
-                                    dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s)
+        c.stream ? ql::launch_gemv_stream_table(d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
+                                                dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s)
+        : c.mf_g ? ql::launch_gemv_mf(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits, c.mf_g,
+                                      dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, s)
                : ql::launch_gemv(none, d_descs, d_tiles + c.first_tile, (int64_t)c.n_tiles, c.m, c.bits,
                                  dt(x_dtype), dt(param_dtype), dt(y_dtype), c.lds, c.xlds, c.g2, s);
     if (e != hipSuccess) return launched(e, fn);
