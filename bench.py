@@ -347,6 +347,33 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         del copies
         torch.cuda.empty_cache()
 
+    # ---------------- prefill GEMM at 6 bits (bitstream rows: codes re-packed as bytes, then the 8-bit
+    # kernel), same layer and M
+    log("leg: prefill GEMM 9B layer, M=2048, 6-bit")
+    tot_flop = tot_ms = 0.0
+    per6 = {}
+    for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
+        w = torch.randn((n, k), generator=gen(45_000 + i), device=dev) * 0.02
+        pk, sc, bi = q.qlinear_quantize(w, 6, 64, torch.bfloat16)
+        del w
+        x = torch.randn((m, k), generator=gen(46_000 + i), device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 6, 64), dtype=torch.uint8, device=dev)
+        avg, _ = _time_launches(
+            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=6, group_size=64, y=y, workspace=ws), 10, 20, stream)
+        flop = 2.0 * m * n * k
+        per6[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+        tot_flop += flop
+        tot_ms += avg
+        del pk, sc, bi, x, y, ws
+    torch.cuda.empty_cache()
+    legs["prefill_gemm_9b_layer_6bit"] = {
+        "tflops": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1),
+        "layer_ms": round(tot_ms, 4),
+        "per_projection": per6,
+        "kernel": "stream_to_bytes + prep16 + gemm16_kernel<8,false,false> (+ splitk_reduce on k/v)",
+    }
+
     # ---------------- bitstream widths (2, 3, 6 bits): the decode step at batch 1, one problem-list
     # launch per step as above
     for bits in (2, 3, 6):
