@@ -28,6 +28,9 @@ Readings of points the pages leave open:
 * dequant: value = fl32(q*s + b) (one rounding; q*s is exact in fp32), then rounded once to
   the output dtype.
 * apply: y = x . dequant(W)^T computed here exactly in fp64 from the fp32 values.
+* quantize_q8_0: the NaN scale of a block holding a NaN is the fp16 quiet NaN 0x7E00 (the page
+  fixes "a NaN scale", not its bits); a block holding an infinity and no NaN takes +inf (0x7C00).
+* take: positions outside [0, rows) are out of range (negative ones too) and give zero bytes.
 
 Float storage types travel as uint16 bit patterns (``'f16'`` or ``'bf16'``); fp32 as numpy
 float32.  All arithmetic below is NumPy on the CPU.
@@ -56,6 +59,8 @@ __all__ = [
     "mxfp4_dequant_f32",
     "q8_0_dequant_f32",
     "q8_0_quantize",
+    "mxfp4_blocks_dequant_f32",
+    "take",
     "route",
     "apply_experts",
     "rel_l2_per_row",
@@ -298,33 +303,74 @@ def q8_0_dequant_f32(blocks_u8) -> np.ndarray:
 
 
 def q8_0_quantize(w_f32) -> np.ndarray:
-    """quantize_q8_0 for finite fp32 input [..., n, k] -> blocks [..., n, k/32*34].
+    """quantize_q8_0 (Nx_quant API docs, quantize_q8_0): fp32 [..., n, k] -> blocks [..., n, k/32*34].
 
-    Per block of 32 values: d = amax/127 in fp32, stored as fp16 (nearest); quants are
-    v * (1/d) in fp32 rounded half away from zero, with 1/d taken from the fp32 d; a block
-    whose d is 0 or whose 1/d is infinite is all zero bytes."""
+    Per block of 32 values: d = amax/127 in fp32, stored as fp16 (nearest, so past fp16's largest
+    it is +inf); quants are v * (1/d) in fp32 rounded half away from zero, with 1/d taken from the
+    fp32 d.  Non-finite rules of the page: a block whose d is 0 or whose 1/d is infinite is all
+    zero bytes; a block holding an infinity (and no NaN) has d = +inf and quants 0; a block
+    holding a NaN has d = NaN (fp16 0x7E00) and quants 0."""
     w = np.asarray(w_f32, dtype=np.float32)
-    assert np.all(np.isfinite(w)), "only the finite path of quantize_q8_0 is used as a test-data generator"
     lead = w.shape[:-1]
     k = w.shape[-1]
     assert k % 32 == 0
     v = w.reshape(lead + (k // 32, 32))
-    amax = np.abs(v).max(axis=-1).astype(np.float32)
+    has_nan = np.isnan(v).any(axis=-1)
+    has_inf = np.isinf(v).any(axis=-1) & ~has_nan
+    finite = ~(has_nan | has_inf)
+    vf = np.where(finite[..., None], v, np.float32(0.0))
+    amax = np.abs(vf).max(axis=-1).astype(np.float32)
     d = (amax / np.float32(127.0)).astype(np.float32)
-    with np.errstate(divide="ignore"):
+    with np.errstate(divide="ignore", over="ignore"):
         inv = np.where(d == 0, np.float32(0.0), (np.float32(1.0) / d)).astype(np.float32)
-    zero_blk = (d == 0) | np.isinf(inv)
-    inv = np.where(zero_blk, np.float32(0.0), inv)
-    prod = (v * inv[..., None]).astype(np.float32).astype(np.float64)
+    zero_blk = finite & ((d == 0) | np.isinf(inv))
+    inv = np.where(zero_blk | ~finite, np.float32(0.0), inv)
+    prod = (vf * inv[..., None]).astype(np.float32).astype(np.float64)
     q = (np.sign(prod) * np.floor(np.abs(prod) + 0.5)).astype(np.int64)
-    q = np.where(zero_blk[..., None], 0, q)
+    q = np.where((zero_blk | ~finite)[..., None], 0, q)
     assert q.min(initial=0) >= -128 and q.max(initial=0) <= 127
-    d_bits = np.where(zero_blk, np.uint16(0), f32_to_f16_bits(d)).astype(np.uint16)
+    with np.errstate(over="ignore"):
+        d_bits = f32_to_f16_bits(d).astype(np.uint16)
+    d_bits = np.where(zero_blk, np.uint16(0), d_bits)
+    d_bits = np.where(has_inf, np.uint16(0x7C00), d_bits)
+    d_bits = np.where(has_nan, np.uint16(0x7E00), d_bits).astype(np.uint16)
     out = np.empty(lead + (k // 32, 34), dtype=np.uint8)
     out[..., 0] = (d_bits & 0xFF).astype(np.uint8)
     out[..., 1] = (d_bits >> 8).astype(np.uint8)
     out[..., 2:] = q.astype(np.int8).view(np.uint8)
     return out.reshape(lead + (k // 32 * 34,))
+
+
+def mxfp4_blocks_dequant_f32(blocks_u8) -> np.ndarray:
+    """MXFP4 in GGUF's blocks (Nx_quant API docs, Weights: Mxfp4_blocks): [..., n, k/32*17] ->
+    fp32 [..., n, k].  Per 32 values: the E8M0 scale byte, then 16 bytes, byte j holding value j
+    in its low nibble and value j + 16 in its high one; values decode as in the split layout."""
+    b = np.asarray(blocks_u8, dtype=np.uint8)
+    lead = b.shape[:-1]
+    assert b.shape[-1] % 17 == 0
+    nb = b.shape[-1] // 17
+    blk = b.reshape(lead + (nb, 17))
+    scales = blk[..., 0]
+    body = blk[..., 1:]
+    nib = np.concatenate([body & 0x0F, body >> 4], axis=-1).astype(np.int64)  # values 0..15, 16..31
+    mag = np.asarray(MXFP4_MAGNITUDES, dtype=np.float64)[nib & 7]
+    sign = np.where(nib & 8, -1.0, 1.0)
+    sc = scales.astype(np.int64)[..., None]
+    with np.errstate(over="ignore", invalid="ignore"):
+        val = sign * np.ldexp(mag, sc - 127)
+        val = np.where(sc == 255, np.nan, val)
+        return val.astype(np.float32).reshape(lead + (nb * 32,))
+
+
+def take(pos, src) -> np.ndarray:
+    """take (Nx_quant API docs): the rows (first axis) of a packed part at positions `pos`, bytes
+    copied with no value decoded; a position outside [0, rows) gives a zero row."""
+    src = np.asarray(src)
+    pos = np.asarray(pos, dtype=np.int64)
+    out = np.zeros((pos.shape[0],) + src.shape[1:], dtype=src.dtype)
+    ok = (pos >= 0) & (pos < src.shape[0])
+    out[ok] = src[pos[ok]]
+    return out
 
 
 # --------------------------------------------------------------------------------------

@@ -399,3 +399,90 @@ def test_rel_l2_tolerance_helper():
     ref = np.array([[3.0, 4.0], [0.0, 0.0]])
     y = np.array([[3.0, 4.0 + 5e-3], [0.0, 0.0]])
     np.testing.assert_allclose(O.rel_l2_per_row(y, ref), [1e-3, 0.0])
+
+
+# ---------------------------------------------------------------- quantize_q8_0 non-finite rules,
+# MXFP4 in GGUF blocks, take (Nx_quant API docs: quantize_q8_0; Weights: Mxfp4_blocks; take)
+
+
+def _blk(b):
+    b = np.asarray(b, dtype=np.uint8)
+    return int(b[0]) | (int(b[1]) << 8), b[2:].view(np.int8).astype(np.int64)
+
+
+def test_q8_0_quantize_nonfinite_and_edge_blocks_by_the_page():
+    w = np.zeros((1, 6 * 32), np.float32)
+    w[0, 0:32] = np.linspace(-1, 1, 32)
+    w[0, 5] = np.inf  # a block holding an infinity: scale +inf, quants 0
+    w[0, 32:64] = 0.5
+    w[0, 40] = np.nan  # a block holding a NaN: NaN scale, quants 0 (even with an infinity beside it)
+    w[0, 41] = -np.inf
+    w[0, 64:96] = 1e-39  # 1/d infinite (amax below ~127 * 2^-128): zero bytes
+    w[0, 96:128] = 0.0  # d = 0: zero bytes
+    w[0, 128:160] = 1e7  # d = 1e7/127 rounds past fp16's largest: scale +inf, quants from the fp32 1/d
+    w[0, 160:192] = np.arange(32, dtype=np.float32) - 16.0  # amax 16: d = 16/127
+    blocks = O.q8_0_quantize(w)[0].reshape(6, 34)
+    d, q = _blk(blocks[0])
+    assert d == 0x7C00 and np.all(q == 0)
+    d, q = _blk(blocks[1])
+    assert d == 0x7E00 and np.all(q == 0)
+    assert np.all(blocks[2] == 0) and np.all(blocks[3] == 0)
+    d, q = _blk(blocks[4])
+    assert d == 0x7C00 and np.all(q == 127)
+    d, q = _blk(blocks[5])
+    d32 = np.float32(16.0) / np.float32(127.0)
+    assert d == int(np.float16(d32).view(np.uint16))
+    inv = np.float32(1.0) / d32
+    want = [int(math.copysign(math.floor(abs(float(np.float32(v) * inv)) + 0.5), v)) for v in w[0, 160:192]]
+    assert list(q) == want and q[0] == -127
+
+
+def test_mxfp4_blocks_equal_split_layout_rearranged_by_hand():
+    """The same codes and scales written in both layouts decode to the same values: split layout
+    value 2i in the low nibble of byte i; GGUF block: scale byte, then byte j with value j low and
+    value j + 16 high (built here value by value)."""
+    g = np.random.default_rng(17)
+    n, k = 5, 96
+    codes = g.integers(0, 256, size=(n, k // 2)).astype(np.uint8)
+    scales = g.integers(100, 140, size=(n, k // 32)).astype(np.uint8)
+    scales[1, 2] = 255
+    blocks = np.zeros((n, k // 32 * 17), np.uint8)
+    for r in range(n):
+        for bi in range(k // 32):
+            blocks[r, bi * 17] = scales[r, bi]
+            for i in range(32):
+                kk = bi * 32 + i
+                nib = (codes[r, kk // 2] >> (4 * (kk % 2))) & 0xF
+                byte = bi * 17 + 1 + (i % 16)
+                blocks[r, byte] |= nib << (4 * (i // 16))
+    a = O.mxfp4_blocks_dequant_f32(blocks)
+    b = O.mxfp4_dequant_f32(codes, scales)
+    np.testing.assert_array_equal(np.isnan(a), np.isnan(b))
+    np.testing.assert_array_equal(a[~np.isnan(a)].view(np.uint32), b[~np.isnan(b)].view(np.uint32))
+
+
+def test_mxfp4_blocks_hand_block():
+    blk = np.zeros(17, np.uint8)
+    blk[0] = 128  # 2^1
+    for j in range(16):
+        blk[1 + j] = j | ((15 - j) << 4)
+    mag = {0: 0.0, 1: 0.5, 2: 1.0, 3: 1.5, 4: 2.0, 5: 3.0, 6: 4.0, 7: 6.0}
+    e2m1 = lambda c: (-1.0 if c & 8 else 1.0) * mag[c & 7]
+    want = [2 * e2m1(j) for j in range(16)] + [2 * e2m1(15 - j) for j in range(16)]
+    np.testing.assert_array_equal(O.mxfp4_blocks_dequant_f32(blk[None, :])[0], np.array(want, np.float32))
+
+
+def test_take_is_the_gather_of_dequantized_rows():
+    """dequant(take(p, w)) equals the rows p of dequant(w) for positions in range; positions out of
+    range gather zero bytes, which decode to zeros (Nx_quant API docs, take)."""
+    n, k, bits, g = 40, 256, 4, 64
+    pk, sb, bb = O.affine_quantize(synth.weights_f32(91, n, k), bits, g, "bf16")
+    D = O.affine_dequant_f32(pk, sb, bb, bits, g, "bf16", k)
+    pos = np.array([3, 0, 39, -1, 40, 7, 7, 1000])
+    T = O.affine_dequant_f32(O.take(pos, pk), O.take(pos, sb), O.take(pos, bb), bits, g, "bf16", k)
+    for i, p in enumerate(pos):
+        want = D[p] if 0 <= p < n else np.zeros(k, np.float32)
+        np.testing.assert_array_equal(T[i], want)
+    # Q8_0 and MXFP4 parts: zero bytes decode to zeros as well
+    assert np.all(O.q8_0_dequant_f32(np.zeros((1, 34), np.uint8)) == 0)
+    assert np.all(O.mxfp4_blocks_dequant_f32(np.zeros((1, 17), np.uint8)) == 0)
