@@ -50,7 +50,7 @@ typedef enum {
 } ql_status;
 
 typedef enum { QL_F32 = 0, QL_F16 = 1, QL_BF16 = 2 } ql_dtype;
-typedef enum { QL_AFFINE = 0, QL_MXFP4 = 1, QL_Q8_0 = 2 } ql_format;
+typedef enum { QL_AFFINE = 0, QL_MXFP4 = 1, QL_Q8_0 = 2, QL_MXFP4_BLOCKS = 3 } ql_format;
 
 /* One GEMV of a problem list: y[m,n] = x[m,k] . dequant(W[n,k])^T (+ layer_bias[n]).
  * All pointers are device memory; layer_bias may be NULL. */
@@ -78,6 +78,25 @@ ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int g
                            ql_dtype param_dtype, uint32_t* packed, void* scales, void* biases,
                            void* stream);
 
+/* quantize_q8_0 (Nx_quant API docs, quantize_q8_0): w [rows, k] fp32 -> blocks [rows, k/32*34].
+ * Per block of 32 values: d = amax/127 in fp32 stored as fp16 (round to nearest even: +inf past
+ * fp16's largest); quants = round(v * (1/d)) half away from zero, 1/d from the fp32 d, products
+ * in fp32.  Non-finite rules of the page: a block with d == 0 or 1/d infinite (amax below about
+ * 127 * 2^-128) is zero bytes; a block holding an infinity and no NaN stores d = +inf and zero
+ * quants; a block holding a NaN stores d = NaN (the fp16 quiet NaN 0x7E00) and zero quants.
+ * k % 32 == 0 (QL_ERR_SHAPE); w 16-byte aligned, blocks 2-byte aligned.  qlinear_dequant with
+ * QL_Q8_0 decodes the result. */
+ql_status qlinear_quantize_q8_0(const float* w, int64_t rows, int64_t k, uint8_t* blocks, void* stream);
+
+/* take (Nx_quant API docs, take): dst row i = src row pos[i] for 0 <= pos[i] < src_rows, else
+ * row_bytes zero bytes (which decode to zeros in every format).  Bytes are copied with no value
+ * decoded; gather each part of a weight with its own row size: affine packed k*bits/8, scales and
+ * biases k/group_size*2, MXFP4 codes k/2 and scales k/32, Q8_0 blocks k/32*34, or whole matrices
+ * (n times those) to gather experts.  pos: int64 [n_pos], 8-byte aligned, device memory; src
+ * [src_rows, row_bytes], dst [n_pos, row_bytes]. */
+ql_status qlinear_take(const int64_t* pos, int64_t n_pos, const void* src, int64_t src_rows,
+                       int64_t row_bytes, void* dst, void* stream);
+
 /* dequant (Nx_quant Products, dequant): every value of W as a float32 value, rounded once to
  * out_dtype (QL_F32, QL_F16 or QL_BF16).  out is [rows, k].
  *   QL_AFFINE: w0 = packed [rows, k*bits/32], w1 = scales, w2 = biases [rows, k/group_size] in
@@ -88,6 +107,10 @@ ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int g
  *              are ignored; w2 must be NULL.
  *   QL_Q8_0:   w0 = blocks [rows, k/32*34] (little-endian fp16 d, then 32 int8), value = d*q
  *              (Nx_quant Weights, Q8_0).  w1 and w2 must be NULL.
+ *   QL_MXFP4_BLOCKS: w0 = GGUF blocks [rows, k/32*17]: per 32 values the E8M0 scale byte, then
+ *              16 bytes, byte j holding value j in its low nibble and value j + 16 in its high one
+ *              (Nx_quant Weights, Mxfp4_blocks); values as QL_MXFP4.  w1 and w2 must be NULL; w0
+ *              needs no alignment.
  * For MXFP4 and Q8_0, `rows` may count the rows of a whole expert stack ([e*n]). */
 ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const void* w2,
                           ql_dtype param_dtype, int64_t rows, int64_t k, int bits,

@@ -164,6 +164,7 @@ def test_route_and_experts_reject_bad_arguments(lib):
         return lib.qlinear_apply_experts(*a)
 
     assert call(fmt=0) == QL_ERR_UNSUPPORTED
+    assert call(fmt=3) == QL_ERR_UNSUPPORTED  # MXFP4 in GGUF blocks: dequant and take only
     assert call(xdt=F16) == QL_ERR_DTYPE
     assert call(k=2881) == QL_ERR_SHAPE
     assert call(ppr=3) == QL_ERR_SHAPE
@@ -179,3 +180,23 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(q, "lib_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         q.load_library()
+
+
+def test_quantize_q8_0_take_and_blocks_reject_bad_arguments(lib):
+    assert lib.qlinear_quantize_q8_0(FAKE, 4, 48, FAKE, None) == QL_ERR_SHAPE  # k % 32
+    assert lib.qlinear_quantize_q8_0(None, 4, 64, FAKE, None) == QL_ERR_NULL
+    assert lib.qlinear_quantize_q8_0(FAKE + 4, 4, 64, FAKE, None) == QL_ERR_ALIGN
+    assert lib.qlinear_quantize_q8_0(FAKE, 4, 64, FAKE + 1, None) == QL_ERR_ALIGN
+    assert lib.qlinear_quantize_q8_0(None, 0, 64, None, None) == QL_OK
+    assert lib.qlinear_take(FAKE, -1, FAKE, 4, 16, FAKE, None) == QL_ERR_SHAPE
+    assert lib.qlinear_take(None, 4, FAKE, 4, 16, FAKE, None) == QL_ERR_NULL
+    assert lib.qlinear_take(FAKE, 4, None, 4, 16, FAKE, None) == QL_ERR_NULL
+    assert lib.qlinear_take(FAKE + 4, 4, FAKE, 4, 16, FAKE, None) == QL_ERR_ALIGN
+    assert lib.qlinear_take(None, 0, None, 0, 16, None, None) == QL_OK
+    assert lib.qlinear_take(FAKE, 4, FAKE, 4, 0, FAKE, None) == QL_OK  # empty rows: nothing to copy
+    # MXFP4 in GGUF blocks: one part only
+    assert lib.qlinear_dequant(3, FAKE, FAKE, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
+    assert lib.qlinear_dequant(3, FAKE, None, None, BF16, 4, 48, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
+    assert lib.qlinear_dequant(3, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE + 2, F32, None) == QL_ERR_ALIGN
+    assert lib.qlinear_dequant(3, None, None, None, BF16, 0, 64, 0, 0, None, F32, None) == QL_OK
+    assert lib.qlinear_dequant(4, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_UNSUPPORTED

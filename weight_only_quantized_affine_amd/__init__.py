@@ -9,6 +9,7 @@ library has not been built, every call raises.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Sequence
 
@@ -17,10 +18,13 @@ __all__ = [
     "QL_AFFINE",
     "QL_MXFP4",
     "QL_Q8_0",
+    "QL_MXFP4_BLOCKS",
     "lib_path",
     "load_library",
     "qlinear_quantize",
     "qlinear_dequant",
+    "qlinear_quantize_q8_0",
+    "qlinear_take",
     "qlinear_gemv",
     "qlinear_gemm",
     "qlinear_gemm_workspace_size",
@@ -33,7 +37,7 @@ __all__ = [
     "qlinear_version",
 ]
 
-QL_AFFINE, QL_MXFP4, QL_Q8_0 = 0, 1, 2
+QL_AFFINE, QL_MXFP4, QL_Q8_0, QL_MXFP4_BLOCKS = 0, 1, 2, 3
 _QL_F32, _QL_F16, _QL_BF16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +75,8 @@ _P, _I64, _INT, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_si
 _SIGNATURES = {
     "qlinear_quantize": (_INT, [_P, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P]),
     "qlinear_dequant": (_INT, [_INT, _P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P]),
+    "qlinear_quantize_q8_0": (_INT, [_P, _I64, _I64, _P, _P]),
+    "qlinear_take": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
@@ -153,9 +159,34 @@ def qlinear_quantize(w, bits: int = 4, group_size: int = 64, param_dtype=None, p
     return packed, scales, biases
 
 
+def qlinear_quantize_q8_0(w, blocks=None):
+    """quantize_q8_0 of fp32 W [rows, k] -> blocks uint8 [rows, k/32*34]."""
+    torch = _torch()
+    lib = load_library()
+    rows, k = w.shape
+    if blocks is None:
+        blocks = torch.empty((rows, k // 32 * 34), dtype=torch.uint8, device=w.device)
+    _check(lib.qlinear_quantize_q8_0(_ptr(w), rows, k, _ptr(blocks), _stream()))
+    return blocks
+
+
+def qlinear_take(pos, src, dst=None):
+    """take: rows of `src` (its first axis; any dtype and trailing shape) at int64 positions
+    `pos`, bytes copied with no value decoded; a position out of range gives a zero row."""
+    torch = _torch()
+    lib = load_library()
+    n_pos = pos.numel()
+    if dst is None:
+        dst = torch.empty((n_pos,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    row_bytes = math.prod(src.shape[1:]) * src.element_size()
+    _check(lib.qlinear_take(_ptr(pos), n_pos, _ptr(src), src.shape[0], row_bytes, _ptr(dst), _stream()))
+    return dst
+
+
 def qlinear_dequant(fmt: int, w0, w1=None, w2=None, *, rows: int, k: int, bits: int = 4, group_size: int = 64,
                     out_dtype=None, out=None):
-    """dequant of an affine / MXFP4 / Q8_0 weight into out [rows, k] (out_dtype, default fp32)."""
+    """dequant of an affine / MXFP4 / Q8_0 / MXFP4-blocks weight into out [rows, k] (out_dtype,
+    default fp32)."""
     torch = _torch()
     lib = load_library()
     out_dtype = out_dtype or torch.float32

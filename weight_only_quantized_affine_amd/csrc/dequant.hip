@@ -130,6 +130,32 @@ __global__ __launch_bounds__(256) void dequant_mxfp4_kernel(const uint8_t* __res
   for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
 }
 
+// MXFP4 in GGUF's blocks (Nx_quant Weights, Mxfp4_blocks): per 32 values the E8M0 scale byte,
+// then 16 bytes, byte j holding value j in its low nibble and value j + 16 in its high one.  One
+// 17-byte block per lane (byte loads: blocks are not aligned), decoded as in the split layout.
+__global__ __launch_bounds__(256) void dequant_mxfp4_blocks_kernel(const uint8_t* __restrict__ blocks, int64_t rows,
+                                                                   int64_t k, void* __restrict__ out, int odt) {
+  const uint32_t twice_mag = 0xC8643210u;  // twice the e2m1 magnitudes, as above
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (k / 32)) return;
+  const uint8_t* bp = blocks + t * 17;
+  const float half_p2 = 0.5f * e8m0_to_f32(bp[0]);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t b = bp[1 + j];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (b >> (4 * h)) & 15u;
+      const float m = (float)((twice_mag >> (4 * (c & 7u))) & 15u) * half_p2;
+      v[16 * h + j] = __uint_as_float(__float_as_uint(m) | ((c & 8u) << 28));
+    }
+  }
+  const int64_t o = t * 32;  // rows of k values: block t covers values 32 t .. 32 t + 31
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
+}
+
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __restrict__ blocks, int64_t rows,
                                                            int64_t k, void* __restrict__ out, int odt) {
   const int64_t blocks_per_row = k / 32;
@@ -183,6 +209,13 @@ hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int
                                 int odt, hipStream_t s) {
   const int64_t total = rows * (k / 32);
   dequant_mxfp4_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(codes, scales, rows, k, out, odt);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp4_blocks(const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt,
+                                       hipStream_t s) {
+  const int64_t total = rows * (k / 32);
+  dequant_mxfp4_blocks_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(blocks, rows, k, out, odt);
   return hipGetLastError();
 }
 

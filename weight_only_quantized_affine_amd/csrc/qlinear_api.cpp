@@ -102,6 +102,30 @@ ql_status qlinear_quantize(const float* w, int64_t n, int64_t k, int bits, int g
                   fn);
 }
 
+ql_status qlinear_quantize_q8_0(const float* w, int64_t rows, int64_t k, uint8_t* blocks, void* stream) {
+  const char* fn = "qlinear_quantize_q8_0";
+  CHECK(rows >= 0 && k >= 0, QL_ERR_SHAPE, "%s: rows and k must be >= 0", fn);
+  CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+  if (rows == 0 || k == 0) return ok();
+  CHECK(w && blocks, QL_ERR_NULL, "%s: w and blocks must not be NULL", fn);
+  CHECK(aligned(w, 16), QL_ERR_ALIGN, "%s: w must be 16-byte aligned", fn);
+  CHECK(aligned(blocks, 2), QL_ERR_ALIGN, "%s: blocks must be 2-byte aligned", fn);
+  return launched(ql::launch_quantize_q8_0(w, rows, k, blocks, (hipStream_t)stream), fn);
+}
+
+ql_status qlinear_take(const int64_t* pos, int64_t n_pos, const void* src, int64_t src_rows, int64_t row_bytes,
+                       void* dst, void* stream) {
+  const char* fn = "qlinear_take";
+  CHECK(n_pos >= 0 && src_rows >= 0 && row_bytes >= 0, QL_ERR_SHAPE,
+        "%s: n_pos, src_rows and row_bytes must be >= 0", fn);
+  if (n_pos == 0 || row_bytes == 0) return ok();
+  CHECK(pos && dst, QL_ERR_NULL, "%s: pos and dst must not be NULL", fn);
+  CHECK(src_rows == 0 || src != nullptr, QL_ERR_NULL, "%s: src must not be NULL", fn);
+  CHECK(aligned(pos, 8), QL_ERR_ALIGN, "%s: pos must be 8-byte aligned", fn);
+  CHECK(n_pos * ((row_bytes + 32767) / 32768) < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: output too large", fn);
+  return launched(ql::launch_take(pos, n_pos, src, src_rows, row_bytes, dst, (hipStream_t)stream), fn);
+}
+
 ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const void* w2, ql_dtype param_dtype,
                           int64_t rows, int64_t k, int bits, int group_size, void* out, ql_dtype out_dtype,
                           void* stream) {
@@ -120,6 +144,14 @@ ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const v
     return launched(ql::launch_dequant_affine((const uint32_t*)w0, w1, w2, dt(param_dtype), rows, k, bits,
                                               group_size, out, dt(out_dtype), s),
                     fn);
+  }
+  if (fmt == QL_MXFP4_BLOCKS) {
+    CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+    CHECK(w1 == nullptr && w2 == nullptr, QL_ERR_SHAPE, "%s: w1 and w2 must be NULL for MXFP4 blocks", fn);
+    if (rows == 0 || k == 0) return ok();
+    CHECK(w0 && out, QL_ERR_NULL, "%s: w0 and out must not be NULL", fn);
+    CHECK(aligned(out, 16), QL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+    return launched(ql::launch_dequant_mxfp4_blocks((const uint8_t*)w0, rows, k, out, dt(out_dtype), s), fn);
   }
   if (fmt == QL_MXFP4 || fmt == QL_Q8_0) {
     CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);

@@ -117,7 +117,57 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__
   }
 }
 
+// quantize_q8_0 (Nx_quant API docs, quantize_q8_0): per block of 32 fp32 values, d = amax / 127
+// stored as fp16 (nearest), quants round(v * (1/d)) half away from zero with 1/d from the fp32 d,
+// products in fp32.  Non-finite rules: d == 0 or 1/d infinite -> zero bytes; a block holding an
+// infinity and no NaN -> d = +inf, quants 0; a block holding a NaN -> d = the fp16 quiet NaN
+// 0x7E00, quants 0.  Eight lanes per block (4 values each, one 16-byte load), reduced by shuffles.
+__global__ __launch_bounds__(256) void quantize_q8_0_kernel(const float* __restrict__ w, int64_t nblocks,
+                                                            uint8_t* __restrict__ blocks) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t b = t >> 3;
+  const int j = (int)(t & 7);
+  const bool live = b < nblocks;  // the 8 lanes of a block are live together
+  const int64_t bb = live ? b : nblocks - 1;
+  const f32x4_t v = *(const f32x4_t*)(w + bb * 32 + 4 * j);
+  float am = 0.0f;
+  int has_nan = 0, has_inf = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    has_nan |= v[e] != v[e];
+    has_inf |= __builtin_isinf(v[e]) ? 1 : 0;
+    am = fmaxf(am, fabsf(v[e]));  // a NaN is skipped here and handled by the flags
+  }
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    am = fmaxf(am, __shfl_xor(am, off));
+    has_nan |= __shfl_xor(has_nan, off);
+    has_inf |= __shfl_xor(has_inf, off);
+  }
+  const bool finite = !has_nan && !has_inf;
+  const float d = __fdiv_rn(am, 127.0f);
+  const float inv = d == 0.0f ? 0.0f : __fdiv_rn(1.0f, d);
+  const bool zero = !finite || d == 0.0f || __builtin_isinf(inv);
+  uint32_t qb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) qb[e] = zero ? 0u : ((uint32_t)(int32_t)roundf(v[e] * inv) & 0xffu);
+  uint32_t d_bits = (finite && !zero) ? f32_to_f16_bits(d) : 0u;
+  if (has_inf) d_bits = 0x7C00u;
+  if (has_nan) d_bits = 0x7E00u;
+  if (!live) return;
+  uint16_t* o = (uint16_t*)(blocks + bb * 34);  // 34-byte blocks: 2-byte aligned
+  if (j == 0) o[0] = (uint16_t)d_bits;
+  o[1 + 2 * j] = (uint16_t)(qb[0] | (qb[1] << 8));
+  o[2 + 2 * j] = (uint16_t)(qb[2] | (qb[3] << 8));
+}
+
 }  // namespace
+
+hipError_t launch_quantize_q8_0(const float* w, int64_t rows, int64_t k, uint8_t* blocks, hipStream_t s) {
+  const int64_t nblocks = rows * (k / 32);
+  quantize_q8_0_kernel<<<(unsigned)((nblocks * 8 + 255) / 256), 256, 0, s>>>(w, nblocks, blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const float* w, int64_t n, int64_t k, int bits, int g, int pdt, uint32_t* packed,
                            void* scales, void* biases, hipStream_t s) {
