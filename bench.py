@@ -405,6 +405,36 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
                                                          group_size=64, out=out), 10, 2, stream)
     byts = out.numel() * 2 + pk.numel() * 4 + sc.numel() * 4
     legs["dequant_4bit_g64_151936x1024_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1)}
+    del pk, sc, bi, out
+
+    # ---------------- quantize_q8_0, MXFP4 in GGUF blocks, take (HBM-bound byte movers)
+    log("leg: quantize_q8_0, MXFP4 blocks dequant, take")
+    blocks = torch.empty((151936, 1024 // 32 * 34), dtype=torch.uint8, device=dev)
+    avg, _ = _time_launches(lambda _i: q.qlinear_quantize_q8_0(w, blocks), 10, 2, stream)
+    byts = w.numel() * 4 + blocks.numel()
+    legs["quantize_q8_0_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                         "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del w, blocks
+    e_, n_, k_ = 32, 5760, 2880
+    mxb = torch.randint(0, 256, (e_ * n_, k_ // 32 * 17), generator=gen(61_000), device=dev,
+                        dtype=torch.int32).to(torch.uint8)
+    mxb.view(e_ * n_, k_ // 32, 17)[:, :, 0] = 127
+    out = torch.empty((e_ * n_, k_), dtype=torch.bfloat16, device=dev)
+    avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_MXFP4_BLOCKS, mxb, rows=e_ * n_, k=k_, out=out),
+                            10, 2, stream)
+    byts = mxb.numel() + out.numel() * 2
+    legs["dequant_mxfp4_blocks_32x5760x2880_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                                      "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del out
+    stack = mxb.view(e_, n_, k_ // 32 * 17)
+    pos = torch.tensor([3, 17, 30, 8], dtype=torch.int64, device=dev)
+    got = torch.empty((4, n_, k_ // 32 * 17), dtype=torch.uint8, device=dev)
+    avg, _ = _time_launches(lambda _i: q.qlinear_take(pos, stack, got), 20, 5, stream)
+    byts = 2 * got.numel()
+    legs["take_4_experts_mxfp4_blocks"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                           "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del mxb, stack, got
+    torch.cuda.empty_cache()
     return legs
 
 
