@@ -61,6 +61,8 @@ __all__ = [
     "q8_0_quantize",
     "mxfp4_blocks_dequant_f32",
     "take",
+    "gptq_transcode",
+    "gptq_dequant_f64",
     "route",
     "apply_experts",
     "rel_l2_per_row",
@@ -249,6 +251,42 @@ def apply(x_f64, w_values, layer_bias=None) -> np.ndarray:
     if layer_bias is not None:
         y = y + np.asarray(layer_bias, dtype=np.float64)[None, :]
     return y
+
+
+def gptq_transcode(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int,
+                   param_dtype: str, v1_zeros: bool = False):
+    """GPTQ (continuous layout) -> MLX affine rows (GPTQModel wiki "MLX Apple Silicon", Packed
+    layouts and exact transcoding: unpack the input-axis codes and the output-axis zeros, scales
+    to [out, groups], additive bias -zero*scale, uint32 row streams; GPTQModel "Packing Formats
+    and Compatibility", GPTQ and GPTQ_V2: qweight [K*b/32, N] codes as a continuous b-bit stream
+    down each column, qzeros [G, N*b/32] a stream along the outputs, scales [G, N], value
+    scale * (code - zero), v1 storing zero - 1).
+
+    Returns (packed [n, k*bits/32], scales [n, G], biases [n, G]) with biases = RNE(-zero * scale)
+    in param_dtype (the product is exact in fp32).  Groups are contiguous (g_idx[k] = k // g)."""
+    qweight = np.asarray(qweight, dtype=np.uint32)
+    qzeros = np.asarray(qzeros, dtype=np.uint32)
+    G = k // group_size
+    assert qweight.shape == (k * bits // 32, n) and qzeros.shape == (G, n * bits // 32)
+    codes = unpack_codes(qweight.T, bits, k)  # column streams down the input axis -> [n, k]
+    zeros = unpack_codes(qzeros, bits, n)  # row streams along the outputs -> [G, n]
+    if v1_zeros:
+        zeros = zeros + 1
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))  # [G, n]
+    b32 = (-(zeros.astype(np.float64)) * s).astype(np.float32)  # exact: |zero| <= 2^8, s has <= 11 bits
+    return (pack_codes(codes, bits), np.ascontiguousarray(np.asarray(scale_bits, dtype=np.uint16).T),
+            np.ascontiguousarray(to_bits(param_dtype, b32).T))
+
+
+def gptq_dequant_f64(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int, param_dtype: str,
+                     v1_zeros: bool = False):
+    """GPTQ's own reconstruction, scale * (code - zero), exactly in fp64: [n, k] (per output row)."""
+    codes = unpack_codes(np.asarray(qweight, dtype=np.uint32).T, bits, k).astype(np.float64)
+    zeros = unpack_codes(np.asarray(qzeros, dtype=np.uint32), bits, n).astype(np.float64) + (1 if v1_zeros else 0)
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))
+    sg = np.repeat(s.T, group_size, axis=1)
+    zg = np.repeat(zeros.T, group_size, axis=1)
+    return sg * (codes - zg)
 
 
 # --------------------------------------------------------------------------------------

@@ -486,3 +486,60 @@ def test_take_is_the_gather_of_dequantized_rows():
     # Q8_0 and MXFP4 parts: zero bytes decode to zeros as well
     assert np.all(O.q8_0_dequant_f32(np.zeros((1, 34), np.uint8)) == 0)
     assert np.all(O.mxfp4_blocks_dequant_f32(np.zeros((1, 17), np.uint8)) == 0)
+
+
+# ---------------------------------------------------------------- GPTQ -> affine transcoder
+# (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact transcoding; GPTQModel "Packing
+# Formats and Compatibility", GPTQ and GPTQ_V2)
+
+
+def _gptq_case(seed, k, n, bits, g, pow2_scales=False):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 1 << bits, size=(k, n))  # [in, out]
+    zeros = rng.integers(0, 1 << bits, size=(k // g, n))
+    # qweight: each column's codes as one stream down the input axis, built with the digit-string
+    # construction (independent of the oracle's packer); qzeros likewise along the outputs
+    qweight = np.stack([_stream_words_from_digits([int(c) for c in codes[:, j]], bits) for j in range(n)], axis=1)
+    qzeros = np.stack([_stream_words_from_digits([int(z) for z in zeros[r]], bits) for r in range(k // g)])
+    if pow2_scales:
+        s = np.ldexp(1.0, rng.integers(-12, -2, size=(k // g, n))).astype(np.float32)
+    else:
+        s = (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32)
+    return codes, zeros, qweight.astype(np.uint32), qzeros.astype(np.uint32), s
+
+
+@pytest.mark.parametrize("bits,pdt", [(4, "f16"), (3, "f16"), (2, "bf16"), (8, "f16")])
+def test_gptq_transcode_reconstructs_scale_times_code_minus_zero(bits, pdt):
+    k, n, g = 256, 64, 64
+    codes, zeros, qw, qz, s = _gptq_case(60 + bits, k, n, bits, g)
+    sb = O.to_bits(pdt, s)
+    pk, so, bo = O.gptq_transcode(qw, qz, sb, bits, g, k, n, pdt)
+    deq = O.affine_dequant_f32(pk, so, bo, bits, g, pdt, k).astype(np.float64)
+    # GPTQ's reconstruction written out directly from the drawn codes, zeros and stored scales
+    sv = O.bits_to_f64(pdt, sb)
+    want = np.repeat(sv.T, g, axis=1) * (codes.T - np.repeat(zeros.T, g, axis=1))
+    # the only rounding beyond fp32's is the bias -zero*scale stored in the parameter dtype
+    bias_exact = -(zeros.T.astype(np.float64)) * sv.T
+    slack = np.abs(O.bits_to_f64(pdt, bo) - bias_exact)
+    bound = np.repeat(slack, g, axis=1) + np.abs(want) * 2.0 ** -23 + 1e-30
+    assert np.all(np.abs(deq - want) <= bound)
+    np.testing.assert_array_equal(O.unpack_codes(pk, bits, k), codes.T)
+    np.testing.assert_array_equal(so, sb.T)
+
+
+def test_gptq_transcode_exact_when_bias_representable_and_v1_zeros():
+    k, n, g, bits = 128, 32, 32, 4
+    codes, zeros, qw, qz, s = _gptq_case(70, k, n, bits, g, pow2_scales=True)
+    sb = O.to_bits("f16", s)
+    pk, so, bo = O.gptq_transcode(qw, qz, sb, bits, g, k, n, "f16")
+    deq = O.affine_dequant_f32(pk, so, bo, bits, g, "f16", k).astype(np.float64)
+    want = np.repeat(s.T.astype(np.float64), g, axis=1) * (codes.T - np.repeat(zeros.T, g, axis=1))
+    np.testing.assert_array_equal(deq, want)
+    # v1 stores zero - 1: the same weight written that way (zeros >= 1 only) transcodes to the same
+    zeros1 = np.maximum(zeros, 1)
+    qz1 = np.stack([_stream_words_from_digits([int(z) - 1 for z in zeros1[r]], bits) for r in range(k // g)])
+    qz2 = np.stack([_stream_words_from_digits([int(z) for z in zeros1[r]], bits) for r in range(k // g)])
+    a = O.gptq_transcode(qw, qz1.astype(np.uint32), sb, bits, g, k, n, "f16", v1_zeros=True)
+    b = O.gptq_transcode(qw, qz2.astype(np.uint32), sb, bits, g, k, n, "f16")
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
