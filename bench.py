@@ -434,6 +434,20 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
     legs["take_4_experts_mxfp4_blocks"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
                                            "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
     del mxb, stack, got
+
+    # ---------------- GPTQ -> affine transcode of a 4096 -> 12288 layer (4-bit g128)
+    log("leg: GPTQ transcode")
+    K, N = 4096, 12288
+    qw = torch.randint(-2**31, 2**31 - 1, (K * 4 // 32, N), generator=gen(62_000), device=dev, dtype=torch.int32)
+    qz = torch.randint(-2**31, 2**31 - 1, (K // 128, N * 4 // 32), generator=gen(62_001), device=dev,
+                       dtype=torch.int32)
+    sc = (torch.rand((K // 128, N), generator=gen(62_002), device=dev) * 0.02 + 1e-3).to(torch.float16)
+    avg, _ = _time_launches(lambda _i: q.qlinear_transcode_gptq(qw, qz, sc, bits=4, group_size=128), 20, 5, stream)
+    byts = 2 * qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2 * 3
+    legs["transcode_gptq_4096x12288_4bit_g128"] = {
+        "ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+    del qw, qz, sc
     torch.cuda.empty_cache()
     return legs
 

@@ -97,6 +97,23 @@ ql_status qlinear_quantize_q8_0(const float* w, int64_t rows, int64_t k, uint8_t
 ql_status qlinear_take(const int64_t* pos, int64_t n_pos, const void* src, int64_t src_rows,
                        int64_t row_bytes, void* dst, void* stream);
 
+/* GPTQ -> MLX affine rows (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact
+ * transcoding; GPTQModel "Packing Formats and Compatibility", GPTQ and GPTQ_V2), continuous
+ * layout with contiguous groups (g_idx[k] = k / group_size):
+ *   in:  qweight [k*bits/32, n] uint32 (output column j's codes as one little-endian bits-wide
+ *        stream down the input axis), qzeros [k/group_size, n*bits/32] uint32 (each group's zeros
+ *        as one stream along the outputs), scales [k/group_size, n] in scale_dtype; the GPTQ value
+ *        is scale * (code - zero), and v1_zeros != 0 means the stored zeros are zero - 1.
+ *   out: packed [n, k*bits/32] (the affine row streams: qweight transposed word for word),
+ *        scales_out [n, k/group_size] (transposed), biases_out [n, k/group_size] =
+ *        RNE(-zero * scale) in scale_dtype (the product is exact in fp32).
+ * bits in {2, 3, 4, 8}; group_size in {32, 64, 128}; k % 32 == 0, k % group_size == 0 and
+ * n*bits % 32 == 0 (QL_ERR_SHAPE).  Word arrays 4-byte aligned, 16-bit arrays 2-byte aligned. */
+ql_status qlinear_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
+                                 ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size,
+                                 int v1_zeros, uint32_t* packed, void* scales_out, void* biases_out,
+                                 void* stream);
+
 /* dequant (Nx_quant Products, dequant): every value of W as a float32 value, rounded once to
  * out_dtype (QL_F32, QL_F16 or QL_BF16).  out is [rows, k].
  *   QL_AFFINE: w0 = packed [rows, k*bits/32], w1 = scales, w2 = biases [rows, k/group_size] in

@@ -1,0 +1,55 @@
+"""GPU parity of the GPTQ -> affine transcoder (GPTQModel wiki "MLX Apple Silicon", Packed
+layouts and exact transcoding; GPTQModel "Packing Formats and Compatibility", GPTQ and GPTQ_V2):
+packed words, scales and biases bit-exact against the oracle, and the transcoded weight through
+qlinear_gemv against GPTQ's own reconstruction scale * (code - zero)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+import weight_only_quantized_affine_amd as q
+from gpu_helpers import DEV, bits_to_dev, dev_to_bits, dev_to_u32, out_f64, u32_to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gptq(seed, k, n, bits, g, pdt):
+    rng = np.random.default_rng(seed)
+    qw = rng.integers(0, 1 << 32, size=(k * bits // 32, n), dtype=np.uint64).astype(np.uint32)
+    qz = rng.integers(0, 1 << 32, size=(k // g, n * bits // 32), dtype=np.uint64).astype(np.uint32)
+    sb = O.to_bits(pdt, (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32))
+    return qw, qz, sb
+
+
+@pytest.mark.parametrize("k,n,bits,g,pdt,v1", [
+    (4096, 4096, 4, 128, "f16", False),
+    (1024, 96, 3, 64, "f16", False),  # 3-bit streams crossing words; n not a multiple of 64
+    (2048, 130 * 16, 2, 32, "bf16", True),
+    (512, 300 * 4 // 4 * 4, 8, 64, "f16", True),
+    (96, 32, 4, 32, "bf16", False),  # a single ragged transpose tile
+])
+def test_transcode_gptq_bitexact(k, n, bits, g, pdt, v1):
+    qw, qz, sb = _gptq(k + n + bits, k, n, bits, g, pdt)
+    pk, so, bo = q.qlinear_transcode_gptq(u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, pdt), bits=bits,
+                                          group_size=g, v1_zeros=v1)
+    torch.cuda.synchronize()
+    opk, oso, obo = O.gptq_transcode(qw, qz, sb, bits, g, k, n, pdt, v1_zeros=v1)
+    np.testing.assert_array_equal(dev_to_u32(pk), opk)
+    np.testing.assert_array_equal(dev_to_bits(so), oso)
+    np.testing.assert_array_equal(dev_to_bits(bo), obo)
+
+
+def test_transcoded_gptq_weight_through_gemv():
+    k, n, bits, g = 2048, 1024, 4, 128
+    qw, qz, sb = _gptq(5, k, n, bits, g, "f16")
+    pk, so, bo = q.qlinear_transcode_gptq(u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, "f16"), bits=bits,
+                                          group_size=g)
+    xb = synth.acts_bits(6, 2, k, "bf16")
+    y = q.qlinear_gemv(bits_to_dev(xb, "bf16"), pk, so, bo, bits=bits, group_size=g, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.apply(O.bits_to_f64("bf16", xb), O.gptq_dequant_f64(qw, qz, sb, bits, g, k, n, "f16"))
+    err = O.rel_l2_per_row(out_f64(y), ref)
+    print(f"gptq transcode + gemv max rel-l2 {err.max():.3e}")
+    # the transcoded bias is -zero*scale rounded once to fp16 (2^-11 relative): well inside 2e-3
+    assert err.max() <= 2e-3

@@ -200,3 +200,24 @@ def test_quantize_q8_0_take_and_blocks_reject_bad_arguments(lib):
     assert lib.qlinear_dequant(3, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE + 2, F32, None) == QL_ERR_ALIGN
     assert lib.qlinear_dequant(3, None, None, None, BF16, 0, 64, 0, 0, None, F32, None) == QL_OK
     assert lib.qlinear_dequant(4, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_UNSUPPORTED
+
+
+def test_transcode_gptq_rejects_bad_arguments(lib):
+    args = [FAKE, FAKE, FAKE, F16, 256, 64, 4, 64, 0, FAKE, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["qw", "qz", "sc", "sdt", "k", "n", "bits", "g", "v1", "pk", "so", "bo", "s"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return lib.qlinear_transcode_gptq(*a)
+
+    assert call(bits=5) == QL_ERR_UNSUPPORTED
+    assert call(g=16) == QL_ERR_UNSUPPORTED
+    assert call(k=250) == QL_ERR_SHAPE
+    assert call(bits=3, n=60) == QL_ERR_SHAPE  # 180 bits: qzeros rows would not fill words
+    assert call(sdt=F32) == QL_ERR_DTYPE
+    assert call(qw=None) == QL_ERR_NULL
+    assert call(qz=FAKE + 2) == QL_ERR_ALIGN
+    assert call(so=FAKE + 1) == QL_ERR_ALIGN
+    assert call(k=0) == QL_OK

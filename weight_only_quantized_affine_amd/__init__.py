@@ -25,6 +25,7 @@ __all__ = [
     "qlinear_dequant",
     "qlinear_quantize_q8_0",
     "qlinear_take",
+    "qlinear_transcode_gptq",
     "qlinear_gemv",
     "qlinear_gemm",
     "qlinear_gemm_workspace_size",
@@ -77,6 +78,7 @@ _SIGNATURES = {
     "qlinear_dequant": (_INT, [_INT, _P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _INT, _P]),
     "qlinear_quantize_q8_0": (_INT, [_P, _I64, _I64, _P, _P]),
     "qlinear_take": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
+    "qlinear_transcode_gptq": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P]),
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
@@ -181,6 +183,22 @@ def qlinear_take(pos, src, dst=None):
     row_bytes = math.prod(src.shape[1:]) * src.element_size()
     _check(lib.qlinear_take(_ptr(pos), n_pos, _ptr(src), src.shape[0], row_bytes, _ptr(dst), _stream()))
     return dst
+
+
+def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: int, v1_zeros: bool = False):
+    """GPTQ (continuous layout, contiguous groups) -> affine (packed [n, k*bits/32] int32, scales and
+    biases [n, k/group_size] in scales' dtype).  qweight [k*bits/32, n], qzeros [G, n*bits/32]
+    (int32), scales [G, n]."""
+    torch = _torch()
+    lib = load_library()
+    n = scales.shape[1]
+    k = qweight.shape[0] * 32 // bits
+    packed = torch.empty((n, qweight.shape[0]), dtype=torch.int32, device=qweight.device)
+    so = torch.empty((n, scales.shape[0]), dtype=scales.dtype, device=qweight.device)
+    bo = torch.empty_like(so)
+    _check(lib.qlinear_transcode_gptq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits, group_size,
+                                      1 if v1_zeros else 0, _ptr(packed), _ptr(so), _ptr(bo), _stream()))
+    return packed, so, bo
 
 
 def qlinear_dequant(fmt: int, w0, w1=None, w2=None, *, rows: int, k: int, bits: int = 4, group_size: int = 64,
