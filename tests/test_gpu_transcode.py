@@ -53,3 +53,27 @@ def test_transcoded_gptq_weight_through_gemv():
     print(f"gptq transcode + gemv max rel-l2 {err.max():.3e}")
     # the transcoded bias is -zero*scale rounded once to fp16 (2^-11 relative): well inside 2e-3
     assert err.max() <= 2e-3
+
+
+def test_transcode_gptq_graph_replay_matches_eager():
+    """The transcoder captured in a HIP graph: each replay (outputs cleared, eager work between)
+    gives the eager outputs bit for bit."""
+    k, n, bits, g = 1024, 512, 4, 64
+    qw, qz, sb = _gptq(9, k, n, bits, g, "f16")
+    args = (u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, "f16"))
+    want = [t.clone() for t in q.qlinear_transcode_gptq(*args, bits=bits, group_size=g)]
+    outs = [torch.empty_like(t) for t in want]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        q.qlinear_transcode_gptq(*args, bits=bits, group_size=g, packed=outs[0], scales_out=outs[1],
+                                 biases_out=outs[2])
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        q.qlinear_transcode_gptq(*args, bits=bits, group_size=g)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            assert torch.equal(o, w), f"replay {rep}"

@@ -185,7 +185,8 @@ def qlinear_take(pos, src, dst=None):
     return dst
 
 
-def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: int, v1_zeros: bool = False):
+def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: int, v1_zeros: bool = False,
+                           packed=None, scales_out=None, biases_out=None):
     """GPTQ (continuous layout, contiguous groups) -> affine (packed [n, k*bits/32] int32, scales and
     biases [n, k/group_size] in scales' dtype).  qweight [k*bits/32, n], qzeros [G, n*bits/32]
     (int32), scales [G, n]."""
@@ -193,9 +194,11 @@ def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: in
     lib = load_library()
     n = scales.shape[1]
     k = qweight.shape[0] * 32 // bits
-    packed = torch.empty((n, qweight.shape[0]), dtype=torch.int32, device=qweight.device)
-    so = torch.empty((n, scales.shape[0]), dtype=scales.dtype, device=qweight.device)
-    bo = torch.empty_like(so)
+    if packed is None:
+        packed = torch.empty((n, qweight.shape[0]), dtype=torch.int32, device=qweight.device)
+    so = scales_out if scales_out is not None else torch.empty((n, scales.shape[0]), dtype=scales.dtype,
+                                                                device=qweight.device)
+    bo = biases_out if biases_out is not None else torch.empty_like(so)
     _check(lib.qlinear_transcode_gptq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits, group_size,
                                       1 if v1_zeros else 0, _ptr(packed), _ptr(so), _ptr(bo), _stream()))
     return packed, so, bo
