@@ -23,6 +23,14 @@
 namespace ql {
 namespace {
 
+typedef __attribute__((ext_vector_type(2))) uint16_t u16x2_t;
+
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
 
 template <typename XT> __device__ __forceinline__ float xval(uint32_t b);
 template <> __device__ __forceinline__ float xval<BF16>(uint32_t b) { return bf16_bits_to_f32(b); }
@@ -191,6 +199,9 @@ __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restri
   constexpr bool BX = std::is_same<XT, BF16>::value;
   constexpr uint32_t MAGIC = BX ? 0x43004300u : 0u;
   constexpr uint32_t ONES = BX ? 0x3F803F80u : 0x3C003C00u;
+  // the 2-bit pair mask and the offset in VGPRs once (the VOP3 forms, v_and_or_b32 among them,
+  // take no literal operand)
+  const uint32_t kMask2 = vgpr_const(0x00030003u), kMagic = vgpr_const(MAGIC);
   // x row j, value v at sx[j * pitch + v + 8 (v / 128)]: 16 bytes of padding after every 128
   // values, so that the lanes of a group (quads 256 bytes apart) read distinct banks
   extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
@@ -282,12 +293,28 @@ __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restri
               uint32_t cw[BITS];  // the chunk's words
 #pragma unroll
               for (int i = 0; i < BITS; ++i) cw[i] = w[r][(cc * BITS + i) >> 2][(cc * BITS + i) & 3];
+              if constexpr (BITS == 2) {
+                // the 8 codes of k-step q8 are one 16-bit half of a word: copied into both halves,
+                // one packed 16-bit shift per pair puts code 2e in the low half and 2e + 1 in the
+                // high one, and one and-or masks them and adds the offset
+                const uint32_t wd = cw[q8 >> 1];
+                const uint32_t hw = (q8 & 1) ? (wd >> 16) : (wd & 0xffffu);
+                const u16x2_t both = __builtin_bit_cast(u16x2_t, hw | (hw << 16));
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int i = 8 * q8 + 2 * e;
-                const uint32_t pr = (stream_code<BITS>(cw, i) | MAGIC) | (stream_code<BITS>(cw, i + 1) << 16);
+                for (int e = 0; e < 4; ++e) {
+                  const u16x2_t sh = {(uint16_t)(4 * e), (uint16_t)(4 * e + 2)};
+                  const uint32_t pr = (__builtin_bit_cast(uint32_t, both >> sh) & kMask2) | kMagic;
 #pragma unroll
-                for (int j = 0; j < MT; ++j) p[r][j] = dot2(XT(), xq[j][e], pr, p[r][j]);
+                  for (int j = 0; j < MT; ++j) p[r][j] = dot2(XT(), xq[j][e], pr, p[r][j]);
+                }
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int i = 8 * q8 + 2 * e;
+                  const uint32_t pr = (stream_code<BITS>(cw, i) | MAGIC) | (stream_code<BITS>(cw, i + 1) << 16);
+#pragma unroll
+                  for (int j = 0; j < MT; ++j) p[r][j] = dot2(XT(), xq[j][e], pr, p[r][j]);
+                }
               }
             }
           }
