@@ -199,9 +199,10 @@ __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restri
   constexpr bool BX = std::is_same<XT, BF16>::value;
   constexpr uint32_t MAGIC = BX ? 0x43004300u : 0u;
   constexpr uint32_t ONES = BX ? 0x3F803F80u : 0x3C003C00u;
-  // the 2-bit pair mask and the offset in VGPRs once (the VOP3 forms, v_and_or_b32 among them,
+  // the 2- and 3-bit pair masks and the offset in VGPRs once (the VOP3 forms, v_and_or_b32 among them,
   // take no literal operand)
   const uint32_t kMask2 = vgpr_const(0x00030003u), kMagic = vgpr_const(MAGIC);
+  const uint32_t kMask3 = vgpr_const(0x00070007u);
   // x row j, value v at sx[j * pitch + v + 8 (v / 128)]: 16 bytes of padding after every 128
   // values, so that the lanes of a group (quads 256 bytes apart) read distinct banks
   extern __shared__ __attribute__((aligned(16))) uint16_t sx[];
@@ -306,6 +307,27 @@ __global__ __launch_bounds__(256) void gemv_quad_kernel(const uint16_t* __restri
                   const uint32_t pr = (__builtin_bit_cast(uint32_t, both >> sh) & kMask2) | kMagic;
 #pragma unroll
                   for (int j = 0; j < MT; ++j) p[r][j] = dot2(XT(), xq[j][e], pr, p[r][j]);
+                }
+              } else if constexpr (BITS == 3) {
+                // two pairs (12 bits) start at bit 6 (2 e) of the stream: one 16-bit window of the
+                // chunk (funnel shift), copied into both halves, serves both; per pair one packed
+                // shift and one and-or as above
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                  const int pos = 3 * (8 * q8 + 4 * e2);
+                  const int wi = pos >> 5, sh = pos & 31;
+                  // only the window's 12 low bits are used: the next word is read only when they
+                  // cross into it (it then exists: pos + 12 <= 96)
+                  const uint32_t win =
+                      sh + 12 <= 32 ? (cw[wi] >> sh) : ((cw[wi] >> sh) | (cw[wi + 1] << (32 - sh)));
+                  const u16x2_t both = __builtin_bit_cast(u16x2_t, (win & 0xffffu) | (win << 16));
+#pragma unroll
+                  for (int h = 0; h < 2; ++h) {
+                    const u16x2_t shv = {(uint16_t)(6 * h), (uint16_t)(6 * h + 3)};
+                    const uint32_t pr = (__builtin_bit_cast(uint32_t, both >> shv) & kMask3) | kMagic;
+#pragma unroll
+                    for (int j = 0; j < MT; ++j) p[r][j] = dot2(XT(), xq[j][2 * e2 + h], pr, p[r][j]);
+                  }
                 }
               } else {
 #pragma unroll
