@@ -105,3 +105,16 @@ def test_take_experts_matrices():
     got = q.qlinear_take(torch.from_numpy(pos_np).to(DEV), u8_to_dev(codes))
     _sync()
     np.testing.assert_array_equal(got.cpu().numpy(), O.take(pos_np, codes))
+
+
+def test_take_four_byte_rows_and_empty_source():
+    """Rows of 12 bytes (4-byte units) and a source with no rows (every position out of range)."""
+    g = np.random.default_rng(44)
+    src = g.integers(0, 2**31, size=(50, 3)).astype(np.int32)
+    pos_np = np.array([49, 0, -5, 50, 25], dtype=np.int64)
+    got = q.qlinear_take(torch.from_numpy(pos_np).to(DEV), torch.from_numpy(src).to(DEV))
+    empty = torch.empty((0, 3), dtype=torch.int32, device=DEV)
+    got0 = q.qlinear_take(torch.from_numpy(pos_np).to(DEV), empty)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got.cpu().numpy(), O.take(pos_np, src))
+    assert np.all(got0.cpu().numpy() == 0)
