@@ -426,7 +426,7 @@ def test_gemv_batched_mixed_bits_small_list():
     _verify_decode(checks8, 8, "batched 8-bit")
 
 
-@pytest.mark.parametrize("bits,m", [(4, 1), (4, 8), (8, 1), (8, 8)])
+@pytest.mark.parametrize("bits,m", [(4, 1), (4, 8), (8, 1), (8, 8), (2, 1), (3, 1), (6, 1), (2, 8)])
 def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     """All 197 projections of the Qwen3-0.6B-shaped decode step in one problem-list launch (the
     bench's configuration), sampled rows of every projection against the oracle; a second launch
