@@ -173,6 +173,15 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   }
   gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
   const int c8n = KP / 8;
+  // x is staged MSU chunks of 8 values per thread at a time, their loads issued together (one
+  // round trip per MSU chunks); chunk t is (x row t / c8n, values 8 (t % c8n) ..), zero past m or k
+  constexpr int MSU = GEMV_MF_SU;
+  auto load_x = [&](int t, int total) __attribute__((always_inline)) {
+    const int xr = t / c8n, c8 = t - xr * c8n;
+    u32x4_t r = {0u, 0u, 0u, 0u};
+    if (t < total && xr < m && c8 * 8 < k) r = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+    return r;
+  };
   // bf16 x into f16 products: per x row the factor 2^-t that brings max |x| into [2^14, 2^15)
   // (t clamped to [-100, 100]; 2^t is kept for the end)
   float xmul[MT];
@@ -180,14 +189,17 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
     __shared__ uint32_t s_amax[MT];
     if (threadIdx.x < MT) s_amax[threadIdx.x] = 0u;
     __syncthreads();
-    for (int t = threadIdx.x; t < MT * c8n; t += 256) {
-      const int xr = t / c8n, c8 = t - xr * c8n;
-      if (xr < m && c8 * 8 < k) {
-        const u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+    for (int t0 = threadIdx.x; t0 < MT * c8n; t0 += 256 * MSU) {
+      u32x4_t raw[MSU];
+#pragma unroll
+      for (int u = 0; u < MSU; ++u) raw[u] = load_x(t0 + 256 * u, MT * c8n);
+#pragma unroll
+      for (int u = 0; u < MSU; ++u) {
+        const int t = t0 + 256 * u, xr = t / c8n;
         uint32_t a = 0u;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a = max(a, max(raw[e] & 0x7fffu, (raw[e] >> 16) & 0x7fffu));
-        atomicMax(&s_amax[xr], a);  // |x| of bf16 bits orders as the integer bits
+        for (int e = 0; e < 4; ++e) a = max(a, max(raw[u][e] & 0x7fffu, (raw[u][e] >> 16) & 0x7fffu));
+        if (t < MT * c8n && xr < m) atomicMax(&s_amax[xr], a);  // |x| of bf16 bits orders as the integer bits
       }
     }
     __syncthreads();
@@ -204,11 +216,19 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
     // One thread per 8 values: stage them, and sum them with the GW/8 neighbours of the same
     // accumulator row and u-block (aligned lane groups; (MT+1) * KP/8 is a multiple of 16).
     constexpr int GL = GW / 8;  // lanes per x sum: 16, 8 or 4
-    for (int t = threadIdx.x; t < (MT + 1) * c8n; t += 256) {
+    const int total = (MT + 1) * c8n;
+    for (int t0 = threadIdx.x; t0 < total; t0 += 256 * MSU) {
+      u32x4_t raws[MSU];
+#pragma unroll
+      for (int u = 0; u < MSU; ++u) raws[u] = load_x(t0 + 256 * u, total);
+#pragma unroll
+      for (int u = 0; u < MSU; ++u) {
+      const int t = t0 + 256 * u;
+      if (t >= total) break;
       const int xr = t / c8n, c8 = t - xr * c8n;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (xr < m && c8 * 8 < k) {
-        u32x4_t raw = *(gptr<u32x4_t>)(xg + (int64_t)xr * k + 8 * c8);
+        u32x4_t raw = raws[u];
         if constexpr (kConvX) {
           float f = 1.0f;
 #pragma unroll
@@ -230,6 +250,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       sum = group_sum(sum, GL);
       const int ub = c8 >> 4, gp = (c8 & 15) / GL;
       if (xr < MT && (c8 & (GL - 1)) == 0) xsum[ub * 16 + xr * GU + gp] = sum;
+      }
     }
     // accumulator rows past MT * GU have no x row: zero sums
     for (int t = threadIdx.x; t < SR * MNU * (16 - MT * GU); t += 256) {

@@ -101,7 +101,7 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #define GEMV_MF_NB 2  // step buffers of the load pipeline
 #endif
 #ifndef GEMV_MF_NB_M8
-#define GEMV_MF_NB_M8 3  // the same for 5 to 8 x rows
+#define GEMV_MF_NB_M8 4  // the same for 5 to 8 x rows
 #endif
 #ifndef GEMV_MF_SCHED
 #define GEMV_MF_SCHED 1
@@ -111,6 +111,9 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #endif
 #ifndef GEMV_MF_AUX
 #define GEMV_MF_AUX 0  // cache policy bits of the weight-word loads
+#endif
+#ifndef GEMV_MF_SU
+#define GEMV_MF_SU 4  // 16-byte chunks of x a thread loads at once when it stages x
 #endif
 struct GemvMfGeom {
   int ublocks;        // k / 128
