@@ -377,7 +377,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
     # ---------------- bitstream widths (2, 3, 6 bits): the decode step at batch 1, one problem-list
     # launch per step as above
     for bits in (2, 3, 6):
-        log(f"leg: {bits}-bit decode m=1 (bitstream GEMV)")
+        log(f"leg: {bits}-bit decode m=1")
         sets_b, wb, io = build_decode(bits, 1, 2, 70_000 + 100 * bits)
         wall, avg = time_decode(sets_b, 200, 300)
         legs[f"decode_{bits}bit_m1"] = {
@@ -385,7 +385,8 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
             "kernel_ms": round(avg, 5),
             "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "weights_bytes": wb,
-            "kernel": "gemv_quad_kernel (one problem-list launch per step)",
+            "kernel": ("gemv_mf_kernel<1, 64, bf16, bf16, 2>" if bits == 2 else "gemv_quad_kernel")
+            + " (one problem-list launch per step)",
         }
         del sets_b
         torch.cuda.empty_cache()

@@ -120,6 +120,8 @@ GEMV_STREAM_CASES = [
     (8, 1024, 1024, 3, 64, "f16", "bf16", "f32"),
     (11, 90, 512, 5, 64, "bf16", "bf16", "f32"),  # 8 + 3 rows of x
     (1, 40, 33792, 2, 64, "bf16", "bf16", "f32"),  # one x row through LDS in 2 slices
+    (8, 777, 2048, 2, 128, "f16", "bf16", "bf16"),  # 2 bits on the matrix cores: 8 x rows, ragged n
+    (2, 1000, 1152, 2, 64, "bf16", "f16", "f32"),  # an odd count of 128-code blocks per row
 ]
 
 

@@ -79,6 +79,26 @@ template <typename XT> struct Unpack<4, XT> {
   }
 };
 
+// 2-bit codes, two words (codes 0..15, 16..31) -> operand pairs as at 4 bits: product t takes the
+// codes 8t..8t+7 (bytes 2t, 2t+1 of the lane's 8), which one byte permute places in the low bytes
+// of the two halves, so that a shift by 2p and the mask give codes (8t+p, 8t+p+4).
+template <typename XT> struct Unpack<2, XT> {
+  static constexpr int NP = 16;
+  static constexpr float kOff = XTraits<XT>::kOff4;
+  static constexpr uint32_t kMask = 0x00030003u, kMagic = XTraits<XT>::kMagic4;
+  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t, uint32_t mk, uint32_t mg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t v = perm(0u, w[j >> 1], (j & 1) ? 0x0C030C02u : 0x0C010C00u);
+      t[4 * j + 0] = (v & mk) | mg;         // codes 8j + 0, 8j + 4
+      t[4 * j + 1] = ((v >> 2) & mk) | mg;  // codes 8j + 1, 8j + 5
+      t[4 * j + 2] = ((v >> 4) & mk) | mg;  // codes 8j + 2, 8j + 6
+      t[4 * j + 3] = ((v >> 6) & mk) | mg;  // codes 8j + 3, 8j + 7
+    }
+  }
+  __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
+};
+
 template <> struct Unpack<8, BF16> {
   static constexpr int NP = 8;
   static constexpr float kOff = 0.0f;

@@ -210,7 +210,7 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
   CHECK(n * k * bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: packed weights of 2 GiB or more", fn);
   for (int64_t m0 = 0; m0 < m; m0 += 8) {
     const int64_t mm = std::min<int64_t>(8, m - m0);
-    if (ql::is_stream_bits(bits)) {
+    if (ql::is_stream_bits(bits) && !ql::gemv_mf_eligible(mm, k, bits, group_size, scales, biases)) {
       ql::GemvStreamArgs a{};
       a.x = (const uint8_t*)x + m0 * k * 2;
       a.m = (int)mm;
@@ -325,8 +325,8 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
                                 probs[i].biases);
   };
   auto key = [&](int i) {
-    if (ql::is_stream_bits(probs[i].bits)) return (2 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256;
     if (mf(i)) return (1 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256 + probs[i].group_size;
+    if (ql::is_stream_bits(probs[i].bits)) return (2 << 16) + ql::gemv_mt(probs[i].m) * 4096 + probs[i].bits * 256;
     const bool g2 = probs[i].bits == 4 && probs[i].group_size == 32;
     return ql::gemv_mt(probs[i].m) * 32 + probs[i].bits * 2 + (g2 ? 1 : 0);
   };
@@ -340,8 +340,8 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
     c.m = 0;
     c.bits = probs[order[j]].bits;
     c.g2 = c.bits == 4 && probs[order[j]].group_size == 32;
-    c.stream = ql::is_stream_bits(c.bits);
-    c.mf_g = !c.stream && mf(order[j]) ? probs[order[j]].group_size : 0;
+    c.mf_g = mf(order[j]) ? probs[order[j]].group_size : 0;
+    c.stream = !c.mf_g && ql::is_stream_bits(c.bits);
     c.first_tile = plan.tiles.size();
     bool fits = true;
     size_t lds_x = 0, lds_lb = 0;
