@@ -122,6 +122,8 @@ GEMV_STREAM_CASES = [
     (1, 40, 33792, 2, 64, "bf16", "bf16", "f32"),  # one x row through LDS in 2 slices
     (8, 777, 2048, 2, 128, "f16", "bf16", "bf16"),  # 2 bits on the matrix cores: 8 x rows, ragged n
     (2, 1000, 1152, 2, 64, "bf16", "f16", "f32"),  # an odd count of 128-code blocks per row
+    (2, 333, 1152, 3, 128, "bf16", "f16", "bf16"),  # 3 bits on the matrix cores, ragged n, odd blocks
+    (4, 500, 2048, 3, 32, "f16", "bf16", "f32"),  # 3 bits, 4 x rows x 4 groups per block
 ]
 
 

@@ -99,6 +99,30 @@ template <typename XT> struct Unpack<2, XT> {
   __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
 };
 
+// 3-bit codes, three words (the lane's 96 bits) -> operand pairs as at 4 bits: the 24 bits of
+// codes 8t..8t+7 (one funnel shift) are split 12 + 12 into the two 16-bit halves, so that a shift
+// by 3p and the mask give codes (8t+p, 8t+p+4); bits above a half's 12 are never selected.
+template <typename XT> struct Unpack<3, XT> {
+  static constexpr int NP = 16;
+  static constexpr float kOff = XTraits<XT>::kOff4;
+  static constexpr uint32_t kMask = 0x00070007u, kMagic = XTraits<XT>::kMagic4;
+  __device__ __forceinline__ static void codes(const u32x4_t& w, uint32_t* t, uint32_t mk, uint32_t mg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = j == 0   ? w[0]
+                         : j == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
+                         : j == 2 ? __builtin_amdgcn_alignbit(w[2], w[1], 16)
+                                  : w[2] >> 8;
+      const uint32_t v = (u & 0xFFFFu) | ((u << 4) & 0xFFFF0000u);
+      t[4 * j + 0] = (v & mk) | mg;         // codes 8j + 0, 8j + 4
+      t[4 * j + 1] = ((v >> 3) & mk) | mg;  // codes 8j + 1, 8j + 5
+      t[4 * j + 2] = ((v >> 6) & mk) | mg;  // codes 8j + 2, 8j + 6
+      t[4 * j + 3] = ((v >> 9) & mk) | mg;  // codes 8j + 3, 8j + 7
+    }
+  }
+  __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
+};
+
 template <> struct Unpack<8, BF16> {
   static constexpr int NP = 8;
   static constexpr float kOff = 0.0f;
