@@ -385,8 +385,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
             "kernel_ms": round(avg, 5),
             "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
             "weights_bytes": wb,
-            "kernel": (f"gemv_mf_kernel<1, 64, bf16, bf16, {bits}>" if bits in (2, 3) else "gemv_quad_kernel")
-            + " (one problem-list launch per step)",
+            "kernel": f"gemv_mf_kernel<1, 64, bf16, bf16, {bits}> (one problem-list launch per step)",
         }
         del sets_b
         torch.cuda.empty_cache()

@@ -124,6 +124,8 @@ GEMV_STREAM_CASES = [
     (2, 1000, 1152, 2, 64, "bf16", "f16", "f32"),  # an odd count of 128-code blocks per row
     (2, 333, 1152, 3, 128, "bf16", "f16", "bf16"),  # 3 bits on the matrix cores, ragged n, odd blocks
     (4, 500, 2048, 3, 32, "f16", "bf16", "f32"),  # 3 bits, 4 x rows x 4 groups per block
+    (4, 300, 1152, 6, 32, "f16", "bf16", "f32"),  # 6 bits on the matrix cores, odd blocks
+    (8, 129, 1024, 6, 64, "bf16", "f16", "bf16"),  # 6 bits, 8 x rows, 16-bit output
 ]
 
 

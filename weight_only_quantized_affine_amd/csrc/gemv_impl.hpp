@@ -123,6 +123,31 @@ template <typename XT> struct Unpack<3, XT> {
   __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
 };
 
+// 6-bit codes, six words (a: words 0..3, b: words 4, 5) -> operand pairs as at 4 bits: the six
+// bytes c0..c5 of codes 8t..8t+7 give two byte permutes, (c0 c1 c3 c4) and (c1 c2 c4 c5), whose
+// shifts by 0, 6 and by 4, 10 with the mask give codes (8t+p, 8t+p+4).  (bf16 128 + q and fp16
+// 1024 + q stay exact for q < 64.)
+template <typename XT> struct Unpack<6, XT> {
+  static constexpr int NP = 16;
+  static constexpr float kOff = XTraits<XT>::kOff4;
+  static constexpr uint32_t kMask = 0x003F003Fu, kMagic = XTraits<XT>::kMagic4;
+  __device__ __forceinline__ static void codes2(const u32x4_t& a, const u32x4_t& b, uint32_t* t, uint32_t mk,
+                                                uint32_t mg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = j == 0 ? a[0] : j == 1 ? a[1] : j == 2 ? a[3] : b[0];
+      const uint32_t hi = j == 0 ? a[1] : j == 1 ? a[2] : j == 2 ? b[0] : b[1];
+      const uint32_t pa = perm(hi, lo, (j & 1) ? 0x06050302u : 0x04030100u);
+      const uint32_t pb = perm(hi, lo, (j & 1) ? 0x07060403u : 0x05040201u);
+      t[4 * j + 0] = (pa & mk) | mg;          // codes 8j + 0, 8j + 4
+      t[4 * j + 1] = ((pa >> 6) & mk) | mg;   // codes 8j + 1, 8j + 5
+      t[4 * j + 2] = ((pb >> 4) & mk) | mg;   // codes 8j + 2, 8j + 6
+      t[4 * j + 3] = ((pb >> 10) & mk) | mg;  // codes 8j + 3, 8j + 7
+    }
+  }
+  __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
+};
+
 template <> struct Unpack<8, BF16> {
   static constexpr int NP = 8;
   static constexpr float kOff = 0.0f;
