@@ -126,6 +126,8 @@ GEMV_STREAM_CASES = [
     (4, 500, 2048, 3, 32, "f16", "bf16", "f32"),  # 3 bits, 4 x rows x 4 groups per block
     (4, 300, 1152, 6, 32, "f16", "bf16", "f32"),  # 6 bits on the matrix cores, odd blocks
     (8, 129, 1024, 6, 64, "bf16", "f16", "bf16"),  # 6 bits, 8 x rows, 16-bit output
+    (8, 600, 2048, 5, 128, "f16", "f16", "f16"),  # 5 bits on the matrix cores, 8 x rows
+    (1, 4096, 1152, 5, 64, "bf16", "bf16", "f32"),  # 5 bits, odd blocks
 ]
 
 

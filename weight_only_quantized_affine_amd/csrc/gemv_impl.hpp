@@ -123,6 +123,33 @@ template <typename XT> struct Unpack<3, XT> {
   __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
 };
 
+// 5-bit codes, five words (a: words 0..3, b: word 4) -> operand pairs as at 4 bits: the 40 bits
+// of codes 8t..8t+7 give two 32-bit windows (funnel shifts at bits 40t and 40t + 10) whose low
+// half keeps its first two codes and whose high half takes its bits 20..35 (shift by 4), so
+// that shifts by 0 and 5 with the mask give codes (8t+p, 8t+p+4).
+template <typename XT> struct Unpack<5, XT> {
+  static constexpr int NP = 16;
+  static constexpr float kOff = XTraits<XT>::kOff4;
+  static constexpr uint32_t kMask = 0x001F001Fu, kMagic = XTraits<XT>::kMagic4;
+  __device__ __forceinline__ static void codes2(const u32x4_t& a, const u32x4_t& b, uint32_t* t, uint32_t mk,
+                                                uint32_t mg) {
+    const uint32_t w[5] = {a[0], a[1], a[2], a[3], b[0]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int o = 40 * j + 10 * hf, i = o / 32, sh = o % 32;  // constants after unrolling
+        const uint32_t u = sh == 0 ? w[i] : i + 1 < 5 ? __builtin_amdgcn_alignbit(w[i + 1 < 5 ? i + 1 : 4], w[i], sh)
+                                                      : w[i] >> sh;
+        const uint32_t v = (u & 0xFFFFu) | ((u >> 4) & 0xFFFF0000u);
+        t[4 * j + 2 * hf + 0] = (v & mk) | mg;         // codes 8j + 2hf, 8j + 2hf + 4
+        t[4 * j + 2 * hf + 1] = ((v >> 5) & mk) | mg;  // codes 8j + 2hf + 1, 8j + 2hf + 5
+      }
+    }
+  }
+  __device__ __forceinline__ static u32x4_t xperm(const u32x4_t& u) { return Unpack<4, XT>::xperm(u); }
+};
+
 // 6-bit codes, six words (a: words 0..3, b: words 4, 5) -> operand pairs as at 4 bits: the six
 // bytes c0..c5 of codes 8t..8t+7 give two byte permutes, (c0 c1 c3 c4) and (c1 c2 c4 c5), whose
 // shifts by 0, 6 and by 4, 10 with the mask give codes (8t+p, 8t+p+4).  (bf16 128 + q and fp16

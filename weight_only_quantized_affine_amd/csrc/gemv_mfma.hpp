@@ -1,18 +1,18 @@
-// Decode GEMV on the matrix cores for 2-, 3-, 4-, 6- and 8-bit affine codes: y[m,n] = x[m,k] . (code*scale +
+// Decode GEMV on the matrix cores for affine codes of 2 to 6 and 8 bits: y[m,n] = x[m,k] . (code*scale +
 // bias)^T, fp32 accumulation, one rounding to the output dtype -- the product of gemv_impl.hpp
 // (Nx_quant API docs, Products: apply; GPTQModel wiki "MLX Apple Silicon", Executing MLX qlinear
 // kernels), with the code-times-x sums done by v_mfma_f32_16x16x32 instead of v_dot2.
 //
 // One product D = A.B takes a 16x32 A and a 32x16 B (lane l: row or column l%16, k-slots
 // 8*(l/16)..+7; D: column l%16, rows 4*(l/16)..+3).  B is 16 weight rows, one per column: every
-// lane reads 32 codes of its row (8 bytes at 2 bits, 12 at 3, 16 at 4, 24 at 6, 32 at 8), and codes 8t..8t+7 of them are its
+// lane reads 32 codes of its row (8 bytes at 2 bits, 12 at 3, 16 at 4, 20 at 5, 24 at 6, 32 at 8), and codes 8t..8t+7 of them are its
 // k-slots in product t, so four products cover a u-block of 128 codes of 16 rows.  A carries x: its row i serves one
 // (x row, group of the u-block) pair, with x in the k-slots of that group and zeros in the others,
 // so accumulator row i collects that group's sum of x*code for that x row.  Each u-block ends with
 // the fold of every accumulator element with its group's scale and bias,
 //   acc += s * (D - off*X) + b * X,   X = that group's sum of x,
 // the codes entering as 16-bit floats off + q (exact), so that D - off*X is the group's sum of
-// x*q: 2-, 3-, 4- and 6-bit codes as bf16 128 + q with bf16 x and as f16 1024 + q with f16 x; 8-bit codes always
+// x*q: 2- to 6-bit codes as bf16 128 + q with bf16 x and as f16 1024 + q with f16 x; 8-bit codes always
 // as f16 1024 + q (bf16 has too few bits for 128 + q), with bf16 x converted to f16 after an exact
 // power-of-two scaling per x row that brings max |x| into [2^14, 2^15) (every bf16 value of that
 // row within 2^31 of the maximum converts exactly); the row's factor is applied at the end.
@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   // CT: the 16-bit type of the products' operands; x is converted (and scaled) to it when it differs
   using CT = typename std::conditional<BITS == 8, F16, XT>::type;
   constexpr bool kConvX = !std::is_same<CT, XT>::value;
-  // loads per row and u-block: one of 8, 12 or 16 bytes at 2, 3 or 4 bits; 16 + 8 at 6; 16 + 16 at 8
-  constexpr int WPB = BITS >= 6 ? 2 : 1;
+  // loads per row and u-block: one of 8, 12 or 16 bytes at 2, 3 or 4 bits; 16 + 4 at 5; 16 + 8 at 6;
+  // 16 + 16 at 8
+  constexpr int WPB = BITS >= 5 ? 2 : 1;
   constexpr int LB = 4 * BITS;                   // bytes of the lane's 32 codes
   using U = Unpack<BITS, CT>;
   constexpr int GU = gemv_mf_gu(G);                // groups per u-block
@@ -145,6 +146,10 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
           const u32x2_t t2 =
               __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
           q.w[rs][u][0] = u32x4_t{t2[0], t2[1], 0u, 0u};
+        } else if constexpr (BITS == 5) {  // 20 bytes at a 4-byte aligned offset
+          q.w[rs][u][0] =
+              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
+          q.w[rs][u][1] = u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, vw + 16, ub * 4 * LB, GEMV_MF_AUX), 0u, 0u, 0u};
         } else if constexpr (BITS == 6) {  // 24 bytes at an 8-byte aligned offset
           q.w[rs][u][0] =
               __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       for (int rs = 0; rs < MRS; ++rs) {
         // 16 operand words: product t takes words 4t .. 4t+3 (codes 8t .. 8t+7 of the lane's 32)
         uint32_t c[16];
-        if constexpr (BITS == 6) {
+        if constexpr (BITS == 5 || BITS == 6) {
           U::codes2(q.w[rs][u][0], q.w[rs][u][1], c, mk, mg);
         } else {
 #pragma unroll
@@ -416,6 +421,7 @@ hipError_t launch_mf_m(const GemvDesc& single, const GemvDesc* table, const Gemv
   if (bits == 2) return launch_mf_b<MT, 2>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
   if (bits == 3) return launch_mf_b<MT, 3>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
   if (bits == 6) return launch_mf_b<MT, 6>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
+  if (bits == 5) return launch_mf_b<MT, 5>(single, table, tiles, grid, lds, g, xdt, pdt, ydt, s);
   return hipErrorInvalidValue;
 }
 

@@ -79,7 +79,7 @@ struct GemvLds {
 };
 GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 
-// Matrix-core GEMV (2-, 3-, 4-, 6- or 8-bit codes, k a multiple of 128): a wave owns 16 * GEMV_MF_RS weight
+// Matrix-core GEMV (2- to 6- or 8-bit codes, k a multiple of 128): a wave owns 16 * GEMV_MF_RS weight
 // rows and walks them in u-blocks of 128 codes (64 or 128 bytes of each row); GEMV_MF_NU u-blocks
 // make one pipeline step.  A 256-thread workgroup walks `batches` sets of 64 * GEMV_MF_RS rows.
 #ifndef GEMV_MF_NU
@@ -152,12 +152,12 @@ __host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int b
 #ifndef GEMV_MF_ENABLE
 #define GEMV_MF_ENABLE 1
 #endif
-// Whether a problem takes the matrix-core GEMV: 2-, 3-, 4-, 6- or 8-bit codes, group size 32, 64 or 128, k a
+// Whether a problem takes the matrix-core GEMV: 2- to 6- or 8-bit codes, group size 32, 64 or 128, k a
 // multiple of 128 with an even number of groups per row, scales and biases 4-byte aligned, at
 // most 16 accumulator rows (rows of x times groups per u-block) and the LDS of one batch within
 // GEMV_MF_LDS_MAX.
 inline bool gemv_mf_eligible(int64_t m, int64_t k, int bits, int g, const void* scales, const void* biases) {
-  if (!GEMV_MF_ENABLE || (bits != 2 && bits != 3 && bits != 4 && bits != 6 && bits != 8) || k < 128 || k % 128 != 0 || (g != 32 && g != 64 && g != 128))
+  if (!GEMV_MF_ENABLE || bits < 2 || bits > 8 || bits == 7 || k < 128 || k % 128 != 0 || (g != 32 && g != 64 && g != 128))
     return false;
   if ((k / g) % 2 != 0 || ((uintptr_t)scales | (uintptr_t)biases) % 4 != 0) return false;
   const int mt = gemv_mt(m);
