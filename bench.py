@@ -376,7 +376,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
 
     # ---------------- bitstream widths (2, 3, 6 bits): the decode step at batch 1, one problem-list
     # launch per step as above
-    for bits in (2, 3, 6):
+    for bits in (2, 3, 5, 6):
         log(f"leg: {bits}-bit decode m=1")
         sets_b, wb, io = build_decode(bits, 1, 2, 70_000 + 100 * bits)
         wall, avg = time_decode(sets_b, 200, 300)
