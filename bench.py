@@ -40,6 +40,11 @@ def parse():
     ap.add_argument("--copies", type=int, default=3)
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated legs to run (decode8, decode4m8, prefill, experts, prefill6, decode_bits, "
+                         "quantize, blocks, transcode) or 'all'")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline decode step (for profiling single legs); prints the legs only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB (4 times): the reference for the HBM byte "
                          "counters that the roofline traffic figure is scaled by")
@@ -180,6 +185,10 @@ def main():
         del gw, gt
         return wall, avg_ms
 
+    if args.no_headline:
+        legs = run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, args.legs)
+        print(json.dumps({"legs": legs}), flush=True)
+        return
     log("building the 4-bit decode workload (3 weight copies)")
     sets4, wbytes4, io4 = build_decode(4, 1, args.copies, 20_000)
     log(f"weights per step {wbytes4} B; timing {args.steps} steps after {args.warmup} warmup")
@@ -228,7 +237,7 @@ def main():
 
     legs = {}
     if not args.no_legs:
-        legs = run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode)
+        legs = run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, args.legs)
     result["legs"] = legs
     if "prefill_gemm_9b_layer" in legs:
         result["prefill_gemm_tflops"] = legs["prefill_gemm_9b_layer"]["tflops"]
@@ -253,10 +262,17 @@ def _time_launches(fn, reps, warmup, stream):
     return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
 
 
-def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
+def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which="all"):
+    sel = set(which.split(",")) if which != "all" else None
+
+    def want(name):
+        return sel is None or name in sel
+
     legs = {}
     # ---------------- 8-bit decode at batch 1 and 8, 4-bit decode at batch 8
     for bits, m in ((8, 1), (8, 8), (4, 8)):
+        if not want("decode4m8" if bits == 4 else "decode8"):
+            continue
         log(f"leg: {bits}-bit decode m={m}")
         sets_b, wb, io = build_decode(bits, m, 2, 30_000 + 100 * bits + m)
         wall, avg = time_decode(sets_b, 200, 300)
@@ -270,200 +286,208 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode):
         torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM, 9B-class layer at M = 2048
-    log("leg: prefill GEMM 9B layer, M=2048")
-    m = 2048
-    per = {}
-    tot_flop = 0.0
-    tot_ms = 0.0
-    for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
-        w = torch.randn((n, k), generator=gen(40_000 + i), device=dev) * 0.02
-        pk, sc, bi = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
-        del w
-        x = torch.randn((m, k), generator=gen(41_000 + i), device=dev).to(torch.bfloat16)
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 4, 64), dtype=torch.uint8, device=dev)
-        avg, med = _time_launches(
-            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 20, 60, stream)
-        flop = 2.0 * m * n * k
-        per[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
-        tot_flop += flop
-        tot_ms += avg
-        del pk, sc, bi, x, y, ws
-    torch.cuda.empty_cache()
-    tflops = tot_flop / (tot_ms * 1e-3) / 1e12
-    legs["prefill_gemm_9b_layer"] = {
-        "tflops": round(tflops, 1),
-        "layer_ms": round(tot_ms, 4),
-        "gflop": round(tot_flop / 1e9, 1),
-        "prefill_tokens_per_s_per_layer": round(m / (tot_ms * 1e-3), 0),
-        "per_projection": per,
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "prep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
-    }
+    if want("prefill"):
+        log("leg: prefill GEMM 9B layer, M=2048")
+        m = 2048
+        per = {}
+        tot_flop = 0.0
+        tot_ms = 0.0
+        for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
+            w = torch.randn((n, k), generator=gen(40_000 + i), device=dev) * 0.02
+            pk, sc, bi = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
+            del w
+            x = torch.randn((m, k), generator=gen(41_000 + i), device=dev).to(torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 4, 64), dtype=torch.uint8, device=dev)
+            avg, med = _time_launches(
+                lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 20, 60, stream)
+            flop = 2.0 * m * n * k
+            per[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+            tot_flop += flop
+            tot_ms += avg
+            del pk, sc, bi, x, y, ws
+        torch.cuda.empty_cache()
+        tflops = tot_flop / (tot_ms * 1e-3) / 1e12
+        legs["prefill_gemm_9b_layer"] = {
+            "tflops": round(tflops, 1),
+            "layer_ms": round(tot_ms, 4),
+            "gflop": round(tot_flop / 1e9, 1),
+            "prefill_tokens_per_s_per_layer": round(m / (tot_ms * 1e-3), 0),
+            "per_projection": per,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
+        }
 
     # ---------------- routed experts, MXFP4 and Q8_0
-    cfg = synth.EXPERTS_32x5760x2880
-    e, n, k, tokens, top = cfg["e"], cfg["n"], cfg["k"], cfg["tokens"], cfg["top"]
-    ids = torch.from_numpy(synth.topk_ids(synth.seed_for(5, part=2), tokens, top, e).reshape(-1)).to(dev)
-    x = torch.randn((tokens, k), generator=gen(50_000), device=dev).to(torch.bfloat16)
-    y = torch.empty((tokens * top, n), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(q.qlinear_apply_experts_workspace_size(tokens * top, e), dtype=torch.uint8, device=dev)
-    flop = 2.0 * tokens * top * n * k
-    for fmt, fname in ((q.QL_MXFP4, "mxfp4"), (q.QL_Q8_0, "q8_0")):
-        log(f"leg: experts {fname}")
-        copies = []
-        for c in range(3):
-            if fmt == q.QL_MXFP4:
-                codes = torch.randint(0, 256, (e, n, k // 2), generator=gen(51_000 + c), device=dev,
-                                      dtype=torch.int32).to(torch.uint8)
-                scales = torch.randint(118, 131, (e, n, k // 32), generator=gen(52_000 + c), device=dev,
-                                       dtype=torch.int32).to(torch.uint8)
-                copies.append((codes, scales))
-                wb = codes.numel() + scales.numel()
-            else:
-                nb = k // 32
-                d = torch.exp2(torch.empty((e, n, nb), device=dev).uniform_(-14, -9, generator=gen(53_000 + c)))
-                d = d.to(torch.float16).view(torch.uint8).view(e, n, nb, 2)
-                qv = torch.randint(-127, 128, (e, n, nb, 32), generator=gen(54_000 + c), device=dev,
-                                   dtype=torch.int32).to(torch.int8).view(torch.uint8)
-                blocks = torch.cat([d, qv], dim=3).reshape(e, n, nb * 34).contiguous()
-                copies.append((blocks, None))
-                wb = blocks.numel()
-        avg, med = _time_launches(
-            lambda i: q.qlinear_apply_experts(fmt, copies[i % 3][0], copies[i % 3][1], ids, x, n=n, k=k,
-                                              pos_per_row=top, y=y, workspace=ws), 20, 20, stream)
-        byts = wb + x.numel() * 2 + y.numel() * 2
-        gbs = byts / (avg * 1e-3) / 1e9
-        legs[f"experts_{fname}"] = {
-            "ms": round(avg, 4),
-            "gbs": round(gbs, 1),
-            "tflops": round(flop / (avg * 1e-3) / 1e12, 1),
-            "weights_bytes": wb,
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                         "kernel": "route_kernel + " + ("experts_mx_kernel" if fname == "mxfp4" else "experts_q8_kernel")},
-        }
-        del copies
-        torch.cuda.empty_cache()
+    if want("experts"):
+        cfg = synth.EXPERTS_32x5760x2880
+        e, n, k, tokens, top = cfg["e"], cfg["n"], cfg["k"], cfg["tokens"], cfg["top"]
+        ids = torch.from_numpy(synth.topk_ids(synth.seed_for(5, part=2), tokens, top, e).reshape(-1)).to(dev)
+        x = torch.randn((tokens, k), generator=gen(50_000), device=dev).to(torch.bfloat16)
+        y = torch.empty((tokens * top, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(q.qlinear_apply_experts_workspace_size(tokens * top, e), dtype=torch.uint8, device=dev)
+        flop = 2.0 * tokens * top * n * k
+        for fmt, fname in ((q.QL_MXFP4, "mxfp4"), (q.QL_Q8_0, "q8_0")):
+            log(f"leg: experts {fname}")
+            copies = []
+            for c in range(3):
+                if fmt == q.QL_MXFP4:
+                    codes = torch.randint(0, 256, (e, n, k // 2), generator=gen(51_000 + c), device=dev,
+                                          dtype=torch.int32).to(torch.uint8)
+                    scales = torch.randint(118, 131, (e, n, k // 32), generator=gen(52_000 + c), device=dev,
+                                           dtype=torch.int32).to(torch.uint8)
+                    copies.append((codes, scales))
+                    wb = codes.numel() + scales.numel()
+                else:
+                    nb = k // 32
+                    d = torch.exp2(torch.empty((e, n, nb), device=dev).uniform_(-14, -9, generator=gen(53_000 + c)))
+                    d = d.to(torch.float16).view(torch.uint8).view(e, n, nb, 2)
+                    qv = torch.randint(-127, 128, (e, n, nb, 32), generator=gen(54_000 + c), device=dev,
+                                       dtype=torch.int32).to(torch.int8).view(torch.uint8)
+                    blocks = torch.cat([d, qv], dim=3).reshape(e, n, nb * 34).contiguous()
+                    copies.append((blocks, None))
+                    wb = blocks.numel()
+            avg, med = _time_launches(
+                lambda i: q.qlinear_apply_experts(fmt, copies[i % 3][0], copies[i % 3][1], ids, x, n=n, k=k,
+                                                  pos_per_row=top, y=y, workspace=ws), 20, 20, stream)
+            byts = wb + x.numel() * 2 + y.numel() * 2
+            gbs = byts / (avg * 1e-3) / 1e9
+            legs[f"experts_{fname}"] = {
+                "ms": round(avg, 4),
+                "gbs": round(gbs, 1),
+                "tflops": round(flop / (avg * 1e-3) / 1e12, 1),
+                "weights_bytes": wb,
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": "route_kernel + " + ("experts_mx_kernel" if fname == "mxfp4" else "experts_q8_kernel")},
+            }
+            del copies
+            torch.cuda.empty_cache()
 
     # ---------------- prefill GEMM at 6 bits (bitstream rows: codes re-packed as bytes, then the 8-bit
     # kernel), same layer and M
-    log("leg: prefill GEMM 9B layer, M=2048, 6-bit")
-    tot_flop = tot_ms = 0.0
-    per6 = {}
-    for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
-        w = torch.randn((n, k), generator=gen(45_000 + i), device=dev) * 0.02
-        pk, sc, bi = q.qlinear_quantize(w, 6, 64, torch.bfloat16)
-        del w
-        x = torch.randn((m, k), generator=gen(46_000 + i), device=dev).to(torch.bfloat16)
-        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 6, 64), dtype=torch.uint8, device=dev)
-        avg, _ = _time_launches(
-            lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=6, group_size=64, y=y, workspace=ws), 10, 20, stream)
-        flop = 2.0 * m * n * k
-        per6[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
-        tot_flop += flop
-        tot_ms += avg
-        del pk, sc, bi, x, y, ws
-    torch.cuda.empty_cache()
-    legs["prefill_gemm_9b_layer_6bit"] = {
-        "tflops": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1),
-        "layer_ms": round(tot_ms, 4),
-        "per_projection": per6,
-        "kernel": "stream_to_bytes + prep16 + gemm16_kernel<8,false,false> (+ splitk_reduce on k/v)",
-    }
-
-    # ---------------- bitstream widths (2, 3, 6 bits): the decode step at batch 1, one problem-list
-    # launch per step as above
-    for bits in (2, 3, 5, 6):
-        log(f"leg: {bits}-bit decode m=1")
-        sets_b, wb, io = build_decode(bits, 1, 2, 70_000 + 100 * bits)
-        wall, avg = time_decode(sets_b, 200, 300)
-        legs[f"decode_{bits}bit_m1"] = {
-            "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 2),
-            "kernel_ms": round(avg, 5),
-            "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
-            "weights_bytes": wb,
-            "kernel": f"gemv_mf_kernel<1, 64, bf16, bf16, {bits}> (one problem-list launch per step)",
-        }
-        del sets_b
+    if want("prefill6"):
+        log("leg: prefill GEMM 9B layer, M=2048, 6-bit")
+        m = 2048
+        tot_flop = tot_ms = 0.0
+        per6 = {}
+        for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
+            w = torch.randn((n, k), generator=gen(45_000 + i), device=dev) * 0.02
+            pk, sc, bi = q.qlinear_quantize(w, 6, 64, torch.bfloat16)
+            del w
+            x = torch.randn((m, k), generator=gen(46_000 + i), device=dev).to(torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 6, 64), dtype=torch.uint8, device=dev)
+            avg, _ = _time_launches(
+                lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=6, group_size=64, y=y, workspace=ws), 10, 20, stream)
+            flop = 2.0 * m * n * k
+            per6[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+            tot_flop += flop
+            tot_ms += avg
+            del pk, sc, bi, x, y, ws
         torch.cuda.empty_cache()
+        legs["prefill_gemm_9b_layer_6bit"] = {
+            "tflops": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1),
+            "layer_ms": round(tot_ms, 4),
+            "per_projection": per6,
+            "kernel": "stream_to_bytes + prep16 + gemm16_kernel<8,false,false> (+ splitk_reduce on k/v)",
+        }
+
+    # ---------------- bitstream widths (2, 3, 5, 6 bits): the decode step at batch 1, one problem-list
+    # launch per step as above
+    if want("decode_bits"):
+        for bits in (2, 3, 5, 6):
+            log(f"leg: {bits}-bit decode m=1")
+            sets_b, wb, io = build_decode(bits, 1, 2, 70_000 + 100 * bits)
+            wall, avg = time_decode(sets_b, 200, 300)
+            legs[f"decode_{bits}bit_m1"] = {
+                "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 2),
+                "kernel_ms": round(avg, 5),
+                "pct_hbm_peak": round(100 * (wb + io) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                "weights_bytes": wb,
+                "kernel": f"gemv_mf_kernel<1, 64, bf16, bf16, {bits}> (one problem-list launch per step)",
+            }
+            del sets_b
+            torch.cuda.empty_cache()
 
     # ---------------- quantizer on the lm_head-sized matrix (151936 x 1024)
-    log("leg: quantize")
-    w = torch.randn((151936, 1024), generator=gen(60_000), device=dev) * 0.02
-    pk = torch.empty((151936, 128), dtype=torch.int32, device=dev)
-    sc = torch.empty((151936, 16), dtype=torch.bfloat16, device=dev)
-    bi = torch.empty_like(sc)
-    avg, _ = _time_launches(lambda _i: q.qlinear_quantize(w, 4, 64, torch.bfloat16, pk, sc, bi), 10, 2, stream)
-    byts = w.numel() * 4 + pk.numel() * 4 + sc.numel() * 4
-    legs["quantize_4bit_g64_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
-                                             "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-    out = torch.empty((151936, 1024), dtype=torch.bfloat16, device=dev)
-    avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_AFFINE, pk, sc, bi, rows=151936, k=1024, bits=4,
-                                                         group_size=64, out=out), 10, 2, stream)
-    byts = out.numel() * 2 + pk.numel() * 4 + sc.numel() * 4
-    legs["dequant_4bit_g64_151936x1024_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1)}
-    del pk, sc, bi, out
+    if want("quantize"):
+        log("leg: quantize")
+        w = torch.randn((151936, 1024), generator=gen(60_000), device=dev) * 0.02
+        pk = torch.empty((151936, 128), dtype=torch.int32, device=dev)
+        sc = torch.empty((151936, 16), dtype=torch.bfloat16, device=dev)
+        bi = torch.empty_like(sc)
+        avg, _ = _time_launches(lambda _i: q.qlinear_quantize(w, 4, 64, torch.bfloat16, pk, sc, bi), 10, 2, stream)
+        byts = w.numel() * 4 + pk.numel() * 4 + sc.numel() * 4
+        legs["quantize_4bit_g64_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                                 "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        out = torch.empty((151936, 1024), dtype=torch.bfloat16, device=dev)
+        avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_AFFINE, pk, sc, bi, rows=151936, k=1024, bits=4,
+                                                             group_size=64, out=out), 10, 2, stream)
+        byts = out.numel() * 2 + pk.numel() * 4 + sc.numel() * 4
+        legs["dequant_4bit_g64_151936x1024_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1)}
+        del pk, sc, bi, out
 
     # ---------------- quantize_q8_0, MXFP4 in GGUF blocks, take (HBM-bound byte movers)
-    log("leg: quantize_q8_0, MXFP4 blocks dequant, take")
-    blocks = torch.empty((151936, 1024 // 32 * 34), dtype=torch.uint8, device=dev)
-    avg, _ = _time_launches(lambda _i: q.qlinear_quantize_q8_0(w, blocks), 10, 2, stream)
-    byts = w.numel() * 4 + blocks.numel()
-    legs["quantize_q8_0_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
-                                         "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-    del w, blocks
-    e_, n_, k_ = 32, 5760, 2880
-    mxb = torch.randint(0, 256, (e_ * n_, k_ // 32 * 17), generator=gen(61_000), device=dev,
-                        dtype=torch.int32).to(torch.uint8)
-    mxb.view(e_ * n_, k_ // 32, 17)[:, :, 0] = 127
-    out = torch.empty((e_ * n_, k_), dtype=torch.bfloat16, device=dev)
-    avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_MXFP4_BLOCKS, mxb, rows=e_ * n_, k=k_, out=out),
-                            10, 2, stream)
-    byts = mxb.numel() + out.numel() * 2
-    legs["dequant_mxfp4_blocks_32x5760x2880_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
-                                                      "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-    del out
-    stack = mxb.view(e_, n_, k_ // 32 * 17)
-    pos = torch.tensor([3, 17, 30, 8], dtype=torch.int64, device=dev)
-    got = torch.empty((4, n_, k_ // 32 * 17), dtype=torch.uint8, device=dev)
-    avg, _ = _time_launches(lambda _i: q.qlinear_take(pos, stack, got), 20, 5, stream)
-    byts = 2 * got.numel()
-    legs["take_4_experts_mxfp4_blocks"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
-                                           "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-    del mxb, stack, got
+    if want("blocks"):
+        log("leg: quantize_q8_0, MXFP4 blocks dequant, take")
+        blocks = torch.empty((151936, 1024 // 32 * 34), dtype=torch.uint8, device=dev)
+        avg, _ = _time_launches(lambda _i: q.qlinear_quantize_q8_0(w, blocks), 10, 2, stream)
+        byts = w.numel() * 4 + blocks.numel()
+        legs["quantize_q8_0_151936x1024"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                             "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del w, blocks
+        e_, n_, k_ = 32, 5760, 2880
+        mxb = torch.randint(0, 256, (e_ * n_, k_ // 32 * 17), generator=gen(61_000), device=dev,
+                            dtype=torch.int32).to(torch.uint8)
+        mxb.view(e_ * n_, k_ // 32, 17)[:, :, 0] = 127
+        out = torch.empty((e_ * n_, k_), dtype=torch.bfloat16, device=dev)
+        avg, _ = _time_launches(lambda _i: q.qlinear_dequant(q.QL_MXFP4_BLOCKS, mxb, rows=e_ * n_, k=k_, out=out),
+                                10, 2, stream)
+        byts = mxb.numel() + out.numel() * 2
+        legs["dequant_mxfp4_blocks_32x5760x2880_bf16"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                                          "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del out
+        stack = mxb.view(e_, n_, k_ // 32 * 17)
+        pos = torch.tensor([3, 17, 30, 8], dtype=torch.int64, device=dev)
+        got = torch.empty((4, n_, k_ // 32 * 17), dtype=torch.uint8, device=dev)
+        avg, _ = _time_launches(lambda _i: q.qlinear_take(pos, stack, got), 20, 5, stream)
+        byts = 2 * got.numel()
+        legs["take_4_experts_mxfp4_blocks"] = {"ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                                               "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del mxb, stack, got
 
     # ---------------- GPTQ -> affine transcode of a 4096 -> 12288 layer (4-bit g128)
-    log("leg: GPTQ transcode")
-    K, N = 4096, 12288
-    qw = torch.randint(-2**31, 2**31 - 1, (K * 4 // 32, N), generator=gen(62_000), device=dev, dtype=torch.int32)
-    qz = torch.randint(-2**31, 2**31 - 1, (K // 128, N * 4 // 32), generator=gen(62_001), device=dev,
-                       dtype=torch.int32)
-    sc = (torch.rand((K // 128, N), generator=gen(62_002), device=dev) * 0.02 + 1e-3).to(torch.float16)
-    pk_o, so_o, bo_o = q.qlinear_transcode_gptq(qw, qz, sc, bits=4, group_size=128)
-    torch.cuda.synchronize()
-    g_tc = torch.cuda.CUDAGraph()  # 20 calls replayed as one graph: GPU time, not host pacing
-    with torch.cuda.graph(g_tc):
-        for _ in range(20):
-            q.qlinear_transcode_gptq(qw, qz, sc, bits=4, group_size=128, packed=pk_o, scales_out=so_o,
-                                     biases_out=bo_o)
-    g_tc.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    g_tc.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    avg = e0.elapsed_time(e1) / 20
-    del g_tc, pk_o, so_o, bo_o
-    byts = 2 * qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2 * 3
-    legs["transcode_gptq_4096x12288_4bit_g128"] = {
-        "ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
-        "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
-    del qw, qz, sc
-    torch.cuda.empty_cache()
+    if want("transcode"):
+        log("leg: GPTQ transcode")
+        K, N = 4096, 12288
+        qw = torch.randint(-2**31, 2**31 - 1, (K * 4 // 32, N), generator=gen(62_000), device=dev, dtype=torch.int32)
+        qz = torch.randint(-2**31, 2**31 - 1, (K // 128, N * 4 // 32), generator=gen(62_001), device=dev,
+                           dtype=torch.int32)
+        sc = (torch.rand((K // 128, N), generator=gen(62_002), device=dev) * 0.02 + 1e-3).to(torch.float16)
+        pk_o, so_o, bo_o = q.qlinear_transcode_gptq(qw, qz, sc, bits=4, group_size=128)
+        torch.cuda.synchronize()
+        g_tc = torch.cuda.CUDAGraph()  # 20 calls replayed as one graph: GPU time, not host pacing
+        with torch.cuda.graph(g_tc):
+            for _ in range(20):
+                q.qlinear_transcode_gptq(qw, qz, sc, bits=4, group_size=128, packed=pk_o, scales_out=so_o,
+                                         biases_out=bo_o)
+        g_tc.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g_tc.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg = e0.elapsed_time(e1) / 20
+        del g_tc, pk_o, so_o, bo_o
+        byts = 2 * qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2 * 3
+        legs["transcode_gptq_4096x12288_4bit_g128"] = {
+            "ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del qw, qz, sc
+        torch.cuda.empty_cache()
     return legs
 
 

@@ -172,10 +172,14 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
  * (count entries), validated on the host like qlinear_gemv; the device table built from it (the
  * problems and their row tiles) is written to `workspace` (device memory of at least
  * qlinear_gemv_batched_workspace_size(probs, count) bytes, which depends on the shapes).
- * upload != 0 copies the table host-to-device on `stream` and waits for that copy (the only
- * synchronizing call of the library); upload == 0 reuses the table an earlier call with the
- * SAME list left in the same workspace (the caller guarantees it is unchanged), so only the
- * launches are enqueued.  The dtypes are shared by the whole list. */
+ * upload != 0 enqueues the copy of the table to the workspace on `stream` (it travels inside the
+ * arguments of small copy launches, so the call neither waits nor keeps any host memory, and it
+ * may be captured into a graph); upload == 0 reuses the table an earlier call with the SAME list
+ * left in the same workspace (the caller guarantees it is unchanged), so only the product
+ * launches are enqueued.  The dtypes are shared by the whole list.
+ * No page defines a list form: each problem is the product of qlinear_gemv (Nx_quant Products,
+ * apply), and the list is this library's way to run a whole decode step's projections in one
+ * launch per class instead of one short launch each. */
 size_t qlinear_gemv_batched_workspace_size(const ql_problem* probs, int count);
 ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dtype,
                                ql_dtype param_dtype, ql_dtype y_dtype, void* workspace,
@@ -207,7 +211,9 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
                                 const void* x, ql_dtype x_dtype, int64_t pos_per_row, void* y,
                                 ql_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
-/* Message of the last failing call on this thread ("" after a successful call). */
+/* Message of the last failing call on this thread ("" after a successful call).  Errors name the
+ * offending argument, as the Nx_quant API docs' constructors and products name the part they
+ * reject (Weights; Products, "Raises Invalid_argument ... naming the part"). */
 const char* qlinear_last_error(void);
 /* Library version string. */
 const char* qlinear_version(void);

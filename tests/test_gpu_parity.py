@@ -426,7 +426,7 @@ def test_gemv_batched_mixed_bits_small_list():
     _verify_decode(checks8, 8, "batched 8-bit")
 
 
-@pytest.mark.parametrize("bits,m", [(4, 1), (4, 8), (8, 1), (8, 8), (2, 1), (3, 1), (6, 1), (2, 8)])
+@pytest.mark.parametrize("bits,m", [(4, 1), (4, 8), (8, 1), (8, 8), (2, 1), (3, 1), (5, 1), (6, 1), (2, 8), (6, 8)])
 def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     """All 197 projections of the Qwen3-0.6B-shaped decode step in one problem-list launch (the
     bench's configuration), sampled rows of every projection against the oracle; a second launch
@@ -442,6 +442,34 @@ def test_gemv_batched_qwen3_0_6b_full_list(bits, m):
     _sync()
     assert all(torch.equal(a, p["y"]) for a, p in zip(first, probs))
     _verify_decode(checks, bits, f"qwen3-0.6b decode {bits}-bit m={m}")
+
+
+def test_gemv_batched_upload_is_asynchronous_and_capturable():
+    """upload=True enqueues the table copy on the stream without waiting: the whole call, upload
+    included, captured into a graph and replayed into a fresh workspace, gives the eager bits."""
+    shapes = synth.QWEN3_0_6B_LAYER[:3]
+    probs, _ = _decode_problems(4, 1, shapes, 72500)
+    arr = q.qlinear_problem_list(probs)
+    nbytes = q.qlinear_gemv_batched_workspace_size(arr)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    kw = dict(x_dtype=torch.bfloat16, param_dtype=torch.bfloat16, y_dtype=torch.float32)
+    q.qlinear_gemv_batched(arr, upload=True, workspace=ws, **kw)
+    _sync()
+    eager = [p["y"].clone() for p in probs]
+    ws2 = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlinear_gemv_batched(arr, upload=True, workspace=ws2, **kw)
+    for rep in range(3):
+        ws2.zero_()
+        for p in probs:
+            p["y"].fill_(rep + 7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ws2, ws), f"replay {rep}: table"
+        assert all(torch.equal(a, p["y"]) for a, p in zip(eager, probs)), f"replay {rep}"
 
 
 def test_gemv_batched_graph_replay_matches_eager():

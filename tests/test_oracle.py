@@ -543,3 +543,31 @@ def test_gptq_transcode_exact_when_bias_representable_and_v1_zeros():
     b = O.gptq_transcode(qw, qz2.astype(np.uint32), sb, bits, g, k, n, "f16")
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("bits,pdt,g", [(4, "f16", 64), (3, "bf16", 32), (2, "f16", 128), (8, "bf16", 64)])
+@pytest.mark.parametrize("v1", [False, True])
+def test_gptq_dequant_is_scale_times_code_minus_zero(bits, pdt, g, v1):
+    """GPTQ's reconstruction (GPTQModel "Packing Formats and Compatibility", GPTQ and GPTQ_V2:
+    value = scale * (code - zero), v1 storing zero - 1) against the drawn codes, zeros and stored
+    scales written out element by element in pure Python (no unpacking shared with the oracle:
+    qweight and qzeros are built by the digit-string construction)."""
+    k, n = 256, 32
+    rng = np.random.default_rng(80 + bits + (7 if v1 else 0))
+    codes = rng.integers(0, 1 << bits, size=(k, n))
+    zeros = rng.integers(1 if v1 else 0, 1 << bits, size=(k // g, n))
+    stored = zeros - 1 if v1 else zeros
+    qw = np.stack([_stream_words_from_digits([int(c) for c in codes[:, j]], bits) for j in range(n)], axis=1)
+    qz = np.stack([_stream_words_from_digits([int(z) for z in stored[r]], bits) for r in range(k // g)])
+    sb = O.to_bits(pdt, (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32))
+    got = O.gptq_dequant_f64(qw.astype(np.uint32), qz.astype(np.uint32), sb, bits, g, k, n, pdt, v1_zeros=v1)
+    assert got.shape == (n, k)
+    sv = O.bits_to_f64(pdt, sb)
+    for j in range(n):
+        for i in range(0, k, 7):  # every 7th input of every output column
+            want = float(sv[i // g, j]) * (int(codes[i, j]) - int(zeros[i // g, j]))
+            assert got[j, i] == want, (j, i)
+    # a plausible misreading of the v1 convention (zero stored as is) shifts every value by one scale
+    if v1:
+        wrong = O.gptq_dequant_f64(qw.astype(np.uint32), qz.astype(np.uint32), sb, bits, g, k, n, pdt)
+        np.testing.assert_allclose(wrong - got, np.repeat(sv.T, g, axis=1))

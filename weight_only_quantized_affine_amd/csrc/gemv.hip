@@ -2,6 +2,9 @@
 // ALU) and gemv_mfma.hpp (matrix cores), their instantiations in gemv_m{1,2,4,8}.hip.
 #include "launch.hpp"
 
+#include <algorithm>
+#include <cstring>
+
 namespace ql {
 
 // Launchers of the per-row-count instantiations (gemv_m{1,2,4,8}.hip).
@@ -63,6 +66,33 @@ hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const Gemv
     case 4: return launch_gemv_m4(single, table, tiles, grid, lds_bytes, xlds, g2, bits, xdt, pdt, ydt, s);
     default: return launch_gemv_m8(single, table, tiles, grid, lds_bytes, xlds, g2, bits, xdt, pdt, ydt, s);
   }
+}
+
+// The problem table of a list travels to the device inside kernel arguments, kUploadWords words
+// per launch: the runtime copies a launch's arguments when it is enqueued, so the host image may
+// be released as soon as the call returns, and the upload is ordered on the stream like any
+// launch (no host wait; it can be captured into a graph).
+constexpr int kUploadWords = 496;  // 1984 bytes of payload per launch, well inside the argument limit
+struct UploadChunk {
+  uint32_t w[kUploadWords];
+};
+__global__ __launch_bounds__(256) void upload_words_kernel(UploadChunk c, int nwords, uint32_t* __restrict__ dst) {
+  for (int i = threadIdx.x; i < nwords; i += 256) dst[i] = c.w[i];
+}
+
+hipError_t launch_upload(const void* host, size_t bytes, void* dst, hipStream_t s) {
+  const uint8_t* src = (const uint8_t*)host;
+  const size_t words = (bytes + 3) / 4;
+  for (size_t w0 = 0; w0 < words; w0 += kUploadWords) {
+    const int nw = (int)std::min<size_t>(kUploadWords, words - w0);
+    UploadChunk c{};
+    const size_t b0 = w0 * 4, nb = std::min<size_t>((size_t)nw * 4, bytes - b0);
+    memcpy(c.w, src + b0, nb);
+    upload_words_kernel<<<1, 256, 0, s>>>(c, nw, (uint32_t*)dst + w0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace ql

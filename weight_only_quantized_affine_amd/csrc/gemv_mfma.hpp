@@ -138,32 +138,34 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
 #pragma unroll
     for (int rs = 0; rs < MRS; ++rs) {
       const int lr = lrow0 + b * kSetRows + rs * 16;
-      const int vw = live ? lr * row_bytes + LB * h : kOOB;
+      // unsigned, so that the second load's vw + 16 past the end wraps instead of overflowing; an
+      // offset at or past 0x7ffffff0 stays outside every resource (they are below 2^31 bytes)
+      const uint32_t vw = live ? (uint32_t)(lr * row_bytes + LB * h) : (uint32_t)kOOB;
 #pragma unroll
       for (int u = 0; u < MNU; ++u) {
         const int ub = min(i * MNU + u, UB - 1);
         if constexpr (BITS == 2) {
           const u32x2_t t2 =
-              __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
+              __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)vw, ub * 4 * LB, GEMV_MF_AUX));
           q.w[rs][u][0] = u32x4_t{t2[0], t2[1], 0u, 0u};
         } else if constexpr (BITS == 5) {  // 20 bytes at a 4-byte aligned offset
           q.w[rs][u][0] =
-              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
-          q.w[rs][u][1] = u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, vw + 16, ub * 4 * LB, GEMV_MF_AUX), 0u, 0u, 0u};
+              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vw, ub * 4 * LB, GEMV_MF_AUX));
+          q.w[rs][u][1] = u32x4_t{__builtin_amdgcn_raw_buffer_load_b32(rw, (int)(vw + 16u), ub * 4 * LB, GEMV_MF_AUX), 0u, 0u, 0u};
         } else if constexpr (BITS == 6) {  // 24 bytes at an 8-byte aligned offset
           q.w[rs][u][0] =
-              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw, ub * 4 * LB, GEMV_MF_AUX));
+              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)vw, ub * 4 * LB, GEMV_MF_AUX));
           const u32x2_t t2 =
-              __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, vw + 16, ub * 4 * LB, GEMV_MF_AUX));
+              __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rw, (int)(vw + 16u), ub * 4 * LB, GEMV_MF_AUX));
           q.w[rs][u][1] = u32x4_t{t2[0], t2[1], 0u, 0u};
         } else if constexpr (BITS == 3) {  // 12 bytes at a 4-byte aligned offset
-          const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(rw, vw, ub * 4 * LB, GEMV_MF_AUX);
+          const auto t3 = __builtin_amdgcn_raw_buffer_load_b96(rw, (int)vw, ub * 4 * LB, GEMV_MF_AUX);
           q.w[rs][u][0] = u32x4_t{t3[0], t3[1], t3[2], 0u};
         } else {
 #pragma unroll
           for (int c = 0; c < WPB; ++c)
             q.w[rs][u][c] = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, vw + 16 * c, ub * 4 * LB, GEMV_MF_AUX));
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(vw + 16u * c), ub * 4 * LB, GEMV_MF_AUX));
         }
       }
     }

@@ -186,6 +186,9 @@ hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, v
 
 // One GEMV (desc passed by value, table == NULL) or `grid` tiles of a device problem table
 // (all problems of one launch share the row-count template of m and bits).
+// Copies `bytes` of host memory to device memory `dst` (4-byte aligned) through kernel arguments:
+// asynchronous on `s`, the host memory may be reused when the call returns.
+hipError_t launch_upload(const void* host, size_t bytes, void* dst, hipStream_t s);
 hipError_t launch_gemv(const GemvDesc& single, const GemvDesc* table, const GemvTile* tiles, int64_t grid, int m,
                        int bits, int xdt, int pdt, int ydt, size_t lds_bytes, int xlds, bool g2, hipStream_t s);
 // The same for the matrix-core GEMV; every problem of the launch has `bits` and group size `g`.

@@ -451,9 +451,8 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
     std::vector<uint8_t> host(plan.bytes);
     memcpy(host.data(), plan.descs.data(), plan.descs.size() * sizeof(ql::GemvDesc));
     memcpy(host.data() + plan.tiles_offset, plan.tiles.data(), plan.tiles.size() * sizeof(ql::GemvTile));
-    hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return launched(e, fn);
-    e = hipStreamSynchronize(s);  // the staging vector is released on return
+    // through kernel arguments: asynchronous, and the host image may go when the call returns
+    const hipError_t e = ql::launch_upload(host.data(), host.size(), ws, s);
     if (e != hipSuccess) return launched(e, fn);
   }
   const ql::GemvDesc* d_descs = (const ql::GemvDesc*)ws;
