@@ -211,6 +211,21 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
                                 const void* x, ql_dtype x_dtype, int64_t pos_per_row, void* y,
                                 ql_dtype y_dtype, void* workspace, size_t ws_bytes, void* stream);
 
+/* qlinear_apply_experts for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and results,
+ * but the routing scratch (offsets, permutation, expert order, x row factors: the workspace of
+ * qlinear_apply_experts_workspace_size(n_pos, e) bytes) lives in a device array built into the
+ * library, QL_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call allocates
+ * nothing.  Sizes that need more scratch than that return QL_ERR_UNSUPPORTED (about 87,000
+ * positions with 32 experts).  Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (on different streams, or from several threads) race and must be ordered by the
+ * caller; calls on one stream are ordered by it. */
+#define QL_NOALLOC_SCRATCH_BYTES (1u << 20)
+ql_status qlinear_apply_experts_noalloc(ql_format fmt, const void* w0, const void* w1, int64_t e,
+                                        int64_t n, int64_t k, const int64_t* ids, int64_t n_pos,
+                                        const void* x, ql_dtype x_dtype, int64_t pos_per_row, void* y,
+                                        ql_dtype y_dtype, void* stream);
+
 /* Message of the last failing call on this thread ("" after a successful call).  Errors name the
  * offending argument, as the Nx_quant API docs' constructors and products name the part they
  * reject (Weights; Products, "Raises Invalid_argument ... naming the part"). */

@@ -221,3 +221,12 @@ def test_transcode_gptq_rejects_bad_arguments(lib):
     assert call(qz=FAKE + 2) == QL_ERR_ALIGN
     assert call(so=FAKE + 1) == QL_ERR_ALIGN
     assert call(k=0) == QL_OK
+
+
+def test_apply_experts_noalloc_rejects_sizes_past_its_scratch(lib):
+    # 100,000 positions need 12 bytes each of routing scratch: past the 1 MiB built-in array
+    st = lib.qlinear_apply_experts_noalloc(1, FAKE, FAKE, 32, 64, 64, FAKE, 100_000, FAKE, BF16, 1, FAKE, BF16, None)
+    assert st == QL_ERR_UNSUPPORTED
+    assert "scratch" in _err(lib)
+    assert lib.qlinear_apply_experts_noalloc(1, FAKE, FAKE, -1, 64, 64, FAKE, 4, FAKE, BF16, 1, FAKE, BF16,
+                                             None) == QL_ERR_SHAPE

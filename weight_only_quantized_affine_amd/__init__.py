@@ -35,6 +35,7 @@ __all__ = [
     "qlinear_route",
     "qlinear_apply_experts",
     "qlinear_apply_experts_workspace_size",
+    "qlinear_apply_experts_noalloc",
     "qlinear_version",
 ]
 
@@ -87,6 +88,7 @@ _SIGNATURES = {
     "qlinear_route": (_INT, [_P, _I64, _I64, _P, _P, _P]),
     "qlinear_apply_experts_workspace_size": (_SZ, [_I64, _I64]),
     "qlinear_apply_experts": (_INT, [_INT, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _INT, _I64, _P, _INT, _P, _SZ, _P]),
+    "qlinear_apply_experts_noalloc": (_INT, [_INT, _P, _P, _I64, _I64, _I64, _P, _I64, _P, _INT, _I64, _P, _INT, _P]),
     "qlinear_last_error": (ctypes.c_char_p, []),
     "qlinear_version": (ctypes.c_char_p, []),
 }
@@ -316,4 +318,14 @@ def qlinear_apply_experts(fmt: int, w0, w1, ids, x, *, n: int, k: int, pos_per_r
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _check(lib.qlinear_apply_experts(fmt, _ptr(w0), _ptr(w1), e, n, k, _ptr(ids), n_pos, _ptr(x), _dt(x), pos_per_row,
                                      _ptr(y), _dt(y), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def qlinear_apply_experts_noalloc(fmt: int, w0, w1, ids, x, *, n: int, k: int, y, pos_per_row: int = 1):
+    """qlinear_apply_experts with the routing scratch in the library's built-in device array: no
+    workspace, nothing allocated (y is the caller's output tensor [n_pos, n])."""
+    lib = load_library()
+    e = w0.shape[0]
+    _check(lib.qlinear_apply_experts_noalloc(fmt, _ptr(w0), _ptr(w1), e, n, k, _ptr(ids), ids.numel(), _ptr(x), _dt(x),
+                                             pos_per_row, _ptr(y), _dt(y), _stream()))
     return y

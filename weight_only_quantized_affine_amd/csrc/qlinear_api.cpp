@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -542,3 +543,53 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- routed apply without allocation
+// The routing scratch of qlinear_apply_experts_noalloc lives in this file-scope device array: one
+// copy per GPU, loaded with the library's code object and held until the process ends.  Host code
+// never uses the array's name as an address: the device address of this GPU's copy is queried
+// once per device (hipGetSymbolAddress, with that device current) and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[QL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; null until its first call
+
+ql_status scratch_for_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return launched(e, fn);
+  CHECK(dev >= 0 && dev < kMaxDevices, QL_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices supported", fn, dev,
+        kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return launched(e, fn);
+    CHECK(p != nullptr, QL_ERR_LAUNCH, "%s: no device address for the scratch array on device %d", fn, dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QL_OK;
+}
+}  // namespace
+
+extern "C" ql_status qlinear_apply_experts_noalloc(ql_format fmt, const void* w0, const void* w1, int64_t e,
+                                                   int64_t n, int64_t k, const int64_t* ids, int64_t n_pos,
+                                                   const void* x, ql_dtype x_dtype, int64_t pos_per_row, void* y,
+                                                   ql_dtype y_dtype, void* stream) {
+  const char* fn = "qlinear_apply_experts_noalloc";
+  CHECK(e >= 0 && n_pos >= 0, QL_ERR_SHAPE, "%s: e and n_pos must be >= 0", fn);
+  const size_t need = qlinear_apply_experts_workspace_size(n_pos, e);
+  CHECK(need <= (size_t)QL_NOALLOC_SCRATCH_BYTES, QL_ERR_UNSUPPORTED,
+        "%s: n_pos=%lld and e=%lld need %zu bytes of routing scratch, more than the %u bytes of the built-in array "
+        "(use qlinear_apply_experts with a workspace)",
+        fn, (long long)n_pos, (long long)e, need, (unsigned)QL_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const ql_status st = scratch_for_current_device(fn, &ws);
+  if (st != QL_OK) return st;
+  // the routing kernel writes every scratch word the apply kernels read, so nothing is cleared
+  return qlinear_apply_experts(fmt, w0, w1, e, n, k, ids, n_pos, x, x_dtype, pos_per_row, y, y_dtype, ws,
+                               (size_t)QL_NOALLOC_SCRATCH_BYTES, stream);
+}
