@@ -285,27 +285,45 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
         del sets_b
         torch.cuda.empty_cache()
 
-    # ---------------- prefill GEMM, 9B-class layer at M = 2048
+    # ---------------- prefill GEMM, 9B-class layer at M = 2048: the layer's four inputs, each through
+    # one call (q|k|v and gate|up as grouped calls over the weights that read the same x), plus each
+    # projection alone through qlinear_gemm
     if want("prefill"):
         log("leg: prefill GEMM 9B layer, M=2048")
         m = 2048
-        per = {}
-        tot_flop = 0.0
-        tot_ms = 0.0
+        wts = {}
         for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
             w = torch.randn((n, k), generator=gen(40_000 + i), device=dev) * 0.02
             pk, sc, bi = q.qlinear_quantize(w, 4, 64, torch.bfloat16)
             del w
-            x = torch.randn((m, k), generator=gen(41_000 + i), device=dev).to(torch.bfloat16)
-            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 4, 64), dtype=torch.uint8, device=dev)
-            avg, med = _time_launches(
-                lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=4, group_size=64, y=y, workspace=ws), 20, 60, stream)
-            flop = 2.0 * m * n * k
-            per[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+            wts[name] = dict(packed=pk, scales=sc, biases=bi, y=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+                             k=k, n=n)
+        calls = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
+        per_call = {}
+        tot_flop = tot_ms = 0.0
+        for ci, (cname, members) in enumerate(calls):
+            k = wts[members[0]]["k"]
+            x = torch.randn((m, k), generator=gen(41_000 + ci), device=dev).to(torch.bfloat16)
+            ws_list = [dict(packed=wts[nm]["packed"], scales=wts[nm]["scales"], biases=wts[nm]["biases"], y=wts[nm]["y"])
+                       for nm in members]
+            ws = torch.empty(q.qlinear_gemm_grouped_workspace_size(m, k, ws_list, 4, 64), dtype=torch.uint8,
+                             device=dev)
+            avg, _ = _time_launches(lambda _i: q.qlinear_gemm_grouped(x, ws_list, bits=4, group_size=64, workspace=ws),
+                                    20, 60, stream)
+            flop = sum(2.0 * m * wts[nm]["n"] * k for nm in members)
+            per_call[cname] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
             tot_flop += flop
             tot_ms += avg
-            del pk, sc, bi, x, y, ws
+            # each projection alone (qlinear_gemm)
+            for nm in members:
+                w_ = wts[nm]
+                ws1 = torch.empty(q.qlinear_gemm_workspace_size(m, w_["n"], k, 4, 64), dtype=torch.uint8, device=dev)
+                a1, _ = _time_launches(lambda _i: q.qlinear_gemm(x, w_["packed"], w_["scales"], w_["biases"], bits=4,
+                                                                 group_size=64, y=w_["y"], workspace=ws1), 20, 30,
+                                       stream)
+                w_["single"] = {"ms": round(a1, 4), "tflops": round(2.0 * m * w_["n"] * k / (a1 * 1e-3) / 1e12, 1)}
+                del ws1
+            del x, ws
         torch.cuda.empty_cache()
         tflops = tot_flop / (tot_ms * 1e-3) / 1e12
         legs["prefill_gemm_9b_layer"] = {
@@ -313,11 +331,13 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
             "layer_ms": round(tot_ms, 4),
             "gflop": round(tot_flop / 1e9, 1),
             "prefill_tokens_per_s_per_layer": round(m / (tot_ms * 1e-3), 0),
-            "per_projection": per,
+            "per_call": per_call,
+            "per_projection_single_call": {nm: wts[nm]["single"] for nm in wts},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "prep16 + gemm16_kernel<4,false,*> (+ splitk_reduce on k/v)"},
+                         "kernel": "prep_pp + gemm_pp_kernel<4,64,128> (q|k|v and gate|up grouped; o, down alone)"},
         }
+        del wts
 
     # ---------------- routed experts, MXFP4 and Q8_0
     if want("experts"):

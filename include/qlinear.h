@@ -166,6 +166,32 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
                        const void* layer_bias, void* y, ql_dtype y_dtype, void* workspace,
                        size_t ws_bytes, void* stream);
 
+/* One weight of qlinear_gemm_grouped: its own packed words, scales, biases (device memory), optional
+ * layer bias, output y [m, n] and row count n.  The weights share k, bits, group_size and dtypes. */
+typedef struct {
+  const uint32_t* packed;
+  const void* scales;
+  const void* biases;
+  const void* layer_bias;
+  void* y;
+  int64_t n;
+} ql_gemm_weight;
+
+/* Prefill GEMM of up to four weights that read the same x (the projections one layer input feeds,
+ * such as q, k and v, or gate and up): y_j = x . dequant(W_j)^T for each, the product of
+ * qlinear_gemm (Nx_quant Products, apply), with x converted once and one launch over the tiles of
+ * every weight, so that small weights do not need a launch of their own.  Each y_j equals what
+ * qlinear_gemm gives for W_j alone whenever that call runs on the same kernel (4- and 8-bit codes
+ * and enough output tiles: then the grouped call always does); at other shapes and widths the
+ * call runs qlinear_gemm once per weight.  Arguments as qlinear_gemm; count in [0, 4]; the
+ * workspace is qlinear_gemm_grouped_workspace_size bytes, 16-byte aligned. */
+size_t qlinear_gemm_grouped_workspace_size(int64_t m, int64_t k, const ql_gemm_weight* weights, int count,
+                                           int bits, int group_size);
+ql_status qlinear_gemm_grouped(const void* x, ql_dtype x_dtype, int64_t m, int64_t k,
+                               const ql_gemm_weight* weights, int count, ql_dtype param_dtype, int bits,
+                               int group_size, ql_dtype y_dtype, void* workspace, size_t ws_bytes,
+                               void* stream);
+
 /* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
  * 1/2/4/8, bits); bits and group_size may differ between problems (at 2, 3, 5 and 6 bits a
  * problem's k must be a positive multiple of 128, else QL_ERR_UNSUPPORTED).  `probs` is HOST memory

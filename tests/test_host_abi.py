@@ -230,3 +230,20 @@ def test_apply_experts_noalloc_rejects_sizes_past_its_scratch(lib):
     assert "scratch" in _err(lib)
     assert lib.qlinear_apply_experts_noalloc(1, FAKE, FAKE, -1, 64, 64, FAKE, 4, FAKE, BF16, 1, FAKE, BF16,
                                              None) == QL_ERR_SHAPE
+
+
+def test_gemm_grouped_rejects_bad_arguments(lib):
+    W = q._GemmWeight
+    arr = (W * 5)()
+    for i in range(5):
+        arr[i] = W(FAKE, FAKE, FAKE, None, FAKE, 64)
+    assert lib.qlinear_gemm_grouped(FAKE, BF16, 8, 64, arr, 5, BF16, 4, 64, F32, FAKE, 1 << 20, None) == QL_ERR_SHAPE
+    assert "count=5" in _err(lib)
+    arr[1] = W(FAKE, FAKE, FAKE, None, FAKE, -1)
+    assert lib.qlinear_gemm_grouped(FAKE, BF16, 8, 64, arr, 2, BF16, 4, 64, F32, FAKE, 1 << 20, None) == QL_ERR_SHAPE
+    assert "weight 1" in _err(lib)
+    arr[1] = W(FAKE, FAKE, FAKE, None, FAKE, 64)
+    assert lib.qlinear_gemm_grouped(FAKE, BF16, 8, 64, arr, 2, BF16, 7, 64, F32, FAKE, 1 << 20, None) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_gemm_grouped(FAKE, BF16, 8, 64, arr, 2, BF16, 4, 64, F32, None, 0, None) == QL_ERR_WORKSPACE
+    assert lib.qlinear_gemm_grouped(FAKE, BF16, 0, 64, arr, 2, BF16, 4, 64, F32, None, 0, None) == QL_OK
+    assert lib.qlinear_gemm_grouped(None, BF16, 8, 64, None, 0, BF16, 4, 64, F32, None, 0, None) == QL_OK

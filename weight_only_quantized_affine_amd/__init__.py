@@ -29,6 +29,8 @@ __all__ = [
     "qlinear_gemv",
     "qlinear_gemm",
     "qlinear_gemm_workspace_size",
+    "qlinear_gemm_grouped",
+    "qlinear_gemm_grouped_workspace_size",
     "qlinear_gemv_batched",
     "qlinear_gemv_batched_workspace_size",
     "qlinear_problem_list",
@@ -53,6 +55,17 @@ class QLError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"[ql_status {status}] {message}")
         self.status = status
+
+
+class _GemmWeight(ctypes.Structure):
+    _fields_ = [
+        ("packed", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("biases", ctypes.c_void_p),
+        ("layer_bias", ctypes.c_void_p),
+        ("y", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
 
 
 class _Problem(ctypes.Structure):
@@ -83,6 +96,9 @@ _SIGNATURES = {
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
+    "qlinear_gemm_grouped_workspace_size": (_SZ, [_I64, _I64, ctypes.POINTER(_GemmWeight), _INT, _INT, _INT]),
+    "qlinear_gemm_grouped": (_INT, [_P, _INT, _I64, _I64, ctypes.POINTER(_GemmWeight), _INT, _INT, _INT, _INT, _INT, _P,
+                                    _SZ, _P]),
     "qlinear_gemv_batched_workspace_size": (_SZ, [ctypes.POINTER(_Problem), _INT]),
     "qlinear_gemv_batched": (_INT, [ctypes.POINTER(_Problem), _INT, _INT, _INT, _INT, _P, _SZ, _INT, _P]),
     "qlinear_route": (_INT, [_P, _I64, _I64, _P, _P, _P]),
@@ -254,6 +270,40 @@ def qlinear_gemm(x, packed, scales, biases, *, bits: int, group_size: int, layer
                             group_size, _ptr(layer_bias), _ptr(y), _dt(y), _ptr(workspace), workspace.numel(),
                             _stream()))
     return y
+
+
+def _gemm_weights(weights):
+    arr = (_GemmWeight * max(1, len(weights)))()
+    for i, w in enumerate(weights):
+        arr[i] = _GemmWeight(_ptr(w["packed"]), _ptr(w["scales"]), _ptr(w["biases"]), _ptr(w.get("layer_bias")),
+                             _ptr(w.get("y")), w["packed"].shape[0])
+    return arr
+
+
+def qlinear_gemm_grouped_workspace_size(m: int, k: int, weights: Sequence[dict], bits: int, group_size: int) -> int:
+    return int(load_library().qlinear_gemm_grouped_workspace_size(m, k, _gemm_weights(weights), len(weights), bits,
+                                                                  group_size))
+
+
+def qlinear_gemm_grouped(x, weights: Sequence[dict], *, bits: int, group_size: int, y_dtype=None, workspace=None):
+    """Prefill products of up to four weights that read the same x: each weight is a dict with
+    tensors packed, scales, biases, optional layer_bias and optional output y (allocated here when
+    absent).  Returns the list of outputs."""
+    torch = _torch()
+    lib = load_library()
+    m, k = x.shape
+    ws_in = [dict(w) for w in weights]
+    for w in ws_in:
+        if w.get("y") is None:
+            w["y"] = torch.empty((m, w["packed"].shape[0]), dtype=y_dtype or x.dtype, device=x.device)
+    arr = _gemm_weights(ws_in)
+    if workspace is None:
+        need = qlinear_gemm_grouped_workspace_size(m, k, ws_in, bits, group_size)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ydt = ws_in[0]["y"] if ws_in else x
+    _check(lib.qlinear_gemm_grouped(_ptr(x), _dt(x), m, k, arr, len(ws_in), _dt(ws_in[0]["scales"]) if ws_in else 2,
+                                    bits, group_size, _dt(ydt), _ptr(workspace), workspace.numel(), _stream()))
+    return [w["y"] for w in ws_in]
 
 
 def qlinear_problem_list(problems):

@@ -43,6 +43,21 @@
 namespace ql {
 namespace {
 
+#ifndef GEMM_PP_INTERLEAVE
+#define GEMM_PP_INTERLEAVE 4  // vector instructions scheduled after each product of the ping-pong kernel
+#endif
+#ifndef GEMM_PP_COPY_IN_COMPUTE
+#define GEMM_PP_COPY_IN_COMPUTE 0  // issue the HBM->LDS copies among the products instead of in the mem phase
+#endif
+#ifndef GEMM_PP_FRAG_FIRST
+#define GEMM_PP_FRAG_FIRST 1  // ping-pong mem phase: fragment reads before the copies
+#endif
+#ifndef GEMM_PP_PRIO
+#define GEMM_PP_PRIO 0  // raise the wave priority during the ping-pong compute phase
+#endif
+#ifndef GEMM_PP_BAND
+#define GEMM_PP_BAND 4  // m-tiles per band of the ping-pong kernel's tile order
+#endif
 #ifndef GEMM_BM
 #define GEMM_BM 256
 #endif
@@ -521,6 +536,451 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
   }
 }
 
+// ---------------------------------------------------------------- ping-pong kernel
+// Records of the ping-pong kernel: group-major, rec4[group * n + row] = S | B << 16 (the fp16 pair
+// of the four-wave kernel's records), so that the records of one group for 32 consecutive rows are
+// 128 contiguous bytes.
+// One workgroup per 64 weight rows: each wave finds the power of two of 16 rows, then all threads
+// write the records group by group (64 rows, 256 contiguous bytes, per group).
+template <typename PT>
+__device__ __forceinline__ void wprep_pp_block(int64_t blk, const uint16_t* __restrict__ scales,
+                                               const uint16_t* __restrict__ biases, int64_t N, int groups,
+                                               uint32_t* __restrict__ rec4, float* __restrict__ wsc) {
+  // One workgroup per 32 weight rows: the rows' (scale, bias) bit pairs are read into LDS, eight
+  // threads per row, while the row's power of two is found; then the records are written group by
+  // group (32 rows, 128 contiguous bytes, per group).
+  extern __shared__ uint32_t s_pair[];  // [32][groups + 1]
+  __shared__ int s_v[32];
+  const int tid = threadIdx.x;
+  const int64_t n0 = blk * 32;
+  const int pitch = groups + 1;
+  {
+    // eight threads per row, every load of the row in flight at once
+    const int r = tid >> 3, part = tid & 7;
+    const int64_t n = n0 + r;
+    float smax = 0.0f, bmax = 0.0f;
+    if (n < N) {
+      const uint16_t* sr = scales + n * groups;
+      const uint16_t* br = biases + n * groups;
+      for (int g = part; g < groups; g += 8) {
+        const uint32_t sbits = sr[g], bbits = br[g];
+        s_pair[r * pitch + g] = sbits | (bbits << 16);
+        smax = fmaxf(smax, fabsf(param_to_f32<PT>(sbits)));
+        bmax = fmaxf(bmax, fabsf(param_to_f32<PT>(bbits)));
+      }
+    }
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) {
+      smax = fmaxf(smax, __shfl_xor(smax, off));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, off));
+    }
+    // the same power of two as the four-wave kernel's records (S and B exact fp16 values)
+    int v = -126;
+    if (smax > 0.0f) {
+      int e;
+      (void)__builtin_frexpf(smax, &e);
+      v = max(v, e + 9);
+    }
+    if (bmax > 0.0f) {
+      int e;
+      (void)__builtin_frexpf(bmax, &e);
+      v = max(v, e - 15);
+    }
+    if (smax == 0.0f && bmax == 0.0f) v = 0;
+    v = min(v, 127);
+    if (part == 0 && n < N) {
+      s_v[r] = v;
+      wsc[n] = __builtin_ldexpf(1.0f, v);
+    }
+  }
+  __syncthreads();
+  const int r = tid & 31;
+  const int64_t n = n0 + r;
+  if (n >= N) return;
+  const int v = s_v[r];
+  for (int g = tid >> 5; g < groups; g += 8) {
+    const uint32_t pr = s_pair[r * pitch + g];
+    const float sv = param_to_f32<PT>(pr & 0xffffu), bv = param_to_f32<PT>(pr >> 16);
+    const uint32_t S = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(sv, 24 - v));
+    const uint32_t B = __builtin_bit_cast(uint16_t, (_Float16)__builtin_ldexpf(bv, -v));
+    rec4[(int64_t)g * N + n] = S | (B << 16);
+  }
+}
+
+// One or more weights that share x (up to four: the projections a layer feeds from one input),
+// their 256-row n-tiles numbered one after another.
+struct PPWeight {
+  const uint32_t* packed;
+  const uint32_t* rec4;
+  const float* wsc;
+  const uint16_t* layer_bias;
+  void* y;
+  int64_t n;
+  int64_t tile0;  // first n-tile of this weight in the launch
+};
+struct PPArgs {
+  const uint16_t* x16;
+  const float* xsc;
+  int64_t M, Kp, K;
+  int groups, lb_bf16, ydt, nw;
+  PPWeight w[4];
+};
+struct PPPrepW {
+  const uint16_t* scales;
+  const uint16_t* biases;
+  uint32_t* rec4;
+  float* wsc;
+  int64_t n;
+  int64_t blk0;  // first workgroup of this weight's records
+};
+struct PPPrep {
+  const uint16_t* x;
+  uint16_t* x16;
+  float* xsc;
+  int64_t M, K, Kp, wblocks;
+  int groups, nw;
+  PPPrepW w[4];
+};
+// The x pre-pass (workgroups 0 .. M-1) and the record pre-pass of every weight in one launch.
+template <typename XT, typename PT, int BITS>
+__global__ __launch_bounds__(256) void prep_pp_kernel(const PPPrep p) {
+  // the weights' record blocks first (workgroups 0 .. wblocks-1), then one workgroup per x row
+  const int64_t b = blockIdx.x;
+  if (b >= p.wblocks) {
+    xprep16_row<XT, BITS>(b - p.wblocks, p.x, p.M, p.K, p.Kp, p.x16, p.xsc);
+    return;
+  }
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if (i < p.nw && b >= p.w[i].blk0) j = i;
+  wprep_pp_block<PT>(b - p.w[j].blk0, p.w[j].scales, p.w[j].biases, p.w[j].n, p.groups, p.w[j].rec4, p.w[j].wsc);
+}
+
+// 512 threads: eight waves, two per SIMD.  Workgroup tile BMT (m) x 256 (n) x BK (k): BK = 128 at
+// 4 bits and 64 at 8 bits, so that a weight row's codes of one k-tile are 64 contiguous bytes (one
+// full request).  Waves 0-3 (group 0) own weight rows 0-127 of the tile, waves 4-7 (group 1) rows
+// 128-255; inside a group, wave (wm, wn) = ((w % 4) / 2, w % 2) owns x rows [BMT/2 wm, +BMT/2) and
+// weight rows [64 wn, +64) of its group's half: (BMT/64) x 2 products of 32x32 per k-step,
+// accumulators private to the wave.
+// The two groups alternate roles every phase (ping-pong): one issues the products of a k-tile with
+// all operands already in registers, while the other issues its half of the HBM->LDS copies of the
+// tile two ahead, reads its fragments of the current tile from LDS and dequantizes them; a barrier
+// ends each phase.  Group 1 trails group 0 by one phase, so each SIMD's matrix core is fed by one of
+// its two waves at a time.  Three LDS stages: tile t in stage t % 3, read in phases 2t (group 0) and
+// 2t+1 (group 1); the copies of tile t+2 go to stage (t+2) % 3 during the mem phases of tile t and
+// their issuing waves wait for them at the end of the mem phases of tile t+1.
+// k-slots: lane half h at k-step t takes the 8-value chunk c = KS h + t (KS = BK / 16 steps), so a
+// lane's codes of a tile are 32 consecutive bytes of its row; x is staged as BK / 64 halves of 64
+// values ([half][row][8 slots]), chunk c in half c / 8, slot c % 8.
+// Records: the stage holds RW words per weight row (the tile's groups, zero past the last one) in
+// blocks of 32 rows ([row / 32][word][row % 32]), copied 4 bytes per lane from rec4.
+template <int BITS, int G, int BMT>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
+  constexpr int BK = BITS == 4 ? 128 : 64;
+  constexpr int KS = BK / 16;                      // k-steps of 16 per tile
+  constexpr int HALVES = BK / 64;                  // 64-value x blocks per tile
+  constexpr int WM = BMT / 2;                      // x rows per wave
+  constexpr int RT = WM / 32;                      // 32-row tiles per wave
+  constexpr int B_ROW = BK * BITS / 8;             // 64 bytes of codes per weight row and tile
+  constexpr int A_HALF = BMT * 128;
+  constexpr int A_BYTES = HALVES * A_HALF;
+  constexpr int B_BYTES = 256 * B_ROW;
+  constexpr int GPK = BK / G > 0 ? BK / G : 1;     // groups a tile touches
+  constexpr int RW = GPK <= 2 ? 2 : 4;             // record words per row in a stage
+  constexpr int R_BYTES = 256 * RW * 4;
+  constexpr int STAGE = A_BYTES + B_BYTES + R_BYTES;
+  constexpr int NA = HALVES * (BMT / 64);          // x copies per thread and mem phase
+  constexpr int NB = 2;                            // code copies
+  constexpr int NR = RW / 2;                       // record copies
+  constexpr int NC = NA + NB + NR;
+  static_assert(B_ROW == 64, "64-byte code rows per tile");
+  // distinct arrays per stage: the compiler then knows that fragment reads of one stage do not
+  // alias the copies in flight into another, and does not wait for those copies before the reads
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+  __shared__ float sXs[BMT];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int wm = w4 >> 1, wn = w4 & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int w4_u = __builtin_amdgcn_readfirstlane(w4);
+  const int grp_u = __builtin_amdgcn_readfirstlane(grp);
+
+  const int64_t M = a.M;
+  const int64_t m_tiles = (M + BMT - 1) / BMT;
+  // Tile order: workgroups are dealt round-robin to the 8 XCDs, so workgroup w runs on XCD w % 8.
+  // Each XCD takes a contiguous range of virtual tile ids, and ids run m-fastest inside bands of
+  // GEMM_PP_BAND m-tiles: the workgroups an XCD runs at once share a few x tiles and a few weight
+  // tiles in its L2 instead of every weight tile.
+  const int64_t T = (int64_t)gridDim.x;
+  int64_t v = blockIdx.x;
+  if (T % 8 == 0) v = (int64_t)(blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
+  int64_t mt, nt;
+  {
+    const int64_t n_tiles = T / m_tiles;
+    const int64_t band = m_tiles % GEMM_PP_BAND == 0 ? GEMM_PP_BAND : 1;
+    const int64_t per_band = band * n_tiles;
+    const int64_t b = v / per_band, r = v % per_band;
+    mt = b * band + r % band;
+    nt = r / band;
+  }
+  int wi = 0;
+#pragma unroll
+  for (int j = 1; j < 4; ++j)
+    if (j < a.nw && nt >= a.w[j].tile0) wi = j;
+  const PPWeight W = a.w[wi];
+  const int64_t m0 = mt * BMT, n0 = (nt - W.tile0) * 256;
+  const int64_t N = W.n;
+  const int64_t KB = a.Kp / 64;                    // 64-value x blocks
+  const int KT = (int)((KB + HALVES - 1) / HALVES);
+  const int64_t row_bytes = a.K * BITS / 8;
+  const int groups = a.groups;
+
+  const uint32_t mk = vconst(BITS == 4 ? 0x000F000Fu : 0x00FF00FFu);
+
+  // ---- this thread's copies (its group's half of every tile)
+  uint32_t a_off[BMT / 64];
+#pragma unroll
+  for (int i = 0; i < BMT / 64; ++i) {
+    const int r = grp * (BMT / 2) + w4 * (BMT / 8) + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ xswz(r);
+    a_off[i] = m0 + r < M ? (uint32_t)(((m0 + r) * 64 + 8 * c) * 2) : kOOB;
+  }
+  uint32_t b_off[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = grp * 128 + w4 * 32 + 16 * i + (lane >> 2);
+    const int c = (lane & 3) ^ bswz<4>(n);
+    b_off[i] = n0 + n < N ? (uint32_t)((n0 + n) * row_bytes + 16 * c) : kOOB;
+  }
+  const int r_row = grp * 128 + 32 * w4 + l32;  // record copies: row, word 2i + h
+  const bool r_ok = n0 + r_row < N;
+  const __amdgpu_buffer_rsrc_t rsA = gemm_rsrc(a.x16, M * a.Kp * 2);
+  const __amdgpu_buffer_rsrc_t rsB = gemm_rsrc(W.packed, N * row_bytes);
+  const __amdgpu_buffer_rsrc_t rsR = gemm_rsrc(W.rec4, N * (int64_t)groups * 4);
+  // copy number c (0 .. NC-1) of this thread's share of tile kt: x blocks, then codes, then records
+  auto copy_one = [&](int kt, uint8_t* stage, int c) __attribute__((always_inline)) {
+    if (c < NA) {
+      const int j = c / (BMT / 64), i = c % (BMT / 64);
+      const int64_t kb = (int64_t)kt * HALVES + j;
+      copy_to_lds<16>(rsA, kb < KB ? a_off[i] : kOOB, (uint32_t)(kb < KB ? kb * M * 128 : 0),
+                      stage + j * A_HALF + (grp_u * (BMT / 2) + w4_u * (BMT / 8) + 8 * i) * 128);
+    } else if (c < NA + NB) {
+      const int i = c - NA;
+      copy_to_lds<16>(rsB, b_off[i], (uint32_t)((int64_t)kt * BK * BITS / 8),
+                      stage + A_BYTES + (grp_u * 128 + w4_u * 32 + 16 * i) * B_ROW);
+    } else {
+      const int i = c - NA - NB;
+      const int gk0 = (int)((int64_t)kt * BK / G);
+      const int w = 2 * i + h;
+      const bool ok = r_ok && w < GPK && gk0 + w < groups;
+      const uint32_t off = ok ? (uint32_t)((((int64_t)(gk0 + w)) * N + n0 + r_row) * 4) : kOOB;
+      copy_to_lds<4>(rsR, off, 0u,
+                     stage + A_BYTES + B_BYTES + (((grp_u * 128 + 32 * w4_u) / 32) * RW + 2 * i) * 128);
+    }
+  };
+  auto copy_half = [&](int kt, uint8_t* stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < HALVES; ++j) {
+      const int64_t kb = (int64_t)kt * HALVES + j;
+#pragma unroll
+      for (int i = 0; i < BMT / 64; ++i)
+        copy_to_lds<16>(rsA, kb < KB ? a_off[i] : kOOB, (uint32_t)(kb < KB ? kb * M * 128 : 0),
+                        stage + j * A_HALF + (grp_u * (BMT / 2) + w4_u * (BMT / 8) + 8 * i) * 128);
+    }
+    const int64_t k0 = (int64_t)kt * BK;
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      copy_to_lds<16>(rsB, b_off[i], (uint32_t)(k0 * BITS / 8),
+                      stage + A_BYTES + (grp_u * 128 + w4_u * 32 + 16 * i) * B_ROW);
+    const int gk0 = (int)(k0 / G);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int w = 2 * i + h;
+      const bool ok = r_ok && w < GPK && gk0 + w < groups;
+      const uint32_t off = ok ? (uint32_t)((((int64_t)(gk0 + w)) * N + n0 + r_row) * 4) : kOOB;
+      copy_to_lds<4>(rsR, off, 0u,
+                     stage + A_BYTES + B_BYTES + (((grp_u * 128 + 32 * w4_u) / 32) * RW + 2 * i) * 128);
+    }
+  };
+
+  f32x16_t acc[RT][2];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // ---- fragments of one k-tile, read during the mem phase: x chunks (RT row-tiles x KS k-steps),
+  // the code words and the group records of the wave's 2 col-tiles.  The codes are dequantized
+  // during the compute phase, one k-step ahead of the products that take them.
+  u32x4_t fa[RT][KS];
+  uint32_t cw[2][8];
+  uint32_t sb[2][GPK > 2 ? 2 : 1];
+  auto mem_frag = [&](const uint8_t* stage) __attribute__((always_inline)) {
+    const uint8_t* sA = stage;
+    const uint8_t* sB = stage + A_BYTES;
+    const uint32_t* sR = (const uint32_t*)(stage + A_BYTES + B_BYTES);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const int n = grp * 128 + wn * 64 + ct * 32 + l32;
+      const uint8_t* row = sB + n * B_ROW;
+      const int sw = bswz<4>(n);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32x4_t v = *(const u32x4_t*)(row + ((2 * h + q) ^ sw) * 16);
+        cw[ct][4 * q + 0] = v[0];
+        cw[ct][4 * q + 1] = v[1];
+        cw[ct][4 * q + 2] = v[2];
+        cw[ct][4 * q + 3] = v[3];
+      }
+      // the group word of the lane's chunks: value offset 8 (KS h + t) of the tile
+      const uint32_t* rr = sR + ((n >> 5) * RW) * 32 + l32;
+      if constexpr (GPK > 2) {  // 4-bit, groups of 32: two groups per lane half
+        sb[ct][0] = rr[(2 * h) * 32];
+        sb[ct][1] = rr[(2 * h + 1) * 32];
+      } else if constexpr (GPK == 2) {
+        sb[ct][0] = rr[(8 * KS * h / G) * 32];
+      } else {
+        sb[ct][0] = rr[0];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int r = wm * WM + rt * 32 + l32;
+        const int c = KS * h + t;
+        const int slot = c & 7;
+        const uint8_t* half = sA + (c >> 3) * A_HALF;
+        fa[rt][t] = *(const u32x4_t*)(half + (r * 8 + (slot ^ xswz(r))) * 16);
+      }
+  };
+  auto dequant = [&](int t, u32x4_t* bq) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint32_t word = GPK > 2 ? sb[ct][t >= KS / 2 ? 1 : 0] : sb[ct][0];
+      const f16x2_t sbv = __builtin_bit_cast(f16x2_t, word);
+      uint32_t r[4];
+      Deq<BITS>::runp(&cw[ct][t * (BITS / 4)], r, f16x2_t{sbv[0], sbv[0]}, f16x2_t{sbv[1], sbv[1]}, mk);
+      bq[ct] = u32x4_t{r[0], r[1], r[2], r[3]};
+    }
+  };
+  // The products of the k-tile; the codes of k-step t+1 are dequantized between the products of
+  // step t (one product, then a few vector instructions).
+  // With copy_kt >= 0 the copies of tile copy_kt into copy_stage are spread over the products, one
+  // after each k-step's products, so that the copy stream is issued evenly over the whole k-tile.
+  auto compute = [&](int copy_kt, uint8_t* copy_stage) __attribute__((always_inline)) {
+    u32x4_t bcur[2], bnext[2];
+    dequant(0, bcur);
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      if (t + 1 < KS) dequant(t + 1, bnext);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma16(fa[rt][t], bcur[ct], acc[rt][ct]);
+      constexpr int per_step = (NC + KS - 1) / KS;
+#pragma unroll
+      for (int c = t * per_step; c < (t + 1) * per_step && c < NC; ++c)
+        if (copy_kt >= 0) copy_one(copy_kt, copy_stage, c);
+      if (t + 1 < KS) {
+#pragma unroll
+        for (int i = 0; i < 2 * RT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+          __builtin_amdgcn_sched_group_barrier(0x002, GEMM_PP_INTERLEAVE, 0);  // vector ALU
+        }
+        if (copy_kt >= 0 && t * per_step < NC) __builtin_amdgcn_sched_group_barrier(0x020, per_step, 0);  // copies
+      }
+      bcur[0] = bnext[0];
+      bcur[1] = bnext[1];
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // One k-tile: mem phase (the copies of tile t+2 into the stage tile t-1 freed, then tile t's
+  // fragments; at its end this wave's copies of tile t+1 must have landed), barrier, compute phase
+  // (products only), barrier.
+  auto step = [&](int t, const uint8_t* cur, uint8_t* free_stage) __attribute__((always_inline)) {
+    if (GEMM_PP_COPY_IN_COMPUTE) {
+      // mem phase: fragments only; this wave's copies (issued during its previous compute phase)
+      // must have landed before the barrier.  Compute phase: the products, with the copies of tile
+      // t+2 spread among them.
+      mem_frag(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();
+      barrier();
+      if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(1);
+      compute(t + 2 < KT ? t + 2 : -1, free_stage);
+      if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+      barrier();
+      return;
+    }
+    if (GEMM_PP_FRAG_FIRST) {
+      mem_frag(cur);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 2 < KT) copy_half(t + 2, free_stage);
+    } else {
+      if (t + 2 < KT) copy_half(t + 2, free_stage);
+      __builtin_amdgcn_sched_barrier(0);
+      mem_frag(cur);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 2 < KT)
+      wait_vmcnt_lgkm0<NC>();
+    else
+      wait_vmcnt_lgkm0<0>();
+    barrier();
+    if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(1);
+    compute(-1, free_stage);
+    if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+    barrier();
+  };
+
+  for (int i = tid; i < BMT; i += 512) sXs[i] = m0 + i < M ? a.xsc[m0 + i] : 0.0f;
+  copy_half(0, st0);
+  if (KT > 1) copy_half(1, st1);
+  wait_vmcnt<0>();
+  barrier();                  // tiles 0 and 1 are in LDS
+  if (grp_u == 1) barrier();  // group 1 trails group 0 by one phase
+  // tile t lives in stage t % 3
+  for (int t = 0; t < KT; t += 3) {
+    step(t, st0, st2);
+    if (t + 1 < KT) step(t + 1, st1, st0);
+    if (t + 2 < KT) step(t + 2, st2, st1);
+  }
+  if (grp_u == 0) barrier();  // the same number of barriers on every wave
+
+  // Epilogue: lane holds column l32 of each 32x32 tile, rows 8*(r/4) + 4*h + (r%4).
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int64_t col = n0 + grp * 128 + wn * 64 + ct * 32 + l32;
+    if (col >= N) continue;
+    const float cs = W.wsc[col];
+    const float add = W.layer_bias ? (a.lb_bf16 ? bf16_bits_to_f32(W.layer_bias[col]) : f16_bits_to_f32(W.layer_bias[col]))
+                                   : 0.0f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + rt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t row = m0 + lr;
+        if (row >= M) continue;
+        store_out(W.y, row * N + col, acc[rt][ct][r] * (sXs[lr] * cs) + add, a.ydt);
+      }
+  }
+}
+
 // Sum of the k-split partial products, plus the layer bias, rounded once to y's dtype.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int splits, int64_t MN,
                                                             int64_t N, const uint16_t* __restrict__ layer_bias,
@@ -568,10 +1028,98 @@ hipError_t launch_main(const uint16_t* x16, const float* xsc, int64_t m, int64_t
   return hipGetLastError();
 }
 
+#ifndef GEMM_PP
+#define GEMM_PP 1
+#endif
+#ifndef GEMM_PP_MIN_TILES
+#define GEMM_PP_MIN_TILES 128  // ping-pong kernel when its 128 x 256 tiles are at least this many
+#endif
+// One weight of a launch over weights that share x.
+struct GemmW {
+  const uint32_t* packed;
+  const void* scales;
+  const void* biases;
+  const void* layer_bias;
+  void* y;
+  int64_t n;
+};
+// Workspace of a launch over weights sharing x: the fp16 copy of x and its row factors, then per
+// weight the records (n * k/g words; the four-wave kernel's pairs take twice that) and row factors.
+size_t ws_x_bytes(int64_t m, int64_t k) { return pad256((size_t)(m * kpad(k)) * 2u) + pad256((size_t)m * 4u); }
+size_t ws_w_bytes(int64_t n, int64_t k, int g) { return pad256((size_t)(n * (k / g)) * 8u) + pad256((size_t)n * 4u); }
+
+inline int64_t pp_tiles(int64_t m, const GemmW* w, int nw) {
+  int64_t nt = 0;
+  for (int j = 0; j < nw; ++j) nt += (w[j].n + 255) / 256;
+  return (m + 127) / 128 * nt;
+}
+// (the record pre-pass stages 32 rows of k/g parameter pairs in at most 64 KiB of LDS)
+inline bool pp_eligible(int64_t m, int64_t k, int g, const GemmW* w, int nw) {
+  return GEMM_PP && 32 * (k / g + 1) * 4 <= 65536 && pp_tiles(m, w, nw) >= GEMM_PP_MIN_TILES;
+}
+
+// The ping-pong path over nw <= 4 weights sharing x: one pre-pass launch (x and every weight's
+// records), one product launch.
+template <int BITS, typename XT, typename PT>
+hipError_t launch_pp(const void* x, int64_t m, int64_t k, const GemmW* w, int nw, int g, int ydt, void* ws,
+                     hipStream_t s) {
+  const int64_t kp = kpad(k);
+  const int groups = (int)(k / g);
+  uint8_t* p = (uint8_t*)ws;
+  uint16_t* x16 = (uint16_t*)p;
+  float* xsc = (float*)(p + pad256((size_t)(m * kp) * 2u));
+  p += ws_x_bytes(m, k);
+  PPPrep pr{};
+  pr.x = (const uint16_t*)x;
+  pr.x16 = x16;
+  pr.xsc = xsc;
+  pr.M = m;
+  pr.K = k;
+  pr.Kp = kp;
+  pr.groups = groups;
+  pr.nw = nw;
+  PPArgs pa{};
+  pa.x16 = x16;
+  pa.xsc = xsc;
+  pa.M = m;
+  pa.Kp = kp;
+  pa.K = k;
+  pa.groups = groups;
+  pa.lb_bf16 = std::is_same<XT, BF16>::value ? 1 : 0;
+  pa.ydt = ydt;
+  pa.nw = nw;
+  int64_t blk = 0, nt = 0;
+  for (int j = 0; j < nw; ++j) {
+    uint32_t* rec4 = (uint32_t*)p;
+    float* wsc = (float*)(p + pad256((size_t)(w[j].n * groups) * 8u));
+    p += ws_w_bytes(w[j].n, k, g);
+    pr.w[j] = PPPrepW{(const uint16_t*)w[j].scales, (const uint16_t*)w[j].biases, rec4, wsc, w[j].n, blk};
+    blk += (w[j].n + 31) / 32;
+    pa.w[j] = PPWeight{w[j].packed, rec4, wsc, (const uint16_t*)w[j].layer_bias, w[j].y, w[j].n, nt};
+    nt += (w[j].n + 255) / 256;
+  }
+  pr.wblocks = blk;
+  prep_pp_kernel<XT, PT, BITS><<<(unsigned)(blk + m), 256, (size_t)32 * (groups + 1) * 4, s>>>(pr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((m + 127) / 128 * nt);
+  if (g == 32)
+    gemm_pp_kernel<BITS, 32, 128><<<grid, 512, 0, s>>>(pa);
+  else if (g == 64)
+    gemm_pp_kernel<BITS, 64, 128><<<grid, 512, 0, s>>>(pa);
+  else
+    gemm_pp_kernel<BITS, 128, 128><<<grid, 512, 0, s>>>(pa);
+  return hipGetLastError();
+}
+
 template <int BITS, typename XT, typename PT>
 hipError_t launch_t(const void* x, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
                     const void* biases, int64_t n, int g, const void* layer_bias, void* y, int ydt, void* ws,
                     hipStream_t s) {
+  {
+    const GemmW w1{packed, scales, biases, layer_bias, y, n};
+    if (pp_eligible(m, k, g, &w1, 1)) return launch_pp<BITS, XT, PT>(x, m, k, &w1, 1, g, ydt, ws, s);
+  }
   const int64_t kp = kpad(k);
   const int groups = (int)(k / g);
   const int splits = gemm_splits(m, n, k);
@@ -634,6 +1182,58 @@ size_t gemm_base_bytes(int64_t m, int64_t n, int64_t k, int g) {
 // The regions above, then (bitstream widths) the codes as bytes, n * k.
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g) {
   return gemm_base_bytes(m, n, k, g) + (is_stream_bits(bits) ? pad256((size_t)(n * k)) : 0u);
+}
+
+hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,
+                       const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,
+                       int ydt, void* ws, hipStream_t s);
+
+// Weights that share x: one pre-pass and one ping-pong launch over all of them when the shape
+// suits that kernel (4- and 8-bit codes, enough tiles), else one qlinear_gemm launch sequence per
+// weight.  Either way each weight's result is the one its own qlinear_gemm call gives when that
+// call takes the ping-pong kernel (the tiles and their sums do not depend on the other weights).
+bool gemm_grouped_pp(int64_t m, int64_t k, const GemmWeight* w, int count, int bits, int g) {
+  if (bits != 4 && bits != 8) return false;
+  GemmW ww[4];
+  for (int j = 0; j < count; ++j) ww[j] = GemmW{w[j].packed, w[j].scales, w[j].biases, w[j].layer_bias, w[j].y, w[j].n};
+  return pp_eligible(m, k, g, ww, count);
+}
+
+size_t gemm_grouped_workspace_bytes(int64_t m, int64_t k, const GemmWeight* w, int count, int bits, int g) {
+  size_t pp = ws_x_bytes(m, k), single = 0;
+  for (int j = 0; j < count; ++j) {
+    pp += ws_w_bytes(w[j].n, k, g);
+    single = std::max(single, gemm_workspace_bytes(m, w[j].n, k, bits, g));
+  }
+  return gemm_grouped_pp(m, k, w, count, bits, g) ? pp : single;
+}
+
+hipError_t launch_gemm_grouped(const void* x, int xdt, int64_t m, int64_t k, const GemmWeight* w, int count, int pdt,
+                               int bits, int g, int ydt, void* ws, hipStream_t s) {
+  if (!gemm_grouped_pp(m, k, w, count, bits, g)) {
+    for (int j = 0; j < count; ++j) {
+      if (w[j].n == 0) continue;
+      const hipError_t e = launch_gemm(x, xdt, m, k, w[j].packed, w[j].scales, w[j].biases, pdt, w[j].n, bits, g,
+                                       w[j].layer_bias, w[j].y, ydt, ws, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GemmW ww[4];
+  int nw = 0;
+  for (int j = 0; j < count; ++j)
+    if (w[j].n > 0) ww[nw++] = GemmW{w[j].packed, w[j].scales, w[j].biases, w[j].layer_bias, w[j].y, w[j].n};
+  const bool xb = xdt == DT_BF16, pb = pdt == DT_BF16;
+  if (bits == 4) {
+    if (xb && pb) return launch_pp<4, BF16, BF16>(x, m, k, ww, nw, g, ydt, ws, s);
+    if (xb) return launch_pp<4, BF16, F16>(x, m, k, ww, nw, g, ydt, ws, s);
+    if (pb) return launch_pp<4, F16, BF16>(x, m, k, ww, nw, g, ydt, ws, s);
+    return launch_pp<4, F16, F16>(x, m, k, ww, nw, g, ydt, ws, s);
+  }
+  if (xb && pb) return launch_pp<8, BF16, BF16>(x, m, k, ww, nw, g, ydt, ws, s);
+  if (xb) return launch_pp<8, BF16, F16>(x, m, k, ww, nw, g, ydt, ws, s);
+  if (pb) return launch_pp<8, F16, BF16>(x, m, k, ww, nw, g, ydt, ws, s);
+  return launch_pp<8, F16, F16>(x, m, k, ww, nw, g, ydt, ws, s);
 }
 
 hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint32_t* packed, const void* scales,

@@ -199,6 +199,18 @@ hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint3
                        const void* biases, int pdt, int64_t n, int bits, int g, const void* layer_bias, void* y,
                        int ydt, void* ws, hipStream_t s);
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits, int g);
+// One weight of a grouped GEMM (mirrors ql_gemm_weight).
+struct GemmWeight {
+  const uint32_t* packed;
+  const void* scales;
+  const void* biases;
+  const void* layer_bias;
+  void* y;
+  int64_t n;
+};
+size_t gemm_grouped_workspace_bytes(int64_t m, int64_t k, const GemmWeight* w, int count, int bits, int g);
+hipError_t launch_gemm_grouped(const void* x, int xdt, int64_t m, int64_t k, const GemmWeight* w, int count, int pdt,
+                               int bits, int g, int ydt, void* ws, hipStream_t s);
 
 // Affine widths whose rows are read as a bitstream of 32-code chunks (BITS words each) rather
 // than by whole codes per word: 2, 3, 5 and 6 bits.

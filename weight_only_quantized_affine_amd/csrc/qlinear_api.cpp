@@ -298,6 +298,60 @@ ql_status qlinear_gemm(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
                   fn);
 }
 
+size_t qlinear_gemm_grouped_workspace_size(int64_t m, int64_t k, const ql_gemm_weight* weights, int count, int bits,
+                                           int group_size) {
+  if (m <= 0 || k <= 0 || count <= 0 || count > 4 || weights == nullptr || group_size <= 0 || bits <= 0) return 0;
+  ql::GemmWeight w[4];
+  for (int j = 0; j < count; ++j)
+    w[j] = ql::GemmWeight{weights[j].packed, weights[j].scales, weights[j].biases, weights[j].layer_bias, weights[j].y,
+                          weights[j].n < 0 ? 0 : weights[j].n};
+  return ql::gemm_grouped_workspace_bytes(m, k, w, count, bits, group_size);
+}
+
+ql_status qlinear_gemm_grouped(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, const ql_gemm_weight* weights,
+                               int count, ql_dtype param_dtype, int bits, int group_size, ql_dtype y_dtype,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "qlinear_gemm_grouped";
+  CHECK(count >= 0 && count <= 4, QL_ERR_SHAPE, "%s: count=%d must be in [0, 4]", fn, count);
+  if (count == 0) return ok();
+  CHECK(weights != nullptr, QL_ERR_NULL, "%s: weights must not be NULL", fn);
+  ql::GemmWeight w[4];
+  bool any = false;
+  for (int j = 0; j < count; ++j) {
+    const ql_gemm_weight& q = weights[j];
+    char name[64];
+    snprintf(name, sizeof(name), "%s: weight %d", fn, j);
+    ql_status st = check_product(name, x, x_dtype, m, k, q.packed, q.scales, q.biases, param_dtype, q.n, bits,
+                                 group_size, q.layer_bias, q.y, y_dtype);
+    if (st != QL_OK) return st;
+    CHECK(q.n * (k * bits / 8) < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+          "%s: weight %d's packed words must be smaller than 2 GiB", fn, j);
+    CHECK(!ql::is_stream_bits(bits) || q.n * k < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+          "%s: at %d bits the codes of weight %d as bytes (n * k) must be smaller than 2 GiB", fn, bits, j);
+    w[j] = ql::GemmWeight{q.packed, q.scales, q.biases, q.layer_bias, q.y, q.n};
+    any = any || q.n > 0;
+  }
+  if (m == 0 || !any) return ok();
+  if (k == 0) {  // no codes: each output is the layer bias (or zeros), as qlinear_gemm writes it
+    for (int j = 0; j < count; ++j) {
+      const ql_status st = qlinear_gemm(x, x_dtype, m, k, w[j].packed, w[j].scales, w[j].biases, param_dtype, w[j].n,
+                                        bits, group_size, w[j].layer_bias, w[j].y, y_dtype, nullptr, 0, stream);
+      if (st != QL_OK) return st;
+    }
+    return ok();
+  }
+  CHECK(m * ((k + 63) / 64 * 64) * 2 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
+        "%s: x (%lld x %lld) must be smaller than 2 GiB", fn, (long long)m, (long long)k);
+  const size_t need = qlinear_gemm_grouped_workspace_size(m, k, weights, count, bits, group_size);
+  CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, need);
+  CHECK(ws_bytes >= need, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn, ws_bytes,
+        need);
+  CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  return launched(ql::launch_gemm_grouped(x, dt(x_dtype), m, k, w, count, dt(param_dtype), bits, group_size,
+                                          dt(y_dtype), workspace, (hipStream_t)stream),
+                  fn);
+}
+
 #ifndef GEMV_TILES_BY_SIZE
 #define GEMV_TILES_BY_SIZE 1
 #endif
