@@ -28,9 +28,10 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
 
 // Round fp32 to bfloat16, nearest with ties to even; NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = (u >> 16) | 0x40u;
+  return (u & 0x7fffffffu) > 0x7f800000u ? nan : rne;  // a select, not a branch
 }
 // Round fp32 to binary16 (the hardware conversion rounds to nearest even).
 __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {

@@ -33,6 +33,75 @@ __device__ __forceinline__ f32x4_t mfma16_bf16(const u32x4_t& a, const u32x4_t& 
                                                  0, 0, 0);
 }
 
+// Output block of one chunk: lane holds weight row ncol0 + 16 ct (column j16 of its tile) for
+// positions 4q + r of each m-subtile.  When every y row is 16-byte aligned (N a multiple of 8), each
+// m-subtile goes through this wave's 3 KB of stage 0 (16 positions x 48 columns) so that every lane
+// writes 16 contiguous bytes of one y row (y 16-byte aligned); otherwise element by element.
+// ESZ = bytes per output element.
+template <int MS, int ESZ>
+__device__ __forceinline__ void mx_store(const f32x4_t (&acc)[XCT][MS], const int32_t* __restrict__ sPos, int rows,
+                                         uint8_t* const* stg, int64_t N, int64_t ncol0, void* __restrict__ y,
+                                         int ydt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j16 = lane & 15, q = lane >> 4;
+  auto bits = [&](float v) __attribute__((always_inline)) {
+    return (uint32_t)(ydt == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
+  };
+  if (N % 8 == 0 && ((uintptr_t)y & 15) == 0) {
+    uint8_t* wbuf = stg[0] + wave * 3072;
+    constexpr int rb = 48 * ESZ;          // bytes of a staged row
+    constexpr int nch = 16 * rb / 16;     // 16-byte chunks of a block: 96 or 192
+    const int64_t col0 = ncol0 - j16;     // the wave's first column
+#pragma unroll
+    for (int rt = 0; rt < MS; ++rt) {
+#pragma unroll
+      for (int ct = 0; ct < XCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint8_t* dst = wbuf + (4 * q + r) * rb + (16 * ct + j16) * ESZ;
+          if constexpr (ESZ == 4)
+            *(float*)dst = acc[ct][rt][r];
+          else
+            *(uint16_t*)dst = (uint16_t)bits(acc[ct][rt][r]);
+        }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS for every lane
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i0 = 0; i0 < nch; i0 += 64) {
+        const int i = i0 + lane;
+        const int row = i / (rb / 16), c = i - row * (rb / 16);
+        const int rr = rt * 16 + row;
+        const int64_t col = col0 + c * (16 / ESZ);
+        if (i < nch && rr < rows && col < N)
+          *(u32x4_t*)((uint8_t*)y + ((int64_t)sPos[rr] * N + col) * ESZ) = *(const u32x4_t*)(wbuf + i * 16);
+      }
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next block is written
+      asm volatile("" ::: "memory");
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < XCT; ++ct) {
+      const int64_t ncol = ncol0 + 16 * ct;
+      if (ncol >= N) continue;
+#pragma unroll
+      for (int rt = 0; rt < MS; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = rt * 16 + 4 * q + r;
+          if (rr < rows) {
+            uint8_t* p = (uint8_t*)y + ((int64_t)sPos[rr] * N + ncol) * ESZ;
+            if constexpr (ESZ == 4)
+              *(float*)p = acc[ct][rt][r];
+            else
+              *(uint16_t*)p = (uint16_t)bits(acc[ct][rt][r]);
+          }
+        }
+    }
+  }
+}
+
 // x stage: row r holds 16 chunks of 8 values (k-tile 128), chunk c at slot c ^ (r % 16), so that the
 // 16 rows of one fragment read hit 16 distinct bank groups.
 template <int MS, bool SCL_LDS>
@@ -158,57 +227,13 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
   ex_wait_vmcnt<0>();  // no copy may still be writing LDS
   __syncthreads();     // every wave is done with the stages: stage 0 now holds the output blocks
 
-  // store: lane holds weight row ncol0 + 16 ct (column j16 of its tile) for positions 4q + r of
-  // each m-subtile.  When every y row is 16-byte aligned (N a multiple of 8), each m-subtile goes
-  // through this wave's 3 KB of stage 0 (16 positions x 48 columns) so that every lane writes 16
-  // contiguous bytes of one y row (y 16-byte aligned); otherwise element by element.
-  const int esz = ydt == DT_F32 ? 4 : 2;
-  if (N % 8 == 0 && ((uintptr_t)y & 15) == 0) {
-    uint8_t* wbuf = stg[0] + wave * 3072;
-    const int rb = 48 * esz;              // bytes of a staged row
-    const int nch = 16 * rb / 16;         // 16-byte chunks of a block: 96 or 192
-    const int64_t col0 = ncol0 - j16;     // the wave's first column
-#pragma unroll
-    for (int rt = 0; rt < MS; ++rt) {
-#pragma unroll
-      for (int ct = 0; ct < XCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint8_t* dst = wbuf + (4 * q + r) * rb + (16 * ct + j16) * esz;
-          const float v = acc[ct][rt][r];
-          if (esz == 4)
-            *(float*)dst = v;
-          else
-            *(uint16_t*)dst = (uint16_t)(ydt == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
-        }
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS for every lane
-      asm volatile("" ::: "memory");
-      for (int i = lane; i < nch; i += 64) {
-        const int row = i / (rb / 16), c = i - row * (rb / 16);
-        const int rr = rt * 16 + row;
-        const int64_t col = col0 + c * (16 / esz);
-        if (rr < rows && col < N)
-          *(u32x4_t*)((uint8_t*)y + ((int64_t)sPos[rr] * N + col) * esz) = *(const u32x4_t*)(wbuf + i * 16);
-      }
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next block is written
-      asm volatile("" ::: "memory");
-    }
-  } else {
-#pragma unroll
-    for (int ct = 0; ct < XCT; ++ct) {
-      const int64_t ncol = ncol0 + 16 * ct;
-      if (ncol >= N) continue;
-#pragma unroll
-      for (int rt = 0; rt < MS; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rr = rt * 16 + 4 * q + r;
-          if (rr < rows) store_out(y, (int64_t)sPos[rr] * N + ncol, acc[ct][rt][r], ydt);
-        }
-    }
-  }
+  // store: the output dtype is dispatched once, outside the loops
+  if (ydt == DT_F32)
+    mx_store<MS, 4>(acc, sPos, rows, stg, N, ncol0, y, DT_F32);
+  else if (ydt == DT_BF16)
+    mx_store<MS, 2>(acc, sPos, rows, stg, N, ncol0, y, DT_BF16);
+  else
+    mx_store<MS, 2>(acc, sPos, rows, stg, N, ncol0, y, DT_F16);
 }
 
 template <bool SCL_LDS>
