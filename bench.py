@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--legs", default="all",
-                    help="comma-separated legs to run (decode8, decode4m8, prefill, experts, prefill6, decode_bits, "
-                         "quantize, blocks, transcode) or 'all'")
+                    help="comma-separated legs to run (decode8, decode4m8, decode_breakdown, prefill, experts, "
+                         "prefill6, decode_bits, quantize, blocks, transcode) or 'all'")
     ap.add_argument("--no-headline", action="store_true",
                     help="skip the headline decode step (for profiling single legs); prints the legs only")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -284,6 +284,48 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
         }
         del sets_b
         torch.cuda.empty_cache()
+
+    # ---------------- where the decode step's time goes: lm_head alone, the 196 layer projections
+    # alone (one list launch each), and all 197 as separate qlinear_gemv launches in one graph
+    if want("decode_breakdown"):
+        log("leg: decode breakdown")
+        sets_b, wb, io = build_decode(4, 1, 3, 20_000)
+        out = {}
+        for label, pick in (("lm_head_alone", lambda pr: pr[-1:]), ("layers_alone", lambda pr: pr[:-1])):
+            sub = []
+            for probs, _, kw in sets_b:
+                sel = pick(probs)
+                arr = q.qlinear_problem_list(sel)
+                ws = torch.empty(q.qlinear_gemv_batched_workspace_size(arr), dtype=torch.uint8, device=dev)
+                kw2 = dict(kw, workspace=ws)
+                q.qlinear_gemv_batched(arr, upload=True, **kw2)
+                sub.append((sel, arr, kw2))
+            byts = sum(p_["packed"].numel() * 4 + p_["scales"].numel() * 4 for p_ in sub[0][0])
+            _, avg = time_decode(sub, 200, 300)
+            out[label] = {"kernel_ms": round(avg, 5), "weight_gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+                          "weights_bytes": byts}
+            del sub
+        # per-projection launches (qlinear_gemv each), 197 per step, captured as one graph
+        torch.cuda.synchronize()
+        gsteps = 20
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(gsteps):
+                probs, _, _ = sets_b[i % len(sets_b)]
+                for p_ in probs:
+                    q.qlinear_gemv(p_["x"], p_["packed"], p_["scales"], p_["biases"], bits=4, group_size=64, y=p_["y"])
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg = e0.elapsed_time(e1) / gsteps
+        out["per_projection_launches_graph"] = {"step_ms": round(avg, 5), "weight_gbs": round(wb / (avg * 1e-3) / 1e9, 1)}
+        del g, sets_b
+        torch.cuda.empty_cache()
+        legs["decode_4bit_breakdown"] = out
 
     # ---------------- prefill GEMM, 9B-class layer at M = 2048: the layer's four inputs, each through
     # one call (q|k|v and gate|up as grouped calls over the weights that read the same x), plus each
