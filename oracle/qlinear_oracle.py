@@ -31,6 +31,9 @@ Readings of points the pages leave open:
 * quantize_q8_0: the NaN scale of a block holding a NaN is the fp16 quiet NaN 0x7E00 (the page
   fixes "a NaN scale", not its bits); a block holding an infinity and no NaN takes +inf (0x7C00).
 * take: positions outside [0, rows) are out of range (negative ones too) and give zero bytes.
+* AWQ lane order [0,2,4,6,1,3,5,7]: read as the columns that the nibbles of a word hold, from
+  the low nibble up (nibble 1 holds column 2), applied to 4-bit qweight and qzeros alike; other
+  widths are plain streams along the outputs.
 
 Float storage types travel as uint16 bit patterns (``'f16'`` or ``'bf16'``); fp32 as numpy
 float32.  All arithmetic below is NumPy on the CPU.
@@ -63,6 +66,10 @@ __all__ = [
     "take",
     "gptq_transcode",
     "gptq_dequant_f64",
+    "AWQ_LANE_ORDER",
+    "awq_codes",
+    "awq_transcode",
+    "awq_dequant_f64",
     "route",
     "apply_experts",
     "rel_l2_per_row",
@@ -287,6 +294,68 @@ def gptq_dequant_f64(qweight, qzeros, scale_bits, bits: int, group_size: int, k:
     sg = np.repeat(s.T, group_size, axis=1)
     zg = np.repeat(zeros.T, group_size, axis=1)
     return sg * (codes - zg)
+
+
+AWQ_LANE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)
+
+
+def _read_stream(words, bits: int, count: int) -> np.ndarray:
+    """The first ``count`` codes of each row's little-endian ``bits``-wide stream (stream bit j is
+    bit j % 32 of word j // 32), for any width 1..8: the words' bits are listed one by one
+    (NumPy's unpackbits, least significant bit first over little-endian bytes) and cut into
+    codes, bit i of a code weighing 2^i."""
+    w = np.ascontiguousarray(np.asarray(words, dtype="<u4"))
+    rows = w.shape[0]
+    flat = np.unpackbits(w.view(np.uint8).reshape(rows, -1), axis=1, bitorder="little")
+    assert flat.shape[1] >= count * bits
+    b = flat[:, : count * bits].reshape(rows, count, bits).astype(np.int64)
+    return (b << np.arange(bits, dtype=np.int64)).sum(axis=2)
+
+
+def awq_codes(words, bits: int, count: int) -> np.ndarray:
+    """Codes of AWQ GEMM rows packed along the outputs, in natural column order: each row is one
+    continuous ``bits``-wide stream; at 4 bits the 8 nibbles of a word hold, from the low nibble
+    up, columns 0, 2, 4, 6, 1, 3, 5, 7 of that word's 8 (GPTQModel wiki "MLX Apple Silicon",
+    ParoQuant: the AWQ lane order; "Packed layouts and exact transcoding", AWQ GEMM row: the 4-bit
+    lane permutation is undone before row packing)."""
+    s = _read_stream(words, bits, count)
+    if bits != 4:
+        return s
+    assert count % 8 == 0
+    out = np.empty_like(s)
+    for slot, col in enumerate(AWQ_LANE_ORDER):
+        out[:, col::8] = s[:, slot::8]
+    return out
+
+
+def awq_transcode(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int, param_dtype: str):
+    """AWQ GEMM -> MLX affine rows (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact
+    transcoding, AWQ GEMM and seven-bit rows; GPTQModel "Packing Formats and Compatibility", AWQ
+    GEMM: qweight [K, N*b/32] codes packed along the outputs, qzeros [G, N*b/32] true zero points
+    packed the same way, scales [G, N] group-major; value scale * (code - zero)).
+
+    Returns (packed [n, k*tb/32], scales [n, G], biases [n, G]) where tb = 8 for 7-bit sources (no
+    7-bit affine rows: the code values are kept in 8-bit words) and tb = bits otherwise, and
+    biases = RNE(-zero * scale) in param_dtype (exact in fp32 before that rounding)."""
+    G = k // group_size
+    qweight = np.asarray(qweight, dtype=np.uint32)
+    qzeros = np.asarray(qzeros, dtype=np.uint32)
+    assert qweight.shape == (k, n * bits // 32) and qzeros.shape == (G, n * bits // 32)
+    tb = 8 if bits == 7 else bits
+    codes = awq_codes(qweight, bits, n)  # [k, n]
+    zeros = awq_codes(qzeros, bits, n)  # [G, n]
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))  # [G, n]
+    b32 = (-(zeros.astype(np.float64)) * s).astype(np.float32)
+    return (pack_codes(codes.T, tb), np.ascontiguousarray(np.asarray(scale_bits, dtype=np.uint16).T),
+            np.ascontiguousarray(to_bits(param_dtype, b32).T))
+
+
+def awq_dequant_f64(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int, param_dtype: str):
+    """AWQ's own reconstruction, scale * (code - zero), exactly in fp64: [n, k] (per output row)."""
+    codes = awq_codes(qweight, bits, n).astype(np.float64)  # [k, n]
+    zeros = awq_codes(qzeros, bits, n).astype(np.float64)  # [G, n]
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))
+    return np.repeat(s.T, group_size, axis=1) * (codes.T - np.repeat(zeros.T, group_size, axis=1))
 
 
 # --------------------------------------------------------------------------------------

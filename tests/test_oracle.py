@@ -80,6 +80,8 @@ def _stream_words_from_digits(codes, bits):
         text, base = "".join(digits[c] for c in reversed(codes)), 1 << bits
     elif bits == 6:  # two octal digits per code
         text, base = "".join(f"{c >> 3}{c & 7}" for c in reversed(codes)), 8
+    elif bits == 7:  # seven binary digits per code
+        text, base = "".join(f"{c:07b}" for c in reversed(codes)), 2
     else:  # bits == 8: two hex digits per code
         text, base = "".join(f"{c:02x}" for c in reversed(codes)), 16
     raw = int(text, base).to_bytes(len(codes) * bits // 8, "little")
@@ -571,3 +573,89 @@ def test_gptq_dequant_is_scale_times_code_minus_zero(bits, pdt, g, v1):
     if v1:
         wrong = O.gptq_dequant_f64(qw.astype(np.uint32), qz.astype(np.uint32), sb, bits, g, k, n, pdt)
         np.testing.assert_allclose(wrong - got, np.repeat(sv.T, g, axis=1))
+
+
+# ---------------------------------------------------------------- AWQ GEMM -> affine transcoder
+# (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact transcoding, AWQ GEMM row, and
+# ParoQuant: the lane order [0,2,4,6,1,3,5,7]; GPTQModel "Packing Formats and Compatibility",
+# AWQ GEMM: qweight [K, N/8], qzeros [G, N/8], scales [G, N])
+
+
+def test_awq_lane_order_hand_words():
+    """A word whose nibble i (from the low nibble up) holds the value i decodes, in natural column
+    order, to the inverse of the page's lane order: column c holds the slot at which c appears in
+    [0,2,4,6,1,3,5,7]."""
+    w = np.array([[0x76543210, 0xFEDCBA98]], dtype=np.uint32)
+    np.testing.assert_array_equal(O.awq_codes(w, 4, 16)[0],
+                                  [0, 4, 1, 5, 2, 6, 3, 7, 8, 12, 9, 13, 10, 14, 11, 15])
+    # a word holding columns 0..7 = 1,2,...,8 in AWQ order, written out nibble by nibble:
+    # slots hold columns 0,2,4,6,1,3,5,7 -> values 1,3,5,7,2,4,6,8 -> 0x86427531
+    np.testing.assert_array_equal(O.awq_codes(np.array([[0x86427531]], dtype=np.uint32), 4, 8)[0],
+                                  [1, 2, 3, 4, 5, 6, 7, 8])
+    # 8-bit rows are plain little-endian byte streams (no permutation); 2-bit likewise
+    np.testing.assert_array_equal(O.awq_codes(np.array([[0x44332211]], dtype=np.uint32), 8, 4)[0],
+                                  [0x11, 0x22, 0x33, 0x44])
+    np.testing.assert_array_equal(O.awq_codes(np.array([[0xE4E4E4E4]], dtype=np.uint32), 2, 16)[0],
+                                  [0, 1, 2, 3] * 4)
+
+
+def _awq_stream_words(natural, bits):
+    """One AWQ row from codes in natural column order: at 4 bits each 8-column block is written in
+    the page's lane order (slot i takes column order[i]), then the row is one little-endian stream
+    built with the digit-string construction."""
+    natural = [int(c) for c in natural]
+    if bits == 4:
+        order = (0, 2, 4, 6, 1, 3, 5, 7)
+        natural = [natural[8 * (i // 8) + order[i % 8]] for i in range(len(natural))]
+    return _stream_words_from_digits(natural, bits)
+
+
+def _awq_case(seed, k, n, bits, g, pow2_scales=False):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 1 << bits, size=(k, n))  # [in, out]
+    zeros = rng.integers(0, 1 << bits, size=(k // g, n))
+    qweight = np.stack([_awq_stream_words(codes[r], bits) for r in range(k)])
+    qzeros = np.stack([_awq_stream_words(zeros[r], bits) for r in range(k // g)])
+    if pow2_scales:
+        s = np.ldexp(1.0, rng.integers(-12, -2, size=(k // g, n))).astype(np.float32)
+    else:
+        s = (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32)
+    return codes, zeros, qweight.astype(np.uint32), qzeros.astype(np.uint32), s
+
+
+@pytest.mark.parametrize("bits,pdt,g", [(4, "f16", 64), (3, "bf16", 32), (2, "f16", 128), (5, "f16", 64),
+                                        (6, "bf16", 64), (7, "f16", 32), (8, "bf16", 64)])
+def test_awq_transcode_reconstructs_scale_times_code_minus_zero(bits, pdt, g):
+    k, n = 256, 64
+    codes, zeros, qw, qz, s = _awq_case(90 + bits, k, n, bits, g)
+    sb = O.to_bits(pdt, s)
+    pk, so, bo = O.awq_transcode(qw, qz, sb, bits, g, k, n, pdt)
+    tb = 8 if bits == 7 else bits
+    assert pk.shape == (n, k * tb // 32)
+    # the affine rows hold the drawn codes (a 7-bit source keeps its values in 8-bit words)
+    np.testing.assert_array_equal(O.unpack_codes(pk, tb, k), codes.T)
+    np.testing.assert_array_equal(so, sb.T)
+    # AWQ's value scale * (code - zero), element by element from the drawn numbers, against the
+    # affine value code * scale + bias; the only rounding is the bias's, to the parameter dtype
+    deq = O.affine_dequant_f32(pk, so, bo, tb, g, pdt, k).astype(np.float64)
+    sv = O.bits_to_f64(pdt, sb)
+    own = O.awq_dequant_f64(qw, qz, sb, bits, g, k, n, pdt)
+    for j in range(0, n, 5):
+        for i in range(0, k, 3):
+            want = float(sv[i // g, j]) * (int(codes[i, j]) - int(zeros[i // g, j]))
+            assert own[j, i] == want, (j, i)
+            bias_err = abs(float(O.bits_to_f64(pdt, bo[j, i // g])) + float(zeros[i // g, j]) * float(sv[i // g, j]))
+            assert abs(deq[j, i] - want) <= bias_err + abs(want) * 2.0 ** -23 + 1e-30, (j, i)
+
+
+def test_awq_transcode_exact_with_power_of_two_scales_and_misorder_fails():
+    k, n, g, bits = 128, 32, 32, 4
+    codes, zeros, qw, qz, s = _awq_case(97, k, n, bits, g, pow2_scales=True)
+    sb = O.to_bits("f16", s)
+    pk, so, bo = O.awq_transcode(qw, qz, sb, bits, g, k, n, "f16")
+    deq = O.affine_dequant_f32(pk, so, bo, bits, g, "f16", k).astype(np.float64)
+    want = np.repeat(s.T.astype(np.float64), g, axis=1) * (codes.T - np.repeat(zeros.T, g, axis=1))
+    np.testing.assert_array_equal(deq, want)
+    # reading the 4-bit words as plain streams (the permutation ignored) gives other codes
+    plain = O.pack_codes(O.unpack_codes(qw, 4, n).T, 4)
+    assert not np.array_equal(plain, pk)
