@@ -550,6 +550,35 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
             "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
         del qw, qz, sc
         torch.cuda.empty_cache()
+
+        # AWQ GEMM of the same layer: codes packed along the outputs, transposed code by code
+        log("leg: AWQ transcode")
+        qw = torch.randint(-2**31, 2**31 - 1, (K, N * 4 // 32), generator=gen(62_010), device=dev, dtype=torch.int32)
+        qz = torch.randint(-2**31, 2**31 - 1, (K // 128, N * 4 // 32), generator=gen(62_011), device=dev,
+                           dtype=torch.int32)
+        sc = (torch.rand((K // 128, N), generator=gen(62_012), device=dev) * 0.02 + 1e-3).to(torch.float16)
+        pk_o, so_o, bo_o = q.qlinear_transcode_awq(qw, qz, sc, bits=4, group_size=128)
+        torch.cuda.synchronize()
+        g_tc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_tc):
+            for _ in range(20):
+                q.qlinear_transcode_awq(qw, qz, sc, bits=4, group_size=128, packed=pk_o, scales_out=so_o,
+                                        biases_out=bo_o)
+        g_tc.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g_tc.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg = e0.elapsed_time(e1) / 20
+        del g_tc, pk_o, so_o, bo_o
+        byts = 2 * qw.numel() * 4 + qz.numel() * 4 + sc.numel() * 2 * 3
+        legs["transcode_awq_4096x12288_4bit_g128"] = {
+            "ms": round(avg, 4), "gbs": round(byts / (avg * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * byts / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        del qw, qz, sc
+        torch.cuda.empty_cache()
     return legs
 
 

@@ -114,6 +114,24 @@ ql_status qlinear_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
                                  int v1_zeros, uint32_t* packed, void* scales_out, void* biases_out,
                                  void* stream);
 
+/* AWQ GEMM -> MLX affine rows (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact
+ * transcoding, the AWQ GEMM and seven-bit rows, and ParoQuant for the lane order; GPTQModel
+ * "Packing Formats and Compatibility", AWQ GEMM):
+ *   in:  qweight [k, n*bits/32] uint32 (input row i's codes as one little-endian bits-wide stream
+ *        along the outputs; at 4 bits the nibbles of each word hold, from the low one up, columns
+ *        0, 2, 4, 6, 1, 3, 5, 7 of its 8), qzeros [k/group_size, n*bits/32] (true zero points,
+ *        packed the same way), scales [k/group_size, n] in scale_dtype; the AWQ value is
+ *        scale * (code - zero).
+ *   out: packed [n, k*tb/32] (the affine row streams, tb = 8 for bits = 7 (the code values kept
+ *        in 8-bit rows), tb = bits otherwise), scales_out [n, k/group_size] (transposed),
+ *        biases_out [n, k/group_size] = RNE(-zero * scale) in scale_dtype.
+ * bits in {2, 3, 4, 5, 6, 7, 8}; group_size in {32, 64, 128}; k and n multiples of 32, k a
+ * multiple of group_size (QL_ERR_SHAPE).  Word arrays 4-byte aligned, 16-bit arrays 2-byte
+ * aligned, all device memory; the outputs must not overlap the inputs. */
+ql_status qlinear_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
+                                ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size,
+                                uint32_t* packed, void* scales_out, void* biases_out, void* stream);
+
 /* dequant (Nx_quant Products, dequant): every value of W as a float32 value, rounded once to
  * out_dtype (QL_F32, QL_F16 or QL_BF16).  out is [rows, k].
  *   QL_AFFINE: w0 = packed [rows, k*bits/32], w1 = scales, w2 = biases [rows, k/group_size] in

@@ -223,6 +223,29 @@ def test_transcode_gptq_rejects_bad_arguments(lib):
     assert call(k=0) == QL_OK
 
 
+def test_transcode_awq_rejects_bad_arguments(lib):
+    args = [FAKE, FAKE, FAKE, F16, 256, 64, 4, 64, FAKE, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["qw", "qz", "sc", "sdt", "k", "n", "bits", "g", "pk", "so", "bo", "s"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return lib.qlinear_transcode_awq(*a)
+
+    assert call(bits=1) == QL_ERR_UNSUPPORTED
+    assert call(bits=9) == QL_ERR_UNSUPPORTED
+    assert call(g=16) == QL_ERR_UNSUPPORTED
+    assert call(k=250) == QL_ERR_SHAPE
+    assert call(k=96, g=64) == QL_ERR_SHAPE  # k not a multiple of the group
+    assert call(n=48) == QL_ERR_SHAPE  # n must be a multiple of 32
+    assert call(sdt=F32) == QL_ERR_DTYPE
+    assert call(qz=None) == QL_ERR_NULL
+    assert call(qw=FAKE + 2) == QL_ERR_ALIGN
+    assert call(bo=FAKE + 1) == QL_ERR_ALIGN
+    assert call(n=0) == QL_OK
+
+
 def test_apply_experts_noalloc_rejects_sizes_past_its_scratch(lib):
     # 100,000 positions need 12 bytes each of routing scratch: past the 1 MiB built-in array
     st = lib.qlinear_apply_experts_noalloc(1, FAKE, FAKE, 32, 64, 64, FAKE, 100_000, FAKE, BF16, 1, FAKE, BF16, None)

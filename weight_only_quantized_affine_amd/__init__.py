@@ -26,6 +26,7 @@ __all__ = [
     "qlinear_quantize_q8_0",
     "qlinear_take",
     "qlinear_transcode_gptq",
+    "qlinear_transcode_awq",
     "qlinear_gemv",
     "qlinear_gemm",
     "qlinear_gemm_workspace_size",
@@ -93,6 +94,7 @@ _SIGNATURES = {
     "qlinear_quantize_q8_0": (_INT, [_P, _I64, _I64, _P, _P]),
     "qlinear_take": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "qlinear_transcode_gptq": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P]),
+    "qlinear_transcode_awq": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
     "qlinear_gemm": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P, _SZ, _P]),
@@ -219,6 +221,25 @@ def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: in
     bo = biases_out if biases_out is not None else torch.empty_like(so)
     _check(lib.qlinear_transcode_gptq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits, group_size,
                                       1 if v1_zeros else 0, _ptr(packed), _ptr(so), _ptr(bo), _stream()))
+    return packed, so, bo
+
+
+def qlinear_transcode_awq(qweight, qzeros, scales, *, bits: int, group_size: int, packed=None, scales_out=None,
+                          biases_out=None):
+    """AWQ GEMM (codes and zeros packed along the outputs) -> affine (packed [n, k*tb/32] int32 with
+    tb = 8 for 7-bit sources, else bits; scales and biases [n, k/group_size] in scales' dtype).
+    qweight [k, n*bits/32], qzeros [G, n*bits/32] (int32), scales [G, n]."""
+    torch = _torch()
+    lib = load_library()
+    k, n = qweight.shape[0], scales.shape[1]
+    tb = 8 if bits == 7 else bits
+    if packed is None:
+        packed = torch.empty((n, k * tb // 32), dtype=torch.int32, device=qweight.device)
+    so = scales_out if scales_out is not None else torch.empty((n, scales.shape[0]), dtype=scales.dtype,
+                                                                device=qweight.device)
+    bo = biases_out if biases_out is not None else torch.empty_like(so)
+    _check(lib.qlinear_transcode_awq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits, group_size,
+                                     _ptr(packed), _ptr(so), _ptr(bo), _stream()))
     return packed, so, bo
 
 

@@ -141,6 +141,31 @@ ql_status qlinear_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
                   fn);
 }
 
+ql_status qlinear_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
+                                ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size, uint32_t* packed,
+                                void* scales_out, void* biases_out, void* stream) {
+  const char* fn = "qlinear_transcode_awq";
+  CHECK(k >= 0 && n >= 0, QL_ERR_SHAPE, "%s: k and n must be >= 0", fn);
+  CHECK(bits >= 2 && bits <= 8, QL_ERR_UNSUPPORTED, "%s: bits=%d not supported (AWQ GEMM widths 2 to 8)", fn, bits);
+  CHECK(group_size == 32 || group_size == 64 || group_size == 128, QL_ERR_UNSUPPORTED,
+        "%s: group_size=%d not supported (32, 64 or 128)", fn, group_size);
+  CHECK(k % 32 == 0 && k % group_size == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32 and of group_size", fn,
+        (long long)k);
+  CHECK(n % 32 == 0, QL_ERR_SHAPE, "%s: n=%lld must be a multiple of 32", fn, (long long)n);
+  CHECK(is16(scale_dtype), QL_ERR_DTYPE, "%s: scale_dtype must be QL_F16 or QL_BF16", fn);
+  if (k == 0 || n == 0) return ok();
+  CHECK(qweight && qzeros && scales && packed && scales_out && biases_out, QL_ERR_NULL,
+        "%s: qweight, qzeros, scales, packed, scales_out and biases_out must not be NULL", fn);
+  CHECK(aligned(qweight, 4) && aligned(qzeros, 4) && aligned(packed, 4), QL_ERR_ALIGN,
+        "%s: qweight, qzeros and packed must be 4-byte aligned", fn);
+  CHECK(aligned(scales, 2) && aligned(scales_out, 2) && aligned(biases_out, 2), QL_ERR_ALIGN,
+        "%s: scales, scales_out and biases_out must be 2-byte aligned", fn);
+  CHECK(n * k / 32 * 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: weight too large", fn);
+  return launched(ql::launch_transcode_awq(qweight, qzeros, scales, dt(scale_dtype), k, n, bits, group_size, packed,
+                                           scales_out, biases_out, (hipStream_t)stream),
+                  fn);
+}
+
 ql_status qlinear_take(const int64_t* pos, int64_t n_pos, const void* src, int64_t src_rows, int64_t row_bytes,
                        void* dst, void* stream) {
   const char* fn = "qlinear_take";

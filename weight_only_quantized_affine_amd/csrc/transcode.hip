@@ -6,6 +6,14 @@
 // qweight transposed word for word; scales transpose to [N, G]; the additive bias is
 // -zero * scale, exact in fp32 (zero < 2^8, scale of at most 11 significant bits) and rounded
 // once to the scale dtype.  v1 checkpoints store zero - 1.
+//
+// AWQ GEMM (same pages, AWQ GEMM row and ParoQuant; "Packing Formats and Compatibility", AWQ GEMM)
+// packs the other axis: qweight [K, N*b/32] holds each input row's codes as one b-bit stream
+// along the outputs, qzeros [G, N*b/32] the true zeros the same way, and at 4 bits the nibbles
+// of a word hold, from the low one up, columns 0, 2, 4, 6, 1, 3, 5, 7 of the word's 8.  The
+// affine rows need the codes along the inputs, so the codes themselves are transposed: a
+// workgroup decodes a 128 x 128 tile of codes into LDS (one byte each, the lane order undone)
+// and writes it back as 128 row streams.  A 7-bit source keeps its code values in 8-bit rows.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -33,17 +41,21 @@ __global__ __launch_bounds__(256) void transpose_words_kernel(const uint32_t* __
 }
 
 // One lane per (output n, group g), g fastest: the zero is bits [b n, b n + b) of row g of qzeros.
+// With awq4 the zeros are 4-bit AWQ words: column c of a word's 8 sits in nibble slot
+// (c >> 1) | ((c & 1) << 2), the inverse of the lane order 0, 2, 4, 6, 1, 3, 5, 7.
 template <typename PT>
 __global__ __launch_bounds__(256) void gptq_params_kernel(const uint32_t* __restrict__ qzeros,
                                                           const uint16_t* __restrict__ scales, int64_t n, int groups,
-                                                          int bits, int v1, uint16_t* __restrict__ scales_out,
+                                                          int bits, int v1, int awq4, uint16_t* __restrict__ scales_out,
                                                           uint16_t* __restrict__ biases_out) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n * groups) return;
   const int64_t o = t / groups;
   const int g = (int)(t - o * groups);
   const uint32_t* zrow = qzeros + (int64_t)g * (n * bits / 32);
-  const int64_t pos = o * bits;
+  const int c = (int)(o & 7);
+  const int64_t slot = awq4 ? ((o & ~(int64_t)7) | (c >> 1) | ((c & 1) << 2)) : o;
+  const int64_t pos = slot * bits;
   const int64_t wi = pos >> 5;
   const int sh = (int)(pos & 31);
   uint32_t z = zrow[wi] >> sh;
@@ -63,6 +75,82 @@ __global__ __launch_bounds__(256) void gptq_params_kernel(const uint32_t* __rest
   biases_out[t] = (uint16_t)(pbits ^ 0x8000u);
 }
 
+hipError_t launch_params(const uint32_t* qzeros, const void* scales, int pdt, int64_t n, int groups, int bits, int v1,
+                         int awq4, void* scales_out, void* biases_out, hipStream_t s) {
+  const unsigned nb = (unsigned)((n * groups + 255) / 256);
+  if (pdt == DT_BF16)
+    gptq_params_kernel<BF16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4,
+                                                (uint16_t*)scales_out, (uint16_t*)biases_out);
+  else
+    gptq_params_kernel<F16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4,
+                                               (uint16_t*)scales_out, (uint16_t*)biases_out);
+  return hipGetLastError();
+}
+
+constexpr int AT = 128;       // AWQ code tile: 128 input rows x 128 output columns
+constexpr int AP = AT + 4;    // LDS pitch of a tile row (bytes)
+
+// Tile (k0, n0) of the code matrix [k, n]: source row r's columns n0 .. n0 + 127 are the
+// 4 * SB words from word n0 * SB / 32 of that row (n0 is a multiple of 128, so whole words);
+// target row n0 + c's codes k0 .. k0 + 127 are the 4 * TB words from word k0 * TB / 32 of it.
+// k and n are multiples of 32, so every 32-code block is wholly inside or outside the matrix.
+template <int SB, int TB>
+__global__ __launch_bounds__(256) void awq_codes_kernel(const uint32_t* __restrict__ qweight, int64_t k, int64_t n,
+                                                        uint32_t* __restrict__ packed) {
+  __shared__ uint8_t tile[AT * AP];
+  const int64_t tiles_n = (n + AT - 1) / AT;
+  const int64_t k0 = (int64_t)(blockIdx.x / tiles_n) * AT, n0 = (int64_t)(blockIdx.x % tiles_n) * AT;
+  const int64_t src_words = n * SB / 32, dst_words = k * TB / 32;
+  // 1. decode: item = (tile row r, 32-column block cb); four consecutive lanes read one row's
+  //    4 * SB consecutive words
+  for (int it = threadIdx.x; it < AT * 4; it += 256) {
+    const int r = it >> 2, cb = it & 3;
+    if (k0 + r >= k || n0 + 32 * cb >= n) continue;
+    const uint32_t* src = qweight + (k0 + r) * src_words + (n0 + 32 * cb) * SB / 32;
+    uint32_t w[SB];
+#pragma unroll
+    for (int i = 0; i < SB; ++i) w[i] = src[i];
+    uint8_t* dst = tile + r * AP + 32 * cb;
+#pragma unroll
+    for (int slot = 0; slot < 32; ++slot) {
+      constexpr uint32_t mask = (1u << SB) - 1u;
+      const int pos = slot * SB, wi = pos >> 5, sh = pos & 31;
+      uint32_t v = w[wi] >> sh;
+      if (sh + SB > 32) v |= w[wi + 1] << (32 - sh);
+      // at 4 bits, nibble slot s of a word holds column ((s & 3) << 1) | (s >> 2) of its 8
+      const int col = SB == 4 ? ((slot & ~7) | ((slot & 3) << 1) | ((slot >> 2) & 1)) : slot;
+      dst[col] = (uint8_t)(v & mask);
+    }
+  }
+  __syncthreads();
+  // 2. pack: item = (tile column c, 32-row block kb); four consecutive lanes write one target
+  //    row's 4 * TB consecutive words
+  for (int it = threadIdx.x; it < AT * 4; it += 256) {
+    const int c = it >> 2, kb = it & 3;
+    if (n0 + c >= n || k0 + 32 * kb >= k) continue;
+    uint32_t w[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) w[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t v = tile[(32 * kb + j) * AP + c];
+      const int pos = j * TB, wi = pos >> 5, sh = pos & 31;
+      w[wi] |= v << sh;
+      if (sh + TB > 32) w[wi + 1] |= v >> (32 - sh);
+    }
+    uint32_t* dst = packed + (n0 + c) * dst_words + (k0 + 32 * kb) * TB / 32;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) dst[i] = w[i];
+  }
+}
+
+template <int SB, int TB>
+hipError_t launch_awq_codes(const uint32_t* qweight, int64_t k, int64_t n, uint32_t* packed, int64_t tiles,
+                            hipStream_t s) {
+  awq_codes_kernel<SB, TB><<<(unsigned)tiles, 256, 0, s>>>(qweight, k, n, packed);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
@@ -74,14 +162,26 @@ hipError_t launch_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int groups = (int)(k / g);
-  const unsigned nb = (unsigned)((n * groups + 255) / 256);
-  if (pdt == DT_BF16)
-    gptq_params_kernel<BF16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1,
-                                                (uint16_t*)scales_out, (uint16_t*)biases_out);
-  else
-    gptq_params_kernel<F16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1,
-                                               (uint16_t*)scales_out, (uint16_t*)biases_out);
-  return hipGetLastError();
+  return launch_params(qzeros, scales, pdt, n, groups, bits, v1, 0, scales_out, biases_out, s);
+}
+
+hipError_t launch_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
+                                int64_t k, int64_t n, int bits, int g, uint32_t* packed, void* scales_out,
+                                void* biases_out, hipStream_t s) {
+  const int64_t tiles = ((k + AT - 1) / AT) * ((n + AT - 1) / AT);
+  hipError_t e = hipSuccess;
+  switch (bits) {
+    case 2: e = launch_awq_codes<2, 2>(qweight, k, n, packed, tiles, s); break;
+    case 3: e = launch_awq_codes<3, 3>(qweight, k, n, packed, tiles, s); break;
+    case 4: e = launch_awq_codes<4, 4>(qweight, k, n, packed, tiles, s); break;
+    case 5: e = launch_awq_codes<5, 5>(qweight, k, n, packed, tiles, s); break;
+    case 6: e = launch_awq_codes<6, 6>(qweight, k, n, packed, tiles, s); break;
+    case 7: e = launch_awq_codes<7, 8>(qweight, k, n, packed, tiles, s); break;
+    case 8: e = launch_awq_codes<8, 8>(qweight, k, n, packed, tiles, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_params(qzeros, scales, pdt, n, (int)(k / g), bits, 0, bits == 4 ? 1 : 0, scales_out, biases_out, s);
 }
 
 }  // namespace ql
