@@ -31,6 +31,10 @@ Readings of points the pages leave open:
 * quantize_q8_0: the NaN scale of a block holding a NaN is the fp16 quiet NaN 0x7E00 (the page
   fixes "a NaN scale", not its bits); a block holding an infinity and no NaN takes +inf (0x7C00).
 * take: positions outside [0, rows) are out of range (negative ones too) and give zero bytes.
+* Q4_K / Q6_K: the pages fix the block sizes, the field order and the value formulas and name
+  ggml's block_q4_K / block_q6_K for the layout; the placement of the 6-bit scales and mins inside
+  Q4_K's 12 bytes and of the quants inside the quant bytes follows that layout as this oracle
+  reads it (_q4_k_fields, _q6_k_fields).  No ggml bytes are at hand to check it against.
 * AWQ lane order [0,2,4,6,1,3,5,7]: read as the columns that the nibbles of a word hold, from
   the low nibble up (nibble 1 holds column 2), applied to 4-bit qweight and qzeros alike; other
   widths are plain streams along the outputs.
@@ -62,6 +66,10 @@ __all__ = [
     "mxfp4_dequant_f32",
     "q8_0_dequant_f32",
     "q8_0_quantize",
+    "Q4_K_BYTES",
+    "Q6_K_BYTES",
+    "q4_k_dequant_f32",
+    "q6_k_dequant_f32",
     "mxfp4_blocks_dequant_f32",
     "take",
     "gptq_transcode",
@@ -407,6 +415,103 @@ def q8_0_dequant_f32(blocks_u8) -> np.ndarray:
     q = blk[..., 2:].view(np.int8).astype(np.float64)
     with np.errstate(invalid="ignore"):
         return (d[..., None] * q).astype(np.float32).reshape(lead + (nb * 32,))
+
+
+# --------------------------------------------------------------------------------------
+# Q4_K and Q6_K (Nx_quant "Weights": per 256 values one block of 144 / 210 bytes in the layout of
+# ggml's block_q4_K / block_q6_K; the value formulas and the rounding rule are the page's, the
+# placement of the sub-fields inside the scale and quant bytes is a reading (below).
+# --------------------------------------------------------------------------------------
+
+Q4_K_BYTES, Q6_K_BYTES = 144, 210
+
+
+def _q4_k_fields():
+    """Index tables of the Q4_K reading: for value v of a block (0..255) the qs byte that holds its
+    quant (16 + 32 (v // 64) + v % 32) and the nibble (low for v % 64 < 32, high otherwise); its
+    sub-block is v // 32.  Sub-block j's 6-bit scale and min: for j < 4 the low 6 bits of scale
+    bytes j and j + 4; for j >= 4 the scale is the low nibble of byte j + 4 with the top two bits of
+    byte j - 4 above it, the min the high nibble of byte j + 4 with the top two bits of byte j."""
+    v = np.arange(256)
+    qbyte = 16 + 32 * (v // 64) + v % 32
+    shift = 4 * ((v % 64) // 32)
+    return qbyte, shift
+
+
+def _q4_k_scale_min(sb):
+    """(sc, m) [..., 8] from the 12 scale bytes [..., 12] (see _q4_k_fields)."""
+    sb = sb.astype(np.int64)
+    sc = np.empty(sb.shape[:-1] + (8,), dtype=np.int64)
+    mn = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = sb[..., j] & 63
+        mn[..., j] = sb[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (sb[..., j + 4] & 15) | ((sb[..., j - 4] >> 6) << 4)
+        mn[..., j] = (sb[..., j + 4] >> 4) | ((sb[..., j] >> 6) << 4)
+    return sc, mn
+
+
+def q4_k_dequant_f32(blocks_u8) -> np.ndarray:
+    """blocks [..., n, k/256*144] -> values [..., n, k] (fp32).  Per block: little-endian fp16 d and
+    dmin, 12 bytes of 6-bit scales and mins of the 8 sub-blocks of 32 values, 128 bytes of 4-bit
+    quants (placement: _q4_k_fields).  value = d*sc*q - dmin*m (Nx_quant "Weights", Q4_K), its
+    products exact and one rounding at the subtraction (Nx_quant, the float32 rule for GGUF values).
+
+    Evaluated in fp64 and rounded once to fp32: d*sc*q and dmin*m have at most 21 significant bits;
+    when their difference needs more than 53 bits, the smaller is below 2^-32 of the larger, so the
+    exact difference and its fp64 rounding lie within a quarter ulp of the larger term, an fp32 value,
+    and both round to it."""
+    b = np.asarray(blocks_u8, dtype=np.uint8)
+    lead = b.shape[:-1]
+    assert b.shape[-1] % Q4_K_BYTES == 0
+    nb = b.shape[-1] // Q4_K_BYTES
+    blk = b.reshape(lead + (nb, Q4_K_BYTES))
+    d = f16_bits_to_f32(blk[..., 0].astype(np.uint16) | (blk[..., 1].astype(np.uint16) << np.uint16(8))).astype(np.float64)
+    dmin = f16_bits_to_f32(blk[..., 2].astype(np.uint16) | (blk[..., 3].astype(np.uint16) << np.uint16(8))).astype(np.float64)
+    sc, mn = _q4_k_scale_min(blk[..., 4:16])
+    qbyte, shift = _q4_k_fields()
+    q = (blk[..., qbyte].astype(np.int64) >> shift) & 15  # [..., nb, 256]
+    sub = np.arange(256) // 32
+    with np.errstate(invalid="ignore"):
+        a = (d[..., None] * sc[..., sub]) * q  # exact
+        m = dmin[..., None] * mn[..., sub]  # exact
+        return (a - m).astype(np.float32).reshape(lead + (nb * 256,))
+
+
+def _q6_k_fields():
+    """Index tables of the Q6_K reading: value v of a block (0..255), with h = v // 128, w = v % 128,
+    g = w // 32, l = w % 32, takes its low 4 bits from ql byte 64 h + 32 (g % 2) + l (low nibble for
+    g < 2, high for g >= 2) and its high 2 bits from bits 2g, 2g + 1 of qh byte 128 + 32 h + l; its
+    sub-block (scale byte 192 + v // 16) is v // 16."""
+    v = np.arange(256)
+    h, w = v // 128, v % 128
+    g, l = w // 32, w % 32
+    lo_byte = 64 * h + 32 * (g % 2) + l
+    lo_shift = 4 * (g // 2)
+    hi_byte = 128 + 32 * h + l
+    hi_shift = 2 * g
+    return lo_byte, lo_shift, hi_byte, hi_shift
+
+
+def q6_k_dequant_f32(blocks_u8) -> np.ndarray:
+    """blocks [..., n, k/256*210] -> values [..., n, k] (fp32).  Per block: 128 bytes of the quants'
+    low 4 bits, 64 of their high 2 bits, an int8 scale per sub-block of 16 values, a little-endian
+    fp16 d (placement: _q6_k_fields).  value = d*sc*(q - 32) (Nx_quant "Weights", Q6_K), exact in
+    fp32: d has at most 11 significant bits, |sc| <= 128 and |q - 32| <= 32, and 2047 * 128 * 32 is
+    below 2^24.  An all-zero block gives -0 (0 * -32)."""
+    b = np.asarray(blocks_u8, dtype=np.uint8)
+    lead = b.shape[:-1]
+    assert b.shape[-1] % Q6_K_BYTES == 0
+    nb = b.shape[-1] // Q6_K_BYTES
+    blk = b.reshape(lead + (nb, Q6_K_BYTES))
+    d = f16_bits_to_f32(blk[..., 208].astype(np.uint16) | (blk[..., 209].astype(np.uint16) << np.uint16(8))).astype(np.float64)
+    sc = blk[..., 192:208].view(np.int8).astype(np.float64)  # [..., nb, 16]
+    lo_byte, lo_shift, hi_byte, hi_shift = _q6_k_fields()
+    q = ((blk[..., lo_byte].astype(np.int64) >> lo_shift) & 15) | (((blk[..., hi_byte].astype(np.int64) >> hi_shift) & 3) << 4)
+    sub = np.arange(256) // 16
+    with np.errstate(invalid="ignore"):
+        return ((d[..., None] * sc[..., sub]) * (q - 32)).astype(np.float32).reshape(lead + (nb * 256,))
 
 
 def q8_0_quantize(w_f32) -> np.ndarray:

@@ -659,3 +659,159 @@ def test_awq_transcode_exact_with_power_of_two_scales_and_misorder_fails():
     # reading the 4-bit words as plain streams (the permutation ignored) gives other codes
     plain = O.pack_codes(O.unpack_codes(qw, 4, n).T, 4)
     assert not np.array_equal(plain, pk)
+
+
+# ---------------------------------------------------------------- Q4_K and Q6_K
+# (Nx_quant API docs, "Weights": Q4_K and Q6_K block layouts and value formulas; the float32 rule
+# for GGUF values: a Q6_K value and a Q4_K product are exact, a Q4_K value rounds once at its
+# subtraction; a zero block decodes to zeros, -0 in Q6_K.)  The blocks below are written by a
+# bit-level builder that places each field where the reading puts it, independently of the
+# oracle's index tables.
+from fractions import Fraction
+
+
+def _put(buf, byte, bit, nbits, value):
+    """Write `value` into `nbits` bits of buf starting at bit `bit` of byte `byte` (within the byte)."""
+    assert 0 <= value < (1 << nbits) and bit + nbits <= 8
+    mask = ((1 << nbits) - 1) << bit
+    buf[byte] = (buf[byte] & ~mask & 0xFF) | (value << bit)
+
+
+def _q4_k_block(d_bits, dmin_bits, sc, mn, q):
+    buf = bytearray(144)
+    buf[0:2] = int(d_bits).to_bytes(2, "little")
+    buf[2:4] = int(dmin_bits).to_bytes(2, "little")
+    for j in range(8):
+        if j < 4:  # low 6 bits of scale bytes j (scale) and j + 4 (min)
+            _put(buf, 4 + j, 0, 6, int(sc[j]))
+            _put(buf, 4 + j + 4, 0, 6, int(mn[j]))
+        else:  # low / high nibble of byte j + 4, top two bits of bytes j - 4 (scale) and j (min)
+            _put(buf, 4 + j + 4, 0, 4, int(sc[j]) & 15)
+            _put(buf, 4 + j + 4, 4, 4, int(mn[j]) & 15)
+            _put(buf, 4 + j - 4, 6, 2, int(sc[j]) >> 4)
+            _put(buf, 4 + j, 6, 2, int(mn[j]) >> 4)
+    for v in range(256):  # 64-value chunks of 32 bytes: values 0..31 low nibbles, 32..63 high
+        _put(buf, 16 + 32 * (v // 64) + v % 32, 4 * ((v % 64) // 32), 4, int(q[v]))
+    return np.frombuffer(bytes(buf), dtype=np.uint8)
+
+
+def _q6_k_block(d_bits, sc, q):
+    buf = bytearray(210)
+    for v in range(256):
+        h, w = divmod(v, 128)
+        g, l = divmod(w, 32)
+        _put(buf, 64 * h + 32 * (g % 2) + l, 4 * (g // 2), 4, int(q[v]) & 15)
+        _put(buf, 128 + 32 * h + l, 2 * g, 2, int(q[v]) >> 4)
+    for i in range(16):
+        buf[192 + i] = int(sc[i]) & 0xFF
+    buf[208:210] = int(d_bits).to_bytes(2, "little")
+    return np.frombuffer(bytes(buf), dtype=np.uint8)
+
+
+def _f16_fraction(bits):
+    return Fraction(float(O.f16_bits_to_f32(np.uint16(bits))))
+
+
+def _rne_f32(x: Fraction) -> float:
+    """x rounded to nearest even at 24 significant bits (x normal in fp32 or 0), exactly."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    scale = Fraction(2) ** (23 - e)
+    n = a * scale
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(Fraction(fl) / scale)
+
+
+def test_q4_k_values_follow_the_formula_with_one_rounding():
+    rng = np.random.default_rng(301)
+    for trial in range(6):
+        d_bits = int(O.f32_to_f16_bits(np.float32(rng.uniform(1e-4, 0.05))))
+        dmin_bits = int(O.f32_to_f16_bits(np.float32(rng.uniform(1e-4, 0.05))))
+        sc, mn = rng.integers(0, 64, 8), rng.integers(0, 64, 8)
+        q = rng.integers(0, 16, 256)
+        blk = _q4_k_block(d_bits, dmin_bits, sc, mn, q)
+        got = O.q4_k_dequant_f32(blk[None, :])[0]
+        d, dmin = _f16_fraction(d_bits), _f16_fraction(dmin_bits)
+        for v in range(256):
+            j = v // 32
+            want = _rne_f32(d * int(sc[j]) * int(q[v]) - dmin * int(mn[j]))
+            assert float(got[v]) == want, (trial, v)
+
+
+def test_q4_k_rounds_once_at_the_subtraction():
+    # d = 1, sc = 63, q = 15: 945 (ulp 2^-14 in fp32); dmin * m = 63 * (1 + 2^-10) * 2^-14 is not a
+    # multiple of that ulp, so the difference rounds, once
+    d_bits, dmin_bits = 0x3C00, 0x0401  # 1.0 and (1 + 2^-10) * 2^-14
+    sc, mn = np.full(8, 63), np.full(8, 63)
+    q = np.full(256, 15)
+    got = O.q4_k_dequant_f32(_q4_k_block(d_bits, dmin_bits, sc, mn, q)[None, :])[0]
+    exact = Fraction(945) - 63 * _f16_fraction(dmin_bits)
+    assert float(got[0]) == _rne_f32(exact)
+    assert Fraction(float(got[0])) != exact  # the value did need rounding
+    # products kept exact: with d = 1 + 2^-10 the product d*sc*q = 945 (1 + 2^-10) has 20 significant
+    # bits; a decode that rounded it to the fp16 scale dtype first (946) would give another value
+    got2 = O.q4_k_dequant_f32(_q4_k_block(0x3C01, dmin_bits, sc, mn, q)[None, :])[0]
+    exact2 = 945 * _f16_fraction(0x3C01) - 63 * _f16_fraction(dmin_bits)
+    assert float(got2[0]) == _rne_f32(exact2)
+    assert float(got2[0]) != _rne_f32(Fraction(946) - 63 * _f16_fraction(dmin_bits))
+
+
+def test_q6_k_values_exact_and_zero_blocks_signed():
+    rng = np.random.default_rng(302)
+    for trial in range(6):
+        d_bits = int(O.f32_to_f16_bits(np.float32(rng.uniform(1e-4, 0.05) * rng.choice([-1, 1]))))
+        sc = rng.integers(-128, 128, 16)
+        q = rng.integers(0, 64, 256)
+        blk = _q6_k_block(d_bits, sc, q)
+        got = O.q6_k_dequant_f32(blk[None, :])[0]
+        d = _f16_fraction(d_bits)
+        for v in range(256):
+            want = d * int(sc[v // 16]) * (int(q[v]) - 32)
+            assert Fraction(float(got[v])) == want, (trial, v)  # exact
+    # extremes of the quant: 0 -> -32, 63 -> 31
+    q = np.array([0, 63] * 128)
+    got = O.q6_k_dequant_f32(_q6_k_block(0x3C00, np.ones(16, dtype=np.int64), q)[None, :])[0]
+    assert got[0] == -32.0 and got[1] == 31.0
+    # zero blocks: Q4_K gives +0, Q6_K gives -0 (0 * (0 - 32))
+    z4 = O.q4_k_dequant_f32(np.zeros((2, 144), dtype=np.uint8))
+    z6 = O.q6_k_dequant_f32(np.zeros((2, 210), dtype=np.uint8))
+    assert np.all(z4 == 0) and not np.any(np.signbit(z4))
+    assert np.all(z6 == 0) and np.all(np.signbit(z6))
+
+
+def test_q4_k_q6_k_nonfinite_scales():
+    q = np.arange(256) % 16
+    inf4 = O.q4_k_dequant_f32(_q4_k_block(0x7C00, 0, np.full(8, 1), np.zeros(8, dtype=np.int64), q)[None, :])[0]
+    assert np.all(np.isinf(inf4[q > 0])) and np.all(np.isnan(inf4[q == 0]))  # inf * 0 is NaN
+    nan6 = O.q6_k_dequant_f32(_q6_k_block(0x7E00, np.ones(16, dtype=np.int64), np.arange(256) % 64)[None, :])[0]
+    assert np.all(np.isnan(nan6))
+
+
+def test_q4_k_q6_k_rows_of_blocks():
+    """A row of several blocks decodes block by block (k = 512: two blocks per row, three rows)."""
+    rng = np.random.default_rng(303)
+    rows4, rows6, want4, want6 = [], [], [], []
+    for r in range(3):
+        b4, b6 = [], []
+        for bi in range(2):
+            blk4 = _q4_k_block(0x2000 + r * 16 + bi, 0x1800 + bi, rng.integers(0, 64, 8), rng.integers(0, 64, 8),
+                               rng.integers(0, 16, 256))
+            blk6 = _q6_k_block(0x2400 + r + bi, rng.integers(-128, 128, 16), rng.integers(0, 64, 256))
+            b4.append(blk4)
+            b6.append(blk6)
+            want4.append(O.q4_k_dequant_f32(blk4[None, :])[0])
+            want6.append(O.q6_k_dequant_f32(blk6[None, :])[0])
+        rows4.append(np.concatenate(b4))
+        rows6.append(np.concatenate(b6))
+    got4 = O.q4_k_dequant_f32(np.stack(rows4))
+    got6 = O.q6_k_dequant_f32(np.stack(rows6))
+    np.testing.assert_array_equal(got4.reshape(-1), np.concatenate(want4))
+    np.testing.assert_array_equal(got6.reshape(-1), np.concatenate(want6))
