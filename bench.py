@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--legs", default="all",
                     help="comma-separated legs to run (decode8, decode4m8, decode_breakdown, prefill, experts, "
-                         "prefill6, decode_bits, quantize, blocks, transcode) or 'all'")
+                         "prefill6, decode_bits, quantize, blocks, transcode, kquant) or 'all'")
     ap.add_argument("--no-headline", action="store_true",
                     help="skip the headline decode step (for profiling single legs); prints the legs only")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -423,6 +423,45 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                              "kernel": "route_kernel + " + ("experts_mx_kernel" if fname == "mxfp4" else "experts_q8_kernel")},
+            }
+            del copies
+            torch.cuda.empty_cache()
+
+    # ---------------- Q4_K / Q6_K routed experts: the same expert stack and routing with k = 2816
+    # (11 blocks of 256 values: the nearest multiple of 256 to 2880)
+    if want("kquant"):
+        cfg = synth.EXPERTS_32x5760x2880
+        e, n, tokens, top = cfg["e"], cfg["n"], cfg["tokens"], cfg["top"]
+        k = 2816
+        ids = torch.from_numpy(synth.topk_ids(synth.seed_for(5, part=2), tokens, top, e).reshape(-1)).to(dev)
+        x = torch.randn((tokens, k), generator=gen(56_000), device=dev).to(torch.bfloat16)
+        y = torch.empty((tokens * top, n), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(q.qlinear_apply_experts_workspace_size(tokens * top, e), dtype=torch.uint8, device=dev)
+        flop = 2.0 * tokens * top * n * k
+        for fmt, fname, nbytes, dat, lo, hi in ((q.QL_Q4_K, "q4_k", 144, 0, -16.0, -11.0),
+                                                (q.QL_Q6_K, "q6_k", 210, 208, -17.0, -12.0)):
+            log(f"leg: experts {fname}")
+            copies = []
+            nb = k // 256
+            for c in range(3):
+                blocks = torch.randint(0, 256, (e, n, nb, nbytes), generator=gen(57_000 + 10 * c + fmt), device=dev,
+                                       dtype=torch.int32).to(torch.uint8)
+                nd = 2 if fmt == q.QL_Q4_K else 1  # fp16 fields: d, dmin (Q4_K) or d (Q6_K)
+                d = torch.exp2(torch.empty((e, n, nb, nd), device=dev).uniform_(lo, hi, generator=gen(58_000 + c)))
+                blocks[..., dat:dat + 2 * nd] = d.to(torch.float16).view(torch.uint8).view(e, n, nb, 2 * nd)
+                copies.append(blocks.reshape(e, n, nb * nbytes).contiguous())
+            wb = copies[0].numel()
+            avg, med = _time_launches(
+                lambda i: q.qlinear_apply_experts(fmt, copies[i % 3], None, ids, x, n=n, k=k, pos_per_row=top, y=y,
+                                                  workspace=ws), 20, 20, stream)
+            byts = wb + x.numel() * 2 + y.numel() * 2
+            gbs = byts / (avg * 1e-3) / 1e9
+            legs[f"experts_{fname}"] = {
+                "ms": round(avg, 4), "gbs": round(gbs, 1), "tflops": round(flop / (avg * 1e-3) / 1e12, 1),
+                "weights_bytes": wb, "k": k,
+                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "kernel": f"route_kernel + experts_kq_kernel<{fmt}>"},
             }
             del copies
             torch.cuda.empty_cache()

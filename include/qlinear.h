@@ -50,7 +50,7 @@ typedef enum {
 } ql_status;
 
 typedef enum { QL_F32 = 0, QL_F16 = 1, QL_BF16 = 2 } ql_dtype;
-typedef enum { QL_AFFINE = 0, QL_MXFP4 = 1, QL_Q8_0 = 2, QL_MXFP4_BLOCKS = 3 } ql_format;
+typedef enum { QL_AFFINE = 0, QL_MXFP4 = 1, QL_Q8_0 = 2, QL_MXFP4_BLOCKS = 3, QL_Q4_K = 4, QL_Q6_K = 5 } ql_format;
 
 /* One GEMV of a problem list: y[m,n] = x[m,k] . dequant(W[n,k])^T (+ layer_bias[n]).
  * All pointers are device memory; layer_bias may be NULL. */
@@ -146,7 +146,15 @@ ql_status qlinear_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros,
  *              16 bytes, byte j holding value j in its low nibble and value j + 16 in its high one
  *              (Nx_quant Weights, Mxfp4_blocks); values as QL_MXFP4.  w1 and w2 must be NULL; w0
  *              needs no alignment.
- * For MXFP4 and Q8_0, `rows` may count the rows of a whole expert stack ([e*n]). */
+ *   QL_Q4_K:   w0 = blocks [rows, k/256*144] (Nx_quant Weights, Q4_K: fp16 d and dmin, 12 bytes of
+ *              6-bit sub-block scales and mins, 128 bytes of 4-bit quants, placed as ggml's
+ *              block_q4_K), value = d*sc*q - dmin*m with exact products and one rounding at the
+ *              subtraction.  w0 16-byte aligned; w1 and w2 must be NULL.
+ *   QL_Q6_K:   w0 = blocks [rows, k/256*210] (Nx_quant Weights, Q6_K: 128 bytes of low 4 bits, 64
+ *              of high 2 bits, 16 int8 scales, fp16 d, placed as ggml's block_q6_K), value =
+ *              d*sc*(q - 32), exact (-0 from a zero block).  w0 2-byte aligned; w1, w2 NULL.
+ *              For both, k % 256 == 0.
+ * For the block formats, `rows` may count the rows of a whole expert stack ([e*n]). */
 ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const void* w2,
                           ql_dtype param_dtype, int64_t rows, int64_t k, int bits,
                           int group_size, void* out, ql_dtype out_dtype, void* stream);
@@ -242,8 +250,16 @@ ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
  * ids[p] is not in [0, e).  A row's bits do not depend on the other positions' experts.
  *   QL_MXFP4: w0 = codes [e, n, k/2], w1 = scales [e, n, k/32].
  *   QL_Q8_0:  w0 = blocks [e, n, k/32*34], w1 = NULL.
+ *   QL_Q4_K:  w0 = blocks [e, n, k/256*144] (16-byte aligned), w1 = NULL; k % 256 == 0.
+ *   QL_Q6_K:  w0 = blocks [e, n, k/256*210] (2-byte aligned), w1 = NULL; k % 256 == 0.
+ *             (Nx_quant Weights, Q4_K / Q6_K; the codes enter the products exactly and each
+ *             sub-block's fp32 sum is scaled by d*sc, plus -dmin*m times its sum of x for Q4_K.)
  * x is [n_pos / pos_per_row, k] (pos_per_row divides n_pos; a token's top-k slots share its row);
- * x_dtype must be QL_BF16 (MXFP4 values are exact in bf16, and so are int8 codes); y is
+ * x_dtype is QL_BF16 or QL_F16 (Nx_quant Products, apply_experts: any float x).  MXFP4 values are
+ * exact in bf16 and meet bf16 x directly; fp16 x enters as the exact sum of two bf16 parts (top 8
+ * significant bits, then the other 3), each through the bf16 products.  Q8_0 takes fp16 products
+ * (bf16 x converted after an exact power-of-two scaling per row, fp16 x as it is); Q4_K and Q6_K
+ * codes are exact in both 16-bit types and meet x in its own dtype's products; y is
  * [n_pos, n] in y_dtype.  k % 32 == 0; 0 <= e <= 4096.  Needs a workspace of
  * qlinear_apply_experts_workspace_size(n_pos, e) bytes (routing scratch: offsets then perm,
  * as qlinear_route writes them, each padded to 16 bytes, then the e experts in decreasing order

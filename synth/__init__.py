@@ -22,6 +22,7 @@ __all__ = [
     "acts_bits",
     "mxfp4_codes_scales",
     "q8_0_random_blocks",
+    "kquant_random_blocks",
     "topk_ids",
     "seed_for",
     "QWEN3_0_6B_LAYER",
@@ -111,6 +112,25 @@ def q8_0_random_blocks(seed: int, e: int, n: int, k: int) -> np.ndarray:
     blocks[..., 0:2] = d.view(np.uint8).reshape(e, n, nb, 2)
     blocks[..., 2:] = q.view(np.uint8)
     return blocks.reshape(e, n, nb * 34)
+
+
+def kquant_random_blocks(seed: int, rows: int, k: int, fmt: str) -> np.ndarray:
+    """Structurally valid Q4_K ('q4_k', 144 bytes) or Q6_K ('q6_k', 210 bytes) blocks [rows,
+    k/256*bytes] with random contents: every byte uniform, then the fp16 fields set to finite
+    values: Q4_K's d and dmin (bytes 0..3) log-uniform in [2^-16, 2^-11] (with 6-bit scales and
+    4-bit quants that spans the +-0.05 of N(0, 0.02) weights), Q6_K's d (bytes 208..209)
+    log-uniform in [2^-17, 2^-12] (int8 scales, quants - 32 in [-32, 31])."""
+    g = rng(seed)
+    nbytes = 144 if fmt == "q4_k" else 210
+    nb = k // 256
+    blocks = g.integers(0, 256, size=(rows, nb, nbytes), dtype=np.uint8)
+    if fmt == "q4_k":
+        dd = np.exp2(g.uniform(-16.0, -11.0, size=(rows, nb, 2))).astype(np.float16)
+        blocks[..., 0:4] = dd.view(np.uint8).reshape(rows, nb, 4)
+    else:
+        d = np.exp2(g.uniform(-17.0, -12.0, size=(rows, nb))).astype(np.float16)
+        blocks[..., 208:210] = d.view(np.uint8).reshape(rows, nb, 2)
+    return blocks.reshape(rows, nb * nbytes)
 
 
 def topk_ids(seed: int, tokens: int, top: int, e: int) -> np.ndarray:

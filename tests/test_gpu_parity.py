@@ -564,6 +564,23 @@ def test_apply_experts_small(fmt, ydt):
 
 
 @pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
+def test_apply_experts_f16_x(fmt):
+    """fp16 activations (Nx_quant Products, apply_experts: any float x): MXFP4 takes them as the
+    exact sum of two bf16 parts, Q8_0 as they are; the same bounds as bf16 x."""
+    (w0, w1), W, ids, _, n, k, top = _experts_small(fmt, 71 + fmt)
+    xh = synth.acts_bits(72 + fmt, ids.shape[0], k, "f16")
+    xh[0, :8] = O.to_bits("f16", np.float32([1e-7, -3e-6, 6.0e4, -5.5e4, 1.0009765625, 2.0**-14, 0.0, -0.0]))
+    y = q.qlinear_apply_experts(fmt, w0, w1, torch.from_numpy(ids.reshape(-1)).to(DEV), bits_to_dev(xh, "f16"), n=n,
+                                k=k, pos_per_row=top, y_dtype=torch.float32)
+    _sync()
+    ref = O.apply_experts(W, ids.reshape(-1), O.bits_to_f64("f16", xh), pos_per_row=top)
+    flat = ids.reshape(-1)
+    live = (flat >= 0) & (flat < W.shape[0])
+    assert np.all(out_f64(y)[~live] == 0.0)
+    _assert_rel(y[torch.from_numpy(live).to(DEV)], ref[live], _experts_tol(fmt), "experts f16 x")
+
+
+@pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
 @pytest.mark.parametrize("e,n,k,tokens,top,skew", [
     (3, 300, 288, 100, 2, True),    # one expert with ~150 positions (two chunks), k % 64 == 32
     (300, 64, 64, 50, 4, False),    # most experts empty; the expert order spans two workgroups

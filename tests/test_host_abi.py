@@ -165,7 +165,7 @@ def test_route_and_experts_reject_bad_arguments(lib):
 
     assert call(fmt=0) == QL_ERR_UNSUPPORTED
     assert call(fmt=3) == QL_ERR_UNSUPPORTED  # MXFP4 in GGUF blocks: dequant and take only
-    assert call(xdt=F16) == QL_ERR_DTYPE
+    assert call(xdt=F32) == QL_ERR_DTYPE  # x is bf16 or fp16
     assert call(k=2881) == QL_ERR_SHAPE
     assert call(ppr=3) == QL_ERR_SHAPE
     assert call(wsb=ws - 1) == QL_ERR_WORKSPACE
@@ -173,6 +173,12 @@ def test_route_and_experts_reject_bad_arguments(lib):
     assert call(fmt=2) == QL_ERR_SHAPE  # Q8_0 takes no w1
     assert call(fmt=2, w1=None, w0=FAKE + 1) == QL_ERR_ALIGN
     assert call(n_pos=0) == QL_OK
+    # Q4_K / Q6_K: k a multiple of 256, no w1, Q4_K blocks 16-byte aligned
+    assert call(fmt=4, w1=None) == QL_ERR_SHAPE  # k = 2880 is not a multiple of 256
+    assert call(fmt=5, w1=None, k=2816, w0=FAKE + 1) == QL_ERR_ALIGN
+    assert call(fmt=4, w1=None, k=2816, w0=FAKE + 2) == QL_ERR_ALIGN
+    assert call(fmt=4, k=2816) == QL_ERR_SHAPE  # w1 given
+    assert call(fmt=6) == QL_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -199,7 +205,16 @@ def test_quantize_q8_0_take_and_blocks_reject_bad_arguments(lib):
     assert lib.qlinear_dequant(3, FAKE, None, None, BF16, 4, 48, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
     assert lib.qlinear_dequant(3, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE + 2, F32, None) == QL_ERR_ALIGN
     assert lib.qlinear_dequant(3, None, None, None, BF16, 0, 64, 0, 0, None, F32, None) == QL_OK
-    assert lib.qlinear_dequant(4, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_UNSUPPORTED
+    assert lib.qlinear_dequant(6, FAKE, None, None, BF16, 4, 64, 0, 0, FAKE, F32, None) == QL_ERR_UNSUPPORTED
+    # Q4_K / Q6_K: k a multiple of 256, one part, Q4_K blocks 16-byte aligned, Q6_K 2-byte
+    for fmt in (4, 5):
+        assert lib.qlinear_dequant(fmt, FAKE, None, None, BF16, 4, 384, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
+        assert lib.qlinear_dequant(fmt, FAKE, FAKE, None, BF16, 4, 256, 0, 0, FAKE, F32, None) == QL_ERR_SHAPE
+        assert lib.qlinear_dequant(fmt, None, None, None, BF16, 4, 256, 0, 0, FAKE, F32, None) == QL_ERR_NULL
+        assert lib.qlinear_dequant(fmt, FAKE, None, None, BF16, 4, 256, 0, 0, FAKE + 8, F32, None) == QL_ERR_ALIGN
+        assert lib.qlinear_dequant(fmt, None, None, None, BF16, 0, 256, 0, 0, None, F32, None) == QL_OK
+    assert lib.qlinear_dequant(4, FAKE + 2, None, None, BF16, 4, 256, 0, 0, FAKE, F32, None) == QL_ERR_ALIGN
+    assert lib.qlinear_dequant(5, FAKE + 1, None, None, BF16, 4, 256, 0, 0, FAKE, F32, None) == QL_ERR_ALIGN
 
 
 def test_transcode_gptq_rejects_bad_arguments(lib):

@@ -19,6 +19,8 @@ __all__ = [
     "QL_MXFP4",
     "QL_Q8_0",
     "QL_MXFP4_BLOCKS",
+    "QL_Q4_K",
+    "QL_Q6_K",
     "lib_path",
     "load_library",
     "qlinear_quantize",
@@ -42,7 +44,7 @@ __all__ = [
     "qlinear_version",
 ]
 
-QL_AFFINE, QL_MXFP4, QL_Q8_0, QL_MXFP4_BLOCKS = 0, 1, 2, 3
+QL_AFFINE, QL_MXFP4, QL_Q8_0, QL_MXFP4_BLOCKS, QL_Q4_K, QL_Q6_K = 0, 1, 2, 3, 4, 5
 _QL_F32, _QL_F16, _QL_BF16 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

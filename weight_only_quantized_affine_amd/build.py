@@ -18,7 +18,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqlinear.so")
 SOURCES = ["qlinear_api.cpp", "quantize.hip", "dequant.hip", "gemv.hip", "gemv_m1.hip", "gemv_m2.hip", "gemv_m4.hip",
            "gemv_m8.hip", "gemm.hip", "experts.hip", "experts_mx.hip",
-           "experts_q8.hip", "gemv_stream.hip", "take.hip", "transcode.hip"]
+           "experts_q8.hip", "experts_kq.hip", "gemv_stream.hip", "take.hip", "transcode.hip"]
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",

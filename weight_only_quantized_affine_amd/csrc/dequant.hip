@@ -178,6 +178,79 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const uint8_t* __rest
   for (int j = 0; j < 4; ++j) store8(out, o + 8 * j, v + 8 * j, odt);
 }
 
+// Q4_K (Nx_quant Weights, Q4_K; the layout of ggml's block_q4_K): per 256 values a 144-byte block of
+// fp16 d and dmin, 12 bytes of 6-bit scales and mins (sub-block j < 4: low 6 bits of bytes j and
+// j + 4; j >= 4: low / high nibble of byte j + 4 under the top two bits of bytes j - 4 / j) and 128
+// bytes of quants (values 64 c + i and 64 c + 32 + i in the low / high nibble of quant byte 32 c + i).
+// One lane per sub-block of 32 values: value = (d*sc)*q - dmin*m, the products exact in fp32 and one
+// rounding at the subtraction.
+__global__ __launch_bounds__(256) void dequant_q4_k_kernel(const uint8_t* __restrict__ blocks, int64_t rows,
+                                                           int64_t k, void* __restrict__ out, int odt) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (k / 256) * 8) return;
+  const int64_t b = t >> 3;
+  const int j = (int)(t & 7);
+  const uint8_t* bp = blocks + b * 144;
+  const u32x4_t hdr = *(const u32x4_t*)bp;  // d, dmin, scale bytes 0..11 (blocks are 16-byte aligned)
+  auto sbyte = [&](int i) __attribute__((always_inline)) { return (hdr[1 + (i >> 2)] >> (8 * (i & 3))) & 0xffu; };
+  uint32_t sc, mn;
+  if (j < 4) {
+    sc = sbyte(j) & 63u;
+    mn = sbyte(j + 4) & 63u;
+  } else {
+    sc = (sbyte(j + 4) & 15u) | ((sbyte(j - 4) >> 6) << 4);
+    mn = (sbyte(j + 4) >> 4) | ((sbyte(j) >> 6) << 4);
+  }
+  const float ds = f16_bits_to_f32(hdr[0] & 0xffffu) * (float)sc;   // exact
+  const float dm = f16_bits_to_f32(hdr[0] >> 16) * (float)mn;       // exact
+  const u32x4_t q0 = *(const u32x4_t*)(bp + 16 + 32 * (j >> 1));
+  const u32x4_t q1 = *(const u32x4_t*)(bp + 32 + 32 * (j >> 1));
+  const int sh = 4 * (j & 1);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t w = i < 16 ? q0[i >> 2] : q1[(i - 16) >> 2];
+    const uint32_t q = (w >> (8 * (i & 3) + sh)) & 15u;
+    v[i] = ds * (float)q - dm;  // ds*q is exact: the only rounding is the subtraction's
+  }
+  const int64_t o = b * 256 + 32 * j;  // rows of k values hold k / 256 blocks each
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store8(out, o + 8 * i, v + 8 * i, odt);
+}
+
+// Q6_K (Nx_quant Weights, Q6_K; the layout of ggml's block_q6_K): per 256 values a 210-byte block of
+// 128 bytes of low 4 bits, 64 bytes of high 2 bits, 16 int8 sub-block scales and fp16 d.  Value
+// 128 h + 32 g + l (l < 32) takes its low bits from byte 64 h + 32 (g % 2) + l (low nibble for g < 2,
+// high for g >= 2) and its high bits from bits 2g, 2g + 1 of byte 128 + 32 h + l; its scale is byte
+// 192 + (value / 16).  One lane per (h, g): value = (d*sc)*(q - 32), exact in fp32 (0 * -32 = -0).
+__global__ __launch_bounds__(256) void dequant_q6_k_kernel(const uint8_t* __restrict__ blocks, int64_t rows,
+                                                           int64_t k, void* __restrict__ out, int odt) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows * (k / 256) * 8) return;
+  const int64_t b = t >> 3;
+  const int h = (int)((t >> 2) & 1), g = (int)(t & 3);
+  const uint16_t* bp = (const uint16_t*)(blocks + b * 210);  // blocks are 2-byte aligned
+  const float d = f16_bits_to_f32(bp[104]);
+  const uint32_t sw = bp[96 + 4 * h + g];  // scale bytes 192 + 8 h + 2 g and the next
+  const float s0 = d * (float)(int8_t)(sw & 0xffu), s1 = d * (float)(int8_t)(sw >> 8);  // exact
+  const int lo_sh = 4 * (g >> 1), hi_sh = 2 * g;
+  float v[32];
+#pragma unroll
+  for (int l2 = 0; l2 < 16; ++l2) {  // two values (l = 2 l2, 2 l2 + 1) per half-word
+    const uint32_t lo = bp[32 * h + 16 * (g & 1) + l2];
+    const uint32_t hi = bp[64 + 16 * h + l2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int l = 2 * l2 + e;
+      const int q = (int)((((lo >> (8 * e)) >> lo_sh) & 15u) | ((((hi >> (8 * e)) >> hi_sh) & 3u) << 4));
+      v[l] = (l < 16 ? s0 : s1) * (float)(q - 32);
+    }
+  }
+  const int64_t o = b * 256 + 128 * h + 32 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store8(out, o + 8 * i, v + 8 * i, odt);
+}
+
 }  // namespace
 
 hipError_t launch_dequant_affine(const uint32_t* packed, const void* scales, const void* biases, int pdt,
@@ -225,4 +298,17 @@ hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, v
   return hipGetLastError();
 }
 
+}  // namespace ql
+
+namespace ql {
+hipError_t launch_dequant_kquant(int fmt_bytes, const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt,
+                                 hipStream_t s) {
+  const int64_t total = rows * (k / 256) * 8;
+  const unsigned nb = (unsigned)((total + 255) / 256);
+  if (fmt_bytes == 144)
+    dequant_q4_k_kernel<<<nb, 256, 0, s>>>(blocks, rows, k, out, odt);
+  else
+    dequant_q6_k_kernel<<<nb, 256, 0, s>>>(blocks, rows, k, out, odt);
+  return hipGetLastError();
+}
 }  // namespace ql

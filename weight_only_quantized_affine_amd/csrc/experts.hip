@@ -12,7 +12,7 @@ namespace ql {
 namespace {
 using namespace ex_detail;
 
-enum : int { FMT_MXFP4 = 1, FMT_Q8_0 = 2 };  // the ql_format values
+enum : int { FMT_MXFP4 = 1, FMT_Q8_0 = 2, FMT_Q4_K = 4, FMT_Q6_K = 5 };  // the ql_format values
 
 // ---------------------------------------------------------------- routing
 
@@ -147,7 +147,6 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
                                 void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, float* xfac,
                                 hipStream_t s) {
-  (void)xdt;
   hipError_t err;
   if (e == 0 || k == 0) {  // no expert, or empty products: every row is zero
     zero_rows_kernel<<<(unsigned)n_pos, 256, 0, s>>>(n, y, ydt);
@@ -156,14 +155,18 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
   // routing, expert order, and zero rows for the positions routed nowhere
   const int64_t x_rows = n_pos / pos_per_row;
   route_kernel<<<(unsigned)e, 1024, (size_t)(e > 1024 ? e : 1024) * 4, s>>>(
-      ids, n_pos, e, offsets, perm, order, y, n, ydt, (const uint16_t*)x, x_rows, k, fmt == FMT_Q8_0 ? xfac : nullptr);
+      ids, n_pos, e, offsets, perm, order, y, n, ydt, (const uint16_t*)x, x_rows, k,
+      fmt == FMT_Q8_0 && xdt == DT_BF16 ? xfac : nullptr);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (fmt == FMT_Q8_0)
-    return launch_experts_q8((const uint8_t*)w0, e, n, k, offsets, perm, order, xfac, (const uint16_t*)x, x_rows,
+    return launch_experts_q8((const uint8_t*)w0, e, n, k, offsets, perm, order, xfac, (const uint16_t*)x, xdt, x_rows,
+                             pos_per_row, y, ydt, s);
+  if (fmt == FMT_Q4_K || fmt == FMT_Q6_K)
+    return launch_experts_kq(fmt, (const uint8_t*)w0, e, n, k, offsets, perm, order, (const uint16_t*)x, xdt, x_rows,
                              pos_per_row, y, ydt, s);
   return launch_experts_mx((const uint8_t*)w0, (const uint8_t*)w1, e, n, k, offsets, perm, order,
-                           (const uint16_t*)x, x_rows, pos_per_row, y, ydt, s);
+                           (const uint16_t*)x, xdt, x_rows, pos_per_row, y, ydt, s);
 }
 
 }  // namespace ql

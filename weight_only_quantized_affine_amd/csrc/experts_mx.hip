@@ -102,9 +102,24 @@ __device__ __forceinline__ void mx_store(const f32x4_t (&acc)[XCT][MS], const in
   }
 }
 
+// 8 fp16 values (one x fragment) -> bf16 fragments hi and lo with hi + lo equal to them exactly: hi
+// keeps the top 8 significant bits of each (its fp32 pattern cut to 16 bits), lo = x - hi holds the
+// other 3 at most, exact in bf16 (fp16's exponent range lies inside bf16's).
+__device__ __forceinline__ void split_f16(const u32x4_t& v, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float f0 = f16_bits_to_f32(v[e] & 0xffffu), f1 = f16_bits_to_f32(v[e] >> 16);
+    const uint32_t h0 = __float_as_uint(f0) & 0xffff0000u, h1 = __float_as_uint(f1) & 0xffff0000u;
+    const uint32_t l0 = __float_as_uint(f0 - __uint_as_float(h0)), l1 = __float_as_uint(f1 - __uint_as_float(h1));
+    hi[e] = (h0 >> 16) | h1;
+    lo[e] = (l0 >> 16) | (l1 & 0xffff0000u);
+  }
+}
+
 // x stage: row r holds 16 chunks of 8 values (k-tile 128), chunk c at slot c ^ (r % 16), so that the
-// 16 rows of one fragment read hit 16 distinct bank groups.
-template <int MS, bool SCL_LDS>
+// 16 rows of one fragment read hit 16 distinct bank groups.  fp16 x (XF16) is staged as it is and
+// each fragment goes through the products twice, as its bf16 hi and lo parts.
+template <int MS, bool SCL_LDS, bool XF16>
 __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
                                          const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
                                          __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K, int64_t N,
@@ -177,17 +192,21 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      u32x4_t af[MS];
+      u32x4_t af[MS], al[XF16 ? MS : 1];
 #pragma unroll
       for (int rt = 0; rt < MS; ++rt) {
         const int r = rt * 16 + j16;
         af[rt] = *(const u32x4_t*)(stage + (r * 16 + ((4 * q + t) ^ j16)) * 16);
+        if constexpr (XF16) split_f16(af[rt], af[rt], al[rt]);
       }
 #pragma unroll
       for (int ct = 0; ct < XCT; ++ct) {
         const u32x4_t bf = decode_mxfp4(wb.c[ct][t], scl[ct]);
 #pragma unroll
-        for (int rt = 0; rt < MS; ++rt) acc[ct][rt] = mfma16_bf16(af[rt], bf, acc[ct][rt]);
+        for (int rt = 0; rt < MS; ++rt) {
+          acc[ct][rt] = mfma16_bf16(af[rt], bf, acc[ct][rt]);
+          if constexpr (XF16) acc[ct][rt] = mfma16_bf16(al[rt], bf, acc[ct][rt]);
+        }
       }
     }
   };
@@ -236,7 +255,7 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     mx_store<MS, 2>(acc, sPos, rows, stg, N, ncol0, y, DT_F16);
 }
 
-template <bool SCL_LDS>
+template <bool SCL_LDS, bool XF16>
 __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
                                           const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
                                           __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K,
@@ -245,7 +264,7 @@ __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int 
   switch ((rows + 15) >> 4) {
 #define QL_MX_CASE(ms)                                                                                             \
   case ms:                                                                                                         \
-    mx_chunk<ms, SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);          \
+    mx_chunk<ms, SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);    \
     break;
     QL_MX_CASE(1)
     QL_MX_CASE(2)
@@ -253,13 +272,13 @@ __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int 
     QL_MX_CASE(4)
     QL_MX_CASE(5)
     default:
-      mx_chunk<6, SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+      mx_chunk<6, SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
       break;
 #undef QL_MX_CASE
   }
 }
 
-template <bool SCL_LDS>
+template <bool SCL_LDS, bool XF16>
 __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales, int64_t e, int64_t N,
                                                             int64_t K, const int32_t* __restrict__ offsets,
@@ -315,7 +334,7 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
     __syncthreads();  // previous chunk's readers of sPos are done (and the scale bytes are staged)
     if (tid < XMC) sPos[tid] = tid < rows ? perm_pos[off + mc + tid] : -1;
     __syncthreads();
-    mx_chunks<SCL_LDS>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+    mx_chunks<SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
   }
 }
 
@@ -323,15 +342,22 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
 
 hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_t e, int64_t n, int64_t k,
                              const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
-                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
-  const int64_t grid = e * ((n + XBN - 1) / XBN);
+                             int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
+  const unsigned grid = (unsigned)(e * ((n + XBN - 1) / XBN));
   const size_t scl = (size_t)((3 + XBN * (k / 32) + 3) / 4 * 4);
-  if (scl <= (size_t)XSCL_MAX)
-    experts_mx_kernel<true><<<(unsigned)grid, XW * 64, scl, s>>>(codes, scales, e, n, k, offsets, perm, order, x,
-                                                                 x_rows, pos_per_row, y, ydt);
+  const bool in_lds = scl <= (size_t)XSCL_MAX;
+#define QL_MX_LAUNCH(L, H)                                                                                          \
+  experts_mx_kernel<L, H><<<grid, XW * 64, L ? scl : 0, s>>>(codes, scales, e, n, k, offsets, perm, order, x, x_rows, \
+                                                             pos_per_row, y, ydt)
+  if (in_lds && xdt == DT_F16)
+    QL_MX_LAUNCH(true, true);
+  else if (in_lds)
+    QL_MX_LAUNCH(true, false);
+  else if (xdt == DT_F16)
+    QL_MX_LAUNCH(false, true);
   else
-    experts_mx_kernel<false><<<(unsigned)grid, XW * 64, 0, s>>>(codes, scales, e, n, k, offsets, perm, order, x,
-                                                                x_rows, pos_per_row, y, ydt);
+    QL_MX_LAUNCH(false, false);
+#undef QL_MX_LAUNCH
   return hipGetLastError();
 }
 

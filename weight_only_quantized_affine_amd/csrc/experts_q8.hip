@@ -6,7 +6,8 @@
 // Each weight is dequantized once, in registers, to fp16: d * q rounded once (2^-12 relative; d is
 // an fp16 and q an int8, so the product has up to 18 significant bits), and x enters as fp16 after
 // an exact power-of-two scaling per x row that brings max |x| into [2^14, 2^15).  The products run
-// on v_mfma_f32_16x16x32_f16 with fp32 accumulation; the row factor is applied at the end.  A block
+// on v_mfma_f32_16x16x32_f16 with fp32 accumulation; the row factor is applied at the end.  fp16 x
+// enters as it is (factor 1).  A block
 // scale |d| > 511.75 could overflow fp16 (|d q| > 65504): a workgroup that meets one recomputes its
 // outputs in fp32 from the blocks directly (slow, exact up to fp32 rounding).
 #include "experts_common.hpp"
@@ -47,7 +48,7 @@ __device__ __forceinline__ void q8_dequant(uint32_t w, f16x2_t d2, uint32_t& lo,
 }
 
 // x stage: row r holds 16 chunks of 8 values, chunk c at slot c ^ (r % 16) (as experts_mx.hip).
-template <int MS>
+template <int MS, bool XF16>
 __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const float* __restrict__ sXinv,
                                          const float* __restrict__ sXs, int* __restrict__ sFlag, int rows,
                                          uint8_t* const* stg, __amdgpu_buffer_rsrc_t rsX,
@@ -177,11 +178,13 @@ __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const
     copy_x(kt + QNS - 1 < KT ? kt + QNS - 1 : KT - 1, refill);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (kt < KT) convert_x(cur);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's conversions are in LDS
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
+    if constexpr (!XF16) {  // fp16 x is staged as it is
+      if (kt < KT) convert_x(cur);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's conversions are in LDS
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (kt < KT) compute(kt, cur, wb);
     __builtin_amdgcn_sched_barrier(0);
@@ -259,6 +262,7 @@ __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const
   }
 }
 
+template <bool XF16>
 __global__ __launch_bounds__(512, 1) void experts_q8_kernel(const uint8_t* __restrict__ blocks, int64_t e, int64_t N,
                                                             int64_t K, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ perm_pos,
@@ -308,15 +312,16 @@ __global__ __launch_bounds__(512, 1) void experts_q8_kernel(const uint8_t* __res
     if (tid < QMC) {
       const int32_t pos = tid < rows ? perm_pos[off + mc + tid] : perm_pos[off + mc];
       sPos[tid] = tid < rows ? pos : -1;
-      sXinv[tid] = xfac[2 * (pos / pos_per_row)];
-      sXs[tid] = xfac[2 * (pos / pos_per_row) + 1];
+      sXinv[tid] = XF16 ? 1.0f : xfac[2 * (pos / pos_per_row)];
+      sXs[tid] = XF16 ? 1.0f : xfac[2 * (pos / pos_per_row) + 1];
     }
     if (tid == 0) sFlag = 0;
     __syncthreads();
     switch ((rows + 15) >> 4) {
 #define QL_Q8_CASE(ms)                                                                                             \
   case ms:                                                                                                         \
-    q8_chunk<ms>(sPos, sXinv, sXs, &sFlag, rows, stg, rsX, rsW, K, N, ncol0, wa, wsh, wend, tail, pos_per_row, y, ydt);        \
+    q8_chunk<ms, XF16>(sPos, sXinv, sXs, &sFlag, rows, stg, rsX, rsW, K, N, ncol0, wa, wsh, wend, tail, pos_per_row, y, \
+                       ydt);                                                                                        \
     break;
       QL_Q8_CASE(1)
       QL_Q8_CASE(2)
@@ -324,7 +329,8 @@ __global__ __launch_bounds__(512, 1) void experts_q8_kernel(const uint8_t* __res
       QL_Q8_CASE(4)
       QL_Q8_CASE(5)
       default:
-        q8_chunk<6>(sPos, sXinv, sXs, &sFlag, rows, stg, rsX, rsW, K, N, ncol0, wa, wsh, wend, tail, pos_per_row, y, ydt);
+        q8_chunk<6, XF16>(sPos, sXinv, sXs, &sFlag, rows, stg, rsX, rsW, K, N, ncol0, wa, wsh, wend, tail, pos_per_row, y,
+                          ydt);
         break;
 #undef QL_Q8_CASE
     }
@@ -342,7 +348,8 @@ __global__ __launch_bounds__(512, 1) void experts_q8_kernel(const uint8_t* __res
           const uint8_t* blk = wr + 34 * b;
           float part = 0.0f;
           for (int jj = 0; jj < 32; ++jj)
-            part = __builtin_fmaf(bf16_bits_to_f32(xr[32 * b + jj]), (float)(int8_t)blk[2 + jj], part);
+            part = __builtin_fmaf(XF16 ? f16_bits_to_f32(xr[32 * b + jj]) : bf16_bits_to_f32(xr[32 * b + jj]),
+                                  (float)(int8_t)blk[2 + jj], part);
           acc = __builtin_fmaf(f16_bits_to_f32((uint32_t)blk[0] | ((uint32_t)blk[1] << 8)), part, acc);
         }
         store_out(y, (int64_t)sPos[rr] * N + col, acc, ydt);
@@ -355,10 +362,14 @@ __global__ __launch_bounds__(512, 1) void experts_q8_kernel(const uint8_t* __res
 
 hipError_t launch_experts_q8(const uint8_t* blocks, int64_t e, int64_t n, int64_t k, const int32_t* offsets,
                              const int32_t* perm, const int32_t* order, const float* xfac, const uint16_t* x,
-                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
+                             int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
   const int64_t grid = e * ((n + QBN - 1) / QBN);
-  experts_q8_kernel<<<(unsigned)grid, QW * 64, 0, s>>>(blocks, e, n, k, offsets, perm, order, xfac, x, x_rows,
-                                                        pos_per_row, y, ydt);
+  if (xdt == DT_F16)
+    experts_q8_kernel<true><<<(unsigned)grid, QW * 64, 0, s>>>(blocks, e, n, k, offsets, perm, order, nullptr, x,
+                                                                x_rows, pos_per_row, y, ydt);
+  else
+    experts_q8_kernel<false><<<(unsigned)grid, QW * 64, 0, s>>>(blocks, e, n, k, offsets, perm, order, xfac, x, x_rows,
+                                                                 pos_per_row, y, ydt);
   return hipGetLastError();
 }
 

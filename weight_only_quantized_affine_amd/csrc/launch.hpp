@@ -185,6 +185,9 @@ hipError_t launch_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
 hipError_t launch_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
                                 int64_t k, int64_t n, int bits, int g, uint32_t* packed, void* scales_out,
                                 void* biases_out, hipStream_t s);
+// Q4_K (block_bytes 144) or Q6_K (210) blocks [rows, k/256 * block_bytes] -> out [rows, k].
+hipError_t launch_dequant_kquant(int block_bytes, const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt,
+                                 hipStream_t s);
 hipError_t launch_dequant_q8_0(const uint8_t* blocks, int64_t rows, int64_t k, void* out, int odt, hipStream_t s);
 
 // One GEMV (desc passed by value, table == NULL) or `grid` tiles of a device problem table
@@ -269,10 +272,14 @@ hipError_t launch_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
 // computes them.
 hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_t e, int64_t n, int64_t k,
                              const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
-                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
+                             int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
 hipError_t launch_experts_q8(const uint8_t* blocks, int64_t e, int64_t n, int64_t k, const int32_t* offsets,
                              const int32_t* perm, const int32_t* order, const float* xfac, const uint16_t* x,
-                             int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
+                             int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s);
+// The Q4_K (fmt 4) / Q6_K (fmt 5) routed apply, after routing.
+hipError_t launch_experts_kq(int fmt, const uint8_t* blocks, int64_t e, int64_t n, int64_t k, const int32_t* offsets,
+                             const int32_t* perm, const int32_t* order, const uint16_t* x, int xdt, int64_t x_rows,
+                             int64_t pos_per_row, void* y, int ydt, hipStream_t s);
 hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t e, int64_t n, int64_t k,
                                 const int64_t* ids, int64_t n_pos, const void* x, int xdt, int64_t pos_per_row,
                                 void* y, int ydt, int32_t* offsets, int32_t* perm, int32_t* order, float* xfac,

@@ -206,6 +206,19 @@ ql_status qlinear_dequant(ql_format fmt, const void* w0, const void* w1, const v
     CHECK(aligned(out, 16), QL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
     return launched(ql::launch_dequant_mxfp4_blocks((const uint8_t*)w0, rows, k, out, dt(out_dtype), s), fn);
   }
+  if (fmt == QL_Q4_K || fmt == QL_Q6_K) {
+    CHECK(k % 256 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 256", fn, (long long)k);
+    CHECK(w1 == nullptr && w2 == nullptr, QL_ERR_SHAPE, "%s: w1 and w2 must be NULL for Q4_K / Q6_K", fn);
+    if (rows == 0 || k == 0) return ok();
+    CHECK(w0 && out, QL_ERR_NULL, "%s: w0 and out must not be NULL", fn);
+    CHECK(aligned(w0, fmt == QL_Q4_K ? 16 : 2), QL_ERR_ALIGN, "%s: Q4_K blocks must be 16-byte aligned, Q6_K 2-byte",
+          fn);
+    CHECK(aligned(out, 16), QL_ERR_ALIGN, "%s: out must be 16-byte aligned", fn);
+    CHECK(rows * (k / 256) * 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: weight too large", fn);
+    return launched(ql::launch_dequant_kquant(fmt == QL_Q4_K ? 144 : 210, (const uint8_t*)w0, rows, k, out,
+                                              dt(out_dtype), s),
+                    fn);
+  }
   if (fmt == QL_MXFP4 || fmt == QL_Q8_0) {
     CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
     CHECK(w2 == nullptr, QL_ERR_SHAPE, "%s: w2 must be NULL for block formats", fn);
@@ -575,14 +588,16 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
                                 int64_t pos_per_row, void* y, ql_dtype y_dtype, void* workspace, size_t ws_bytes,
                                 void* stream) {
   const char* fn = "qlinear_apply_experts";
-  CHECK(fmt == QL_MXFP4 || fmt == QL_Q8_0, QL_ERR_UNSUPPORTED, "%s: format must be QL_MXFP4 or QL_Q8_0", fn);
+  const bool kq = fmt == QL_Q4_K || fmt == QL_Q6_K;
+  CHECK(fmt == QL_MXFP4 || fmt == QL_Q8_0 || kq, QL_ERR_UNSUPPORTED,
+        "%s: format must be QL_MXFP4, QL_Q8_0, QL_Q4_K or QL_Q6_K", fn);
   CHECK(e >= 0 && e <= 4096, QL_ERR_SHAPE, "%s: e=%lld must be in [0, 4096]", fn, (long long)e);
   CHECK(n >= 0 && k >= 0 && n_pos >= 0 && n_pos < (int64_t(1) << 31), QL_ERR_SHAPE,
         "%s: n, k must be >= 0 and n_pos in [0, 2^31)", fn);
-  CHECK(k % 32 == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32", fn, (long long)k);
+  CHECK(k % (kq ? 256 : 32) == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of %d", fn, (long long)k, kq ? 256 : 32);
   CHECK(pos_per_row >= 1 && n_pos % pos_per_row == 0, QL_ERR_SHAPE,
         "%s: pos_per_row=%lld must be >= 1 and divide n_pos=%lld", fn, (long long)pos_per_row, (long long)n_pos);
-  CHECK(x_dtype == QL_BF16, QL_ERR_DTYPE, "%s: x_dtype must be QL_BF16", fn);
+  CHECK(x_dtype == QL_BF16 || x_dtype == QL_F16, QL_ERR_DTYPE, "%s: x_dtype must be QL_BF16 or QL_F16", fn);
   CHECK(is_out(y_dtype), QL_ERR_DTYPE, "%s: y_dtype must be QL_F32, QL_F16 or QL_BF16", fn);
   if (n_pos == 0 || n == 0) return ok();
   CHECK(ids && y, QL_ERR_NULL, "%s: ids and y must not be NULL", fn);
@@ -600,11 +615,14 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
     CHECK(w1 != nullptr, QL_ERR_NULL, "%s: MXFP4 scales (w1) must not be NULL", fn);
     CHECK(aligned(w0, 16), QL_ERR_ALIGN, "%s: MXFP4 codes (w0) must be 16-byte aligned", fn);
   } else {
-    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0", fn);
-    CHECK(aligned(w0, 2), QL_ERR_ALIGN, "%s: Q8_0 blocks (w0) must be 2-byte aligned", fn);
+    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0, Q4_K and Q6_K", fn);
+    CHECK(aligned(w0, fmt == QL_Q4_K ? 16 : 2), QL_ERR_ALIGN,
+          "%s: blocks (w0) must be 16-byte aligned (Q4_K) or 2-byte aligned (Q8_0, Q6_K)", fn);
   }
   // the kernel addresses x and the expert weights with 32-bit buffer offsets
-  const int64_t wbytes = fmt == QL_MXFP4 ? e * n * (k / 2) : e * n * (k / 32) * 34;
+  const int64_t wbytes = fmt == QL_MXFP4  ? e * n * (k / 2)
+                         : fmt == QL_Q8_0 ? e * n * (k / 32) * 34
+                                          : e * n * (k / 256) * (fmt == QL_Q4_K ? 144 : 210);
   CHECK((n_pos / pos_per_row) * k * 2 < (int64_t(1) << 31) && wbytes < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
         "%s: x and the expert weights must each be smaller than 2 GiB", fn);
   const size_t need = qlinear_apply_experts_workspace_size(n_pos, e);
