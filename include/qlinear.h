@@ -219,8 +219,9 @@ ql_status qlinear_gemm_grouped(const void* x, ql_dtype x_dtype, int64_t m, int64
                                void* stream);
 
 /* A list of independent GEMVs (each m <= 8) in one launch per class of (row-count template
- * 1/2/4/8, bits); bits and group_size may differ between problems (at 2, 3, 5 and 6 bits a
- * problem's k must be a positive multiple of 128, else QL_ERR_UNSUPPORTED).  `probs` is HOST memory
+ * 1/2/4/8, bits); bits and group_size may differ between problems (a problem at 2, 3, 5 or 6 bits
+ * whose k is not a positive multiple of 128 runs in a launch of its own, as qlinear_gemv runs it,
+ * with no table entry).  `probs` is HOST memory
  * (count entries), validated on the host like qlinear_gemv; the device table built from it (the
  * problems and their row tiles) is written to `workspace` (device memory of at least
  * qlinear_gemv_batched_workspace_size(probs, count) bytes, which depends on the shapes).
@@ -249,6 +250,7 @@ ql_status qlinear_route(const int64_t* ids, int64_t n_pos, int64_t e, int32_t* o
  * y[p, :] = RNE_y( x[p / pos_per_row, :] . W_{ids[p]}^T ) summed in fp32, or zeros when
  * ids[p] is not in [0, e).  A row's bits do not depend on the other positions' experts.
  *   QL_MXFP4: w0 = codes [e, n, k/2], w1 = scales [e, n, k/32].
+ *   QL_MXFP4_BLOCKS: w0 = GGUF blocks [e, n, k/32*17] (any alignment), w1 = NULL; values as QL_MXFP4.
  *   QL_Q8_0:  w0 = blocks [e, n, k/32*34], w1 = NULL.
  *   QL_Q4_K:  w0 = blocks [e, n, k/256*144] (16-byte aligned), w1 = NULL; k % 256 == 0.
  *   QL_Q6_K:  w0 = blocks [e, n, k/256*210] (2-byte aligned), w1 = NULL; k % 256 == 0.

@@ -234,11 +234,14 @@ def test_gemv_bitstream_graph_replay_matches_eager():
 def test_gemv_batched_with_bitstream_widths():
     """One problem list mixing 2, 3, 4, 5, 6 and 8 bits, 1 to 8 rows of x and every group size:
     each y against the oracle (fp32 output).  Most problems take the matrix-core kernel; those it
-    does not take (8 x rows of k = 8192, 6 x rows at g = 32) run as one bitstream class."""
+    does not take (8 x rows of k = 8192, 6 x rows at g = 32) run as one bitstream class, and those
+    whose k is not a multiple of 128 in launches of their own."""
     specs = [  # bits, m, n, k, g
         (2, 1, 300, 1024, 64), (3, 1, 1000, 3072, 64), (6, 1, 2048, 1024, 128), (5, 3, 129, 384, 32),
         (2, 8, 250, 2048, 64), (6, 2, 517, 2048, 64), (4, 1, 400, 1024, 64), (8, 1, 300, 1024, 64),
-        (3, 8, 64, 8192, 64), (2, 1, 7, 128, 32), (2, 6, 100, 1024, 32)]
+        (3, 8, 64, 8192, 64), (2, 1, 7, 128, 32), (2, 6, 100, 1024, 32),
+        # k not a multiple of 128: launches of their own, as qlinear_gemv runs them
+        (3, 1, 200, 1056, 32), (5, 4, 96, 320, 64), (6, 8, 77, 96, 32), (2, 2, 33, 160, 32)]
     probs, refs = [], []
     for i, (bits, m, n, k, g) in enumerate(specs):
         (pk, sc, bi), D = _affine_case(1500 + i, n, k, bits, g, "bf16")

@@ -118,3 +118,33 @@ def test_take_four_byte_rows_and_empty_source():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(got.cpu().numpy(), O.take(pos_np, src))
     assert np.all(got0.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("e,n,k,tokens,top,xdt", [
+    (3, 201, 288, 40, 2, "bf16"),   # 3 * 201 * 9 * 17 bytes: the blocks end inside a word
+    (4, 384, 1024, 70, 4, "bf16"),  # whole tiles of 384 rows
+    (2, 100, 4160, 20, 2, "f16"),   # long rows, fp16 x
+])
+def test_apply_experts_mxfp4_blocks(e, n, k, tokens, top, xdt):
+    """The routed apply on MXFP4 in GGUF blocks (Nx_quant Products: apply_experts takes any weight;
+    Weights, Mxfp4_blocks): against the oracle's fp64 sums of the decoded values, 1e-4 per row (the
+    values are exact in bf16, so this is fp32 accumulation only)."""
+    g = np.random.default_rng(e * 1000 + n + k)
+    blocks = g.integers(0, 256, size=(e, n, k // 32, 17)).astype(np.uint8)
+    blocks[..., 0] = g.integers(118, 131, size=(e, n, k // 32))
+    blocks = blocks.reshape(e, n, k // 32 * 17)
+    W = O.mxfp4_blocks_dequant_f32(blocks)
+    ids = g.integers(-1, e + 1, size=(tokens, top)).astype(np.int64)
+    xb = synth.acts_bits(e + n + k, tokens, k, xdt)
+    print(f"mxfp4 blocks apply_experts e={e} n={n} k={k} x={xdt}", flush=True)
+    y = q.qlinear_apply_experts(q.QL_MXFP4_BLOCKS, u8_to_dev(blocks), None, torch.from_numpy(ids.reshape(-1)).to(DEV),
+                                bits_to_dev(xb, xdt), n=n, k=k, pos_per_row=top, y_dtype=torch.float32)
+    _sync()
+    flat = ids.reshape(-1)
+    ref = O.apply_experts(W, flat, O.bits_to_f64(xdt, xb), pos_per_row=top)
+    live = (flat >= 0) & (flat < e)
+    out = y.cpu().numpy().astype(np.float64)
+    assert np.all(out[~live] == 0.0)
+    err = O.rel_l2_per_row(out[live], ref[live])
+    print(f"mxfp4 blocks experts max rel-l2 {err.max():.3e}")
+    assert err.max() <= 1e-4

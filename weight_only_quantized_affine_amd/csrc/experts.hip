@@ -12,7 +12,7 @@ namespace ql {
 namespace {
 using namespace ex_detail;
 
-enum : int { FMT_MXFP4 = 1, FMT_Q8_0 = 2, FMT_Q4_K = 4, FMT_Q6_K = 5 };  // the ql_format values
+enum : int { FMT_MXFP4 = 1, FMT_Q8_0 = 2, FMT_MXFP4_BLOCKS = 3, FMT_Q4_K = 4, FMT_Q6_K = 5 };  // ql_format values
 
 // ---------------------------------------------------------------- routing
 
@@ -165,8 +165,9 @@ hipError_t launch_apply_experts(int fmt, const void* w0, const void* w1, int64_t
   if (fmt == FMT_Q4_K || fmt == FMT_Q6_K)
     return launch_experts_kq(fmt, (const uint8_t*)w0, e, n, k, offsets, perm, order, (const uint16_t*)x, xdt, x_rows,
                              pos_per_row, y, ydt, s);
-  return launch_experts_mx((const uint8_t*)w0, (const uint8_t*)w1, e, n, k, offsets, perm, order,
-                           (const uint16_t*)x, xdt, x_rows, pos_per_row, y, ydt, s);
+  // MXFP4 with its scales apart (w1), or in GGUF blocks (w1 = NULL)
+  return launch_experts_mx((const uint8_t*)w0, fmt == FMT_MXFP4_BLOCKS ? nullptr : (const uint8_t*)w1, e, n, k,
+                           offsets, perm, order, (const uint16_t*)x, xdt, x_rows, pos_per_row, y, ydt, s);
 }
 
 }  // namespace ql

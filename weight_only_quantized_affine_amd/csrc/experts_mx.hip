@@ -1,6 +1,12 @@
 // Routed apply for MXFP4 experts (Nx_quant API docs, Products: apply_experts; Nx_quant Weights:
 // MXFP4): y[p, :] = x[p / pos_per_row, :] . W_{ids[p]}^T in fp32, the codes decoded while summing.
 // The routing (offsets, permutation and expert order) is computed by experts.hip.
+//
+// MXFP4 in GGUF's blocks (Nx_quant Weights, Mxfp4_blocks: per 32 values the scale byte, then 16
+// bytes, byte j holding value j in its low nibble and value j + 16 in its high one) takes the same
+// kernel (BLK): each lane reads the 17-byte block from the aligned 20-byte window around it,
+// takes the scale byte and regroups the nibbles into the split layout's order (byte i holding
+// values 2i and 2i + 1), then decodes as above.
 #include "experts_common.hpp"
 
 namespace ql {
@@ -24,9 +30,32 @@ constexpr int XBK = 128, XMC = 96, XCT = 3, XW = 8, XBN = XW * 16 * XCT, XNS = 3
 constexpr int XSCL_MAX = 48 * 1024;  // LDS bytes for the staged scale bytes
 
 struct MxBuf {
-  u32x4_t c[XCT];   // this lane's 32 codes (block 4 kt + q of its row), per column tile
-  uint32_t s[XCT];  // that block's scale byte (per-lane loads only)
+  u32x4_t c[XCT];   // this lane's 32 codes (block 4 kt + q of its row), per column tile; BLK: the
+                    // first 16 bytes of the aligned window holding the block
+  uint32_t s[XCT];  // that block's scale byte (per-lane loads only); BLK: the window's last word
 };
+
+// GGUF block -> split layout: from the 20-byte window w (block at byte sh, 0 <= sh < 4) the scale
+// byte and the code words of the split layout (word t: values 8t .. 8t + 7, byte i of it holding
+// values 8t + 2i and 8t + 2i + 1 in its low and high nibble).  The block's byte j (j < 16) holds
+// values j and j + 16, so words 0 and 1 gather low nibbles, words 2 and 3 high ones.
+__device__ __forceinline__ void gguf_block_to_split(const u32x4_t& w03, uint32_t w4, uint32_t sh, uint32_t& scale,
+                                                    u32x4_t& codes) {
+  const uint32_t w[5] = {w03[0], w03[1], w03[2], w03[3], w4};
+  scale = (w[0] >> (8 * sh)) & 0xffu;
+  uint32_t b[4];  // block bytes 1 .. 16 as four words
+#pragma unroll
+  for (int t = 0; t < 4; ++t) b[t] = (uint32_t)(((((uint64_t)w[t + 1]) << 32) | w[t]) >> (8 * (sh + 1)));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // nibbles of bytes 8 (t % 2) .. + 7: low ones for t < 2, high ones for t >= 2
+    const int sft = t < 2 ? 0 : 4;
+    const uint32_t n0 = (b[2 * (t & 1)] >> sft) & 0x0f0f0f0fu, n1 = (b[2 * (t & 1) + 1] >> sft) & 0x0f0f0f0fu;
+    // pairs of neighbouring nibbles into one byte: bytes 0 and 2 of (n | n >> 4)
+    const uint32_t p0 = n0 | (n0 >> 4), p1 = n1 | (n1 >> 4);
+    codes[t] = perm(p1, p0, 0x06040200u);
+  }
+}
 
 __device__ __forceinline__ f32x4_t mfma16_bf16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -119,14 +148,14 @@ __device__ __forceinline__ void split_f16(const u32x4_t& v, u32x4_t& hi, u32x4_t
 // x stage: row r holds 16 chunks of 8 values (k-tile 128), chunk c at slot c ^ (r % 16), so that the
 // 16 rows of one fragment read hit 16 distinct bank groups.  fp16 x (XF16) is staged as it is and
 // each fragment goes through the products twice, as its bf16 hi and lo parts.
-template <int MS, bool SCL_LDS, bool XF16>
+template <int MS, bool SCL_LDS, bool XF16, bool BLK>
 __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
                                          const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
                                          __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K, int64_t N,
                                          int64_t ncol0, const uint32_t* wo, const uint32_t* so, int64_t pos_per_row,
                                          void* __restrict__ y, int ydt) {
   constexpr int CPW = (MS + 1) / 2;                // x copies per wave and k-tile (32 rows per copy round)
-  constexpr int NW = SCL_LDS ? XCT : 2 * XCT;     // weight loads per lane and k-tile
+  constexpr int NW = BLK ? 5 * XCT : (SCL_LDS ? XCT : 2 * XCT);  // weight loads per lane and k-tile
   constexpr int L = NW + (XNS - 2) * (CPW + NW);  // loads issued after x(kt) when kt is due
   static_assert(L < 64, "vmcnt range");
   // the copies of a k-tile (1 KB each, at (XW i + w) KB) and the output blocks (3 KB per wave)
@@ -164,8 +193,24 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
   auto load_w = [&](int kt, MxBuf& wb) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < XCT; ++ct) {
-      wb.c[ct] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsW, wo[ct], (uint32_t)(kt * 64), 0));
-      if constexpr (!SCL_LDS) wb.s[ct] = __builtin_amdgcn_raw_buffer_load_b8(rsS, so[ct], (uint32_t)(kt * 4), 0);
+      if constexpr (BLK) {
+        // the aligned 20-byte window of block 4 kt + q (4 blocks = 68 bytes per k-tile, so the block's
+        // place in its window is the same on every tile): wo = window offset in tile 0, so = place;
+        // the word that the end of all blocks cuts is rebuilt from bytes (sScl holds it, see below)
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          const uint32_t a = wo[ct] + (uint32_t)(kt * 68) + 4u * i;
+          uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rsW, a, 0, 0);
+          if (a == *(const uint32_t*)sScl) v = *(const uint32_t*)(sScl + 4);
+          if (i < 4)
+            wb.c[ct][i] = v;
+          else
+            wb.s[ct] = v;
+        }
+      } else {
+        wb.c[ct] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsW, wo[ct], (uint32_t)(kt * 64), 0));
+        if constexpr (!SCL_LDS) wb.s[ct] = __builtin_amdgcn_raw_buffer_load_b8(rsS, so[ct], (uint32_t)(kt * 4), 0);
+      }
     }
   };
 
@@ -181,13 +226,17 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     // the block scale 2^(s-127) as fp32 (s = 0: the subnormal 2^-127), NaN for s = 255, 0 past K
     const bool kin = kt * XBK + 32 * q < kint;
     float scl[XCT];
+    u32x4_t cw[XCT];
 #pragma unroll
     for (int ct = 0; ct < XCT; ++ct) {
       uint32_t sb;
-      if constexpr (SCL_LDS)
+      if constexpr (BLK)
+        gguf_block_to_split(wb.c[ct], wb.s[ct], so[ct], sb, cw[ct]);
+      else if constexpr (SCL_LDS)
         sb = sScl[so[ct] + 4 * kt];
       else
         sb = wb.s[ct] & 0xffu;
+      if constexpr (!BLK) cw[ct] = wb.c[ct];
       scl[ct] = !kin ? 0.0f : __uint_as_float(sb == 255u ? 0x7fc00000u : (sb == 0u ? 0x00400000u : sb << 23));
     }
 #pragma unroll
@@ -201,7 +250,7 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
       }
 #pragma unroll
       for (int ct = 0; ct < XCT; ++ct) {
-        const u32x4_t bf = decode_mxfp4(wb.c[ct][t], scl[ct]);
+        const u32x4_t bf = decode_mxfp4(cw[ct][t], scl[ct]);
 #pragma unroll
         for (int rt = 0; rt < MS; ++rt) {
           acc[ct][rt] = mfma16_bf16(af[rt], bf, acc[ct][rt]);
@@ -255,7 +304,7 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     mx_store<MS, 2>(acc, sPos, rows, stg, N, ncol0, y, DT_F16);
 }
 
-template <bool SCL_LDS, bool XF16>
+template <bool SCL_LDS, bool XF16, bool BLK>
 __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
                                           const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
                                           __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K,
@@ -264,7 +313,8 @@ __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int 
   switch ((rows + 15) >> 4) {
 #define QL_MX_CASE(ms)                                                                                             \
   case ms:                                                                                                         \
-    mx_chunk<ms, SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);    \
+    mx_chunk<ms, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y,   \
+                                     ydt);                                                                         \
     break;
     QL_MX_CASE(1)
     QL_MX_CASE(2)
@@ -272,13 +322,13 @@ __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int 
     QL_MX_CASE(4)
     QL_MX_CASE(5)
     default:
-      mx_chunk<6, SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+      mx_chunk<6, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
       break;
 #undef QL_MX_CASE
   }
 }
 
-template <bool SCL_LDS, bool XF16>
+template <bool SCL_LDS, bool XF16, bool BLK>
 __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales, int64_t e, int64_t N,
                                                             int64_t K, const int32_t* __restrict__ offsets,
@@ -305,8 +355,9 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
   if (cnt <= 0) return;
 
   const __amdgpu_buffer_rsrc_t rsX = ex_rsrc(x, x_rows * K * 2);
-  const __amdgpu_buffer_rsrc_t rsW = ex_rsrc(codes, e * N * (K / 2));
-  const __amdgpu_buffer_rsrc_t rsS = ex_rsrc(scales, e * N * (K / 32));
+  const int64_t wtotal = BLK ? e * N * (K / 32) * 17 : e * N * (K / 2);
+  const __amdgpu_buffer_rsrc_t rsW = ex_rsrc(codes, wtotal);
+  const __amdgpu_buffer_rsrc_t rsS = ex_rsrc(scales, BLK ? 0 : e * N * (K / 32));
   // this lane's weight rows of the expert, one per column tile (ncol0 + 16 ct; past N the last row
   // stands in): byte offsets of its 16 code bytes in the first k-tile, and of its block's scale
   // byte (in the staged LDS copy, or in the scales array)
@@ -317,9 +368,28 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
 #pragma unroll
   for (int ct = 0; ct < XCT; ++ct) {
     const int64_t wrow = ex * N + min(ncol0 + 16 * ct, N - 1);
-    wo[ct] = (uint32_t)(wrow * (K / 2) + 16 * (lane >> 4));
-    so[ct] = SCL_LDS ? (uint32_t)(ssh + (wrow - ex * N - nt * XBN) * (K / 32) + (lane >> 4))
-                     : (uint32_t)(wrow * (K / 32) + (lane >> 4));
+    if constexpr (BLK) {  // the aligned window of block q of the row, and the block's place in it
+      const int64_t o = wrow * (K / 32) * 17 + 17 * (lane >> 4);
+      wo[ct] = (uint32_t)(o & ~(int64_t)3);
+      so[ct] = (uint32_t)(o & 3);
+    } else {
+      wo[ct] = (uint32_t)(wrow * (K / 2) + 16 * (lane >> 4));
+      so[ct] = SCL_LDS ? (uint32_t)(ssh + (wrow - ex * N - nt * XBN) * (K / 32) + (lane >> 4))
+                       : (uint32_t)(wrow * (K / 32) + (lane >> 4));
+    }
+  }
+  if constexpr (BLK) {
+    // the word that the end of all blocks cuts (a word load past the end reads zero): its offset
+    // and its bytes, for load_w; 0xffffffff when the blocks end on a word boundary
+    if (tid == 0) {
+      uint32_t a = 0xffffffffu, w = 0u;
+      if (wtotal & 3) {
+        a = (uint32_t)(wtotal & ~(int64_t)3);
+        for (int i = 0; i < (int)(wtotal & 3); ++i) w |= __builtin_amdgcn_raw_buffer_load_b8(rsW, a + i, 0, 0) << (8 * i);
+      }
+      sScl32[0] = a;
+      sScl32[1] = w;
+    }
   }
   if constexpr (SCL_LDS) {
     // rows of the tile that exist, K/32 bytes each, from the aligned word at or below the first
@@ -334,7 +404,7 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
     __syncthreads();  // previous chunk's readers of sPos are done (and the scale bytes are staged)
     if (tid < XMC) sPos[tid] = tid < rows ? perm_pos[off + mc + tid] : -1;
     __syncthreads();
-    mx_chunks<SCL_LDS, XF16>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+    mx_chunks<SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
   }
 }
 
@@ -345,18 +415,24 @@ hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_
                              int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
   const unsigned grid = (unsigned)(e * ((n + XBN - 1) / XBN));
   const size_t scl = (size_t)((3 + XBN * (k / 32) + 3) / 4 * 4);
-  const bool in_lds = scl <= (size_t)XSCL_MAX;
-#define QL_MX_LAUNCH(L, H)                                                                                          \
-  experts_mx_kernel<L, H><<<grid, XW * 64, L ? scl : 0, s>>>(codes, scales, e, n, k, offsets, perm, order, x, x_rows, \
-                                                             pos_per_row, y, ydt)
-  if (in_lds && xdt == DT_F16)
-    QL_MX_LAUNCH(true, true);
+  const bool blk = scales == nullptr;  // GGUF blocks: codes holds the 17-byte blocks
+  const bool in_lds = !blk && scl <= (size_t)XSCL_MAX;
+  const bool h = xdt == DT_F16;
+#define QL_MX_LAUNCH(L, H, B)                                                                                       \
+  experts_mx_kernel<L, H, B><<<grid, XW * 64, L ? scl : (B ? 8 : 0), s>>>(codes, scales, e, n, k, offsets, perm,    \
+                                                                          order, x, x_rows, pos_per_row, y, ydt)
+  if (blk && h)
+    QL_MX_LAUNCH(false, true, true);
+  else if (blk)
+    QL_MX_LAUNCH(false, false, true);
+  else if (in_lds && h)
+    QL_MX_LAUNCH(true, true, false);
   else if (in_lds)
-    QL_MX_LAUNCH(true, false);
-  else if (xdt == DT_F16)
-    QL_MX_LAUNCH(false, true);
+    QL_MX_LAUNCH(true, false, false);
+  else if (h)
+    QL_MX_LAUNCH(false, true, false);
   else
-    QL_MX_LAUNCH(false, false);
+    QL_MX_LAUNCH(false, false, false);
 #undef QL_MX_LAUNCH
   return hipGetLastError();
 }

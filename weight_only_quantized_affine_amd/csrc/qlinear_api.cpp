@@ -406,13 +406,21 @@ struct BatchedPlan {
     size_t first_tile, n_tiles, lds;
   };
   std::vector<Cls> classes;
+  // problems at 2, 3, 5 or 6 bits whose k is not a positive multiple of 128: one launch each, by the
+  // kernel qlinear_gemv takes for them (they need no table)
+  std::vector<int> singles;
   size_t tiles_offset = 0, bytes = 0;
 };
 
 void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
   std::vector<int> order;
-  for (int i = 0; i < count; ++i)
-    if (probs[i].m > 0 && probs[i].n > 0) order.push_back(i);
+  for (int i = 0; i < count; ++i) {
+    if (probs[i].m <= 0 || probs[i].n <= 0) continue;
+    if (ql::is_stream_bits(probs[i].bits) && (probs[i].k <= 0 || probs[i].k % 128 != 0))
+      plan.singles.push_back(i);
+    else
+      order.push_back(i);
+  }
   auto mf = [&](int i) {
     return ql::gemv_mf_eligible(probs[i].m, probs[i].k, probs[i].bits, probs[i].group_size, probs[i].scales,
                                 probs[i].biases);
@@ -525,21 +533,38 @@ ql_status qlinear_gemv_batched(const ql_problem* probs, int count, ql_dtype x_dt
     if (st != QL_OK) return st;
     CHECK(p.m <= 8, QL_ERR_UNSUPPORTED, "%s: problem %d has m=%lld > 8 (use qlinear_gemv or qlinear_gemm)", fn, i,
           (long long)p.m);
-    CHECK(!ql::is_stream_bits(p.bits) || (p.k > 0 && p.k % 128 == 0), QL_ERR_UNSUPPORTED,
-          "%s: problem %d has bits=%d and k=%lld (lists take 2, 3, 5 and 6 bits when k is a positive multiple "
-          "of 128; use qlinear_gemv)", fn, i, p.bits, (long long)p.k);
     CHECK(p.n * p.k * p.bits / 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
           "%s: problem %d has packed weights of 2 GiB or more", fn, i);
   }
   BatchedPlan plan;
   make_plan(probs, count, plan);
+  hipStream_t s = (hipStream_t)stream;
+  for (int i : plan.singles) {
+    const ql_problem& p = probs[i];
+    ql::GemvStreamArgs a{};
+    a.x = p.x;
+    a.m = (int)p.m;
+    a.k = p.k;
+    a.packed = p.packed;
+    a.scales = p.scales;
+    a.biases = p.biases;
+    a.n = p.n;
+    a.g = p.group_size;
+    a.layer_bias = p.layer_bias;
+    a.y = p.y;
+    a.ydt = dt(y_dtype);
+    a.bits = p.bits;
+    a.xdt = dt(x_dtype);
+    a.pdt = dt(param_dtype);
+    const hipError_t e = ql::launch_gemv_stream(a, s);
+    if (e != hipSuccess) return launched(e, fn);
+  }
   if (plan.descs.empty()) return ok();
   CHECK(workspace != nullptr, QL_ERR_WORKSPACE, "%s: workspace must not be NULL (%zu bytes needed)", fn, plan.bytes);
   CHECK(ws_bytes >= plan.bytes, QL_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
         ws_bytes, plan.bytes);
   CHECK(aligned(workspace, 16), QL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
   uint8_t* ws = (uint8_t*)workspace;
-  hipStream_t s = (hipStream_t)stream;
   if (upload) {
     std::vector<uint8_t> host(plan.bytes);
     memcpy(host.data(), plan.descs.data(), plan.descs.size() * sizeof(ql::GemvDesc));
@@ -589,8 +614,8 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
                                 void* stream) {
   const char* fn = "qlinear_apply_experts";
   const bool kq = fmt == QL_Q4_K || fmt == QL_Q6_K;
-  CHECK(fmt == QL_MXFP4 || fmt == QL_Q8_0 || kq, QL_ERR_UNSUPPORTED,
-        "%s: format must be QL_MXFP4, QL_Q8_0, QL_Q4_K or QL_Q6_K", fn);
+  CHECK(fmt == QL_MXFP4 || fmt == QL_Q8_0 || fmt == QL_MXFP4_BLOCKS || kq, QL_ERR_UNSUPPORTED,
+        "%s: format must be QL_MXFP4, QL_MXFP4_BLOCKS, QL_Q8_0, QL_Q4_K or QL_Q6_K", fn);
   CHECK(e >= 0 && e <= 4096, QL_ERR_SHAPE, "%s: e=%lld must be in [0, 4096]", fn, (long long)e);
   CHECK(n >= 0 && k >= 0 && n_pos >= 0 && n_pos < (int64_t(1) << 31), QL_ERR_SHAPE,
         "%s: n, k must be >= 0 and n_pos in [0, 2^31)", fn);
@@ -615,14 +640,15 @@ ql_status qlinear_apply_experts(ql_format fmt, const void* w0, const void* w1, i
     CHECK(w1 != nullptr, QL_ERR_NULL, "%s: MXFP4 scales (w1) must not be NULL", fn);
     CHECK(aligned(w0, 16), QL_ERR_ALIGN, "%s: MXFP4 codes (w0) must be 16-byte aligned", fn);
   } else {
-    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for Q8_0, Q4_K and Q6_K", fn);
-    CHECK(aligned(w0, fmt == QL_Q4_K ? 16 : 2), QL_ERR_ALIGN,
+    CHECK(w1 == nullptr, QL_ERR_SHAPE, "%s: w1 must be NULL for block formats", fn);
+    CHECK(aligned(w0, fmt == QL_Q4_K ? 16 : (fmt == QL_MXFP4_BLOCKS ? 1 : 2)), QL_ERR_ALIGN,
           "%s: blocks (w0) must be 16-byte aligned (Q4_K) or 2-byte aligned (Q8_0, Q6_K)", fn);
   }
   // the kernel addresses x and the expert weights with 32-bit buffer offsets
-  const int64_t wbytes = fmt == QL_MXFP4  ? e * n * (k / 2)
-                         : fmt == QL_Q8_0 ? e * n * (k / 32) * 34
-                                          : e * n * (k / 256) * (fmt == QL_Q4_K ? 144 : 210);
+  const int64_t wbytes = fmt == QL_MXFP4          ? e * n * (k / 2)
+                         : fmt == QL_MXFP4_BLOCKS ? e * n * (k / 32) * 17
+                         : fmt == QL_Q8_0         ? e * n * (k / 32) * 34
+                                                  : e * n * (k / 256) * (fmt == QL_Q4_K ? 144 : 210);
   CHECK((n_pos / pos_per_row) * k * 2 < (int64_t(1) << 31) && wbytes < (int64_t(1) << 31), QL_ERR_UNSUPPORTED,
         "%s: x and the expert weights must each be smaller than 2 GiB", fn);
   const size_t need = qlinear_apply_experts_workspace_size(n_pos, e);
