@@ -10,7 +10,8 @@ import weight_only_quantized_affine_amd as q
 from gpu_helpers import DEV, TDT, bits_to_dev, out_f64, u32_to_dev
 
 pytestmark = pytest.mark.gpu
-TOL = 2e-3
+TOL = 2e-3  # the products' bound (relative l2 per row): 16-bit outputs
+GEMM_TOL = 1e-3  # fp32 outputs: one fp16 rounding per weight, ~2^-11/sqrt(3) per row (2.7e-4 worst measured)
 
 
 def _weight(seed, n, k, bits, g, pdt):
@@ -53,7 +54,7 @@ def test_gemm_grouped_ragged(m, ns, k, bits, g, xdt, pdt, ydt):
             ref = O.bits_to_f64(ydt, O.to_bits(ydt, ref.astype(np.float32)))
         err = O.rel_l2_per_row(got[rows], ref)
         print(f"weight {j} (n={w['packed'].shape[0]}): max rel-l2 {err.max():.3e}")
-        assert err.max() <= TOL
+        assert err.max() <= (GEMM_TOL if ydt == "f32" else TOL)
 
 
 def test_gemm_grouped_9b_qkv_matches_single_calls_and_oracle():
@@ -82,7 +83,7 @@ def test_gemm_grouped_9b_qkv_matches_single_calls_and_oracle():
         D = O.affine_dequant_f32(opk, osb, obb, 4, 64, "bf16", k)
         err = O.rel_l2_per_row(out_f64(w["y"])[rows], O.apply(xf, D))
         print(f"{'qkv'[j]}: max rel-l2 over whole rows {err.max():.3e}")
-        assert err.max() <= TOL
+        assert err.max() <= GEMM_TOL
 
 
 def test_gemm_grouped_small_shapes_fall_back_to_single_calls():
