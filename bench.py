@@ -630,12 +630,25 @@ def cpu_baseline(min_seconds: float = 8.0):
     import oracle as O
     import synth
 
+    threads, blas = 1, "unknown"
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({os.path.basename(i.get('filepath', ''))})"
+                         for i in info) or "unknown"
     except Exception:  # noqa: BLE001
-        threads = 1
+        threadpool_limits = None
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     log("cpu baseline: oracle over whole decode steps")
     g = np.random.default_rng(990)
     prepared = []
@@ -646,21 +659,33 @@ def cpu_baseline(min_seconds: float = 8.0):
         xb = O.bits_to_f64("bf16", synth.acts_bits(991, 1, k, "bf16"))
         prepared.append((pk, sb, bb, xb, k))
     wbytes = sum(pk.nbytes + sb.nbytes + bb.nbytes for (pk, sb, bb, _, _) in prepared)
-    passes = 0
-    t0 = time.perf_counter()
-    while True:
-        for (pk, sb, bb, x, k) in prepared:
-            D = O.affine_dequant_f32(pk, sb, bb, 4, 64, "bf16", k)
-            O.apply(x, D)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= 5:
-            break
+
+    def timed(limit_s):
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            for (pk, sb, bb, x, k) in prepared:
+                D = O.affine_dequant_f32(pk, sb, bb, 4, 64, "bf16", k)
+                O.apply(x, D)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= limit_s or passes >= 5:
+                return passes, dt
+
+    passes, dt = timed(min_seconds)
+    one = None
+    if threadpool_limits is not None:
+        log("cpu baseline: the same on one BLAS thread")
+        with threadpool_limits(limits=1, user_api="blas"):
+            p1, d1 = timed(min_seconds / 2)
+        one = {"value": round(wbytes * p1 / d1 / 1e9, 4), "unit": "GB/s", "cores": 1, "seconds": round(d1, 2),
+               "passes": p1}
     return {"value": round(wbytes * passes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{passes} whole decode step(s) of the qwen3-0.6b-shaped workload (197 projections, "
                       f"{wbytes} weight bytes each, batch 1, 4-bit g64 bf16, synthetic packed words) in {dt:.2f} s: "
                       f"unpack + fp64 dequant (single-threaded NumPy) + matmul ({threads} BLAS threads)",
-            "seconds": round(dt, 2), "tokens_per_s": round(passes / dt, 3)}
+            "seconds": round(dt, 2), "tokens_per_s": round(passes / dt, 3), "one_thread": one,
+            "cpu_model": cpu_model, "host_threads": os.cpu_count(), "blas": blas}
 
 
 if __name__ == "__main__":

@@ -13,12 +13,13 @@
 // weight value enters exactly; the result differs from a sum of the decoded fp32 values only by
 // fp32 rounding.
 //
-// One workgroup of 4 waves per (expert, 128 weight rows), in decreasing order of the experts'
+// One workgroup of 8 waves per (expert, 256 weight rows), in decreasing order of the experts'
 // position counts; wave w owns two column tiles of 16 rows and all of the chunk's positions (up to
-// 64: MS m-subtiles of 16).  Per 256-value block of k: the chunk's x rows are staged in LDS
-// (16-byte chunk c of row r at slot c ^ (r % 16), so that the 16 rows of one operand read hit 16
-// distinct bank groups), the sub-block sums are formed from them, and each lane reads its row's
-// block bytes from global memory (issued before the x staging, so the two overlap).
+// 64: MS m-subtiles of 16).  Per 256-value block of k: the chunk's x rows go HBM -> LDS by DMA into
+// one of two buffers (16-byte chunk c of row r at slot c ^ (r % 16), so that the 16 rows of one
+// operand read hit 16 distinct bank groups), the sub-block sums are formed from them, and each lane
+// reads its rows' block bytes into registers.  The x copies and weight loads of block kb + 1 are
+// issued before block kb's sums and products, so they are in flight while those run.
 #include "experts_common.hpp"
 
 namespace ql {
@@ -27,7 +28,8 @@ using namespace ex_detail;
 
 constexpr int KQ_MC = 64;                 // positions per chunk
 constexpr int KQ_CT = 2;                  // column tiles of 16 rows per wave
-constexpr int KQ_BN = 4 * 16 * KQ_CT;     // weight rows per workgroup
+constexpr int KQ_W = 8;                   // waves per workgroup
+constexpr int KQ_BN = KQ_W * 16 * KQ_CT;  // weight rows per workgroup
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
@@ -152,13 +154,13 @@ template <> struct KQ<5> {  // Q6_K
 };
 
 template <int FMT, typename XT, int MS>
-__device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int rows, uint8_t* __restrict__ sx,
-                                         float* __restrict__ sxs, __amdgpu_buffer_rsrc_t rsX,
-                                         __amdgpu_buffer_rsrc_t rsW, int64_t K, int64_t N, int64_t ncol0,
-                                         const uint32_t* wrow_off, int64_t pos_per_row, void* __restrict__ y,
-                                         int ydt) {
+__device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int rows, uint8_t* sx0, uint8_t* sx1,
+                                         float* sxs0, float* sxs1, __amdgpu_buffer_rsrc_t rsX, __amdgpu_buffer_rsrc_t rsW,
+                                         int64_t K, int64_t N, int64_t ncol0, const uint32_t* wrow_off,
+                                         int64_t pos_per_row, void* __restrict__ y, int ydt) {
   using F = KQ<FMT>;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int j16 = lane & 15, q = lane >> 4;
   const int KB = (int)(K / 256);
   f32x4_t acc[KQ_CT][MS];
@@ -167,35 +169,54 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
 #pragma unroll
     for (int rt = 0; rt < MS; ++rt) acc[ct][rt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int kb = 0; kb < KB; ++kb) {
-    typename F::Lane L[KQ_CT];
+  // x copies: 16 MS rows x 32 chunks, two rows per wave instruction (1 KB): instruction i of wave w
+  // covers rows 2 (KQ_W i + w) and the next; lane l -> row + l / 32, slot l % 32 (chunk (l % 32) ^
+  // (row % 16)).  Rows past the chunk read zeros.
+  constexpr int CPW = (16 * MS / 2 + KQ_W - 1) / KQ_W;
+  uint32_t xoff[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int r = 2 * (KQ_W * i + wave) + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 15);
+    xoff[i] = r < rows ? (uint32_t)((((int64_t)sPos[r] / pos_per_row) * K + 8 * c) * 2) : kExOOB;
+  }
+  auto copy_x = [&](int kb, uint8_t* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i)
+      if (2 * (KQ_W * i + wave_u) < 16 * MS)  // uniform
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsX, (lds_void*)(buf + (KQ_W * i + wave_u) * 1024), 16,
+                                                 xoff[i] == kExOOB ? kExOOB : xoff[i] + (uint32_t)(kb * 512), 0, 0,
+                                                 0);
+  };
+  auto load_w = [&](int kb, typename F::Lane* L) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < KQ_CT; ++ct) F::load(rsW, wrow_off[ct] + (uint32_t)(kb * F::kBytes), q, L[ct]);
-    __syncthreads();  // every wave is done with the previous block's x and sums
-    // x: 16 * MS rows x 32 chunks of 8 values; rows past the chunk read zeros
-    for (int t = tid; t < 16 * MS * 32; t += 256) {
-      const int r = t >> 5, c = t & 31;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (r < rows) {
-        const int64_t xr = sPos[r] / pos_per_row;
-        v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rsX, (uint32_t)((xr * K + (int64_t)kb * 256 + 8 * c) * 2), 0, 0));
-      }
-      *(u32x4_t*)(sx + (r * 32 + (c ^ (r & 15))) * 16) = v;
+  };
+
+  typename F::Lane Lc[KQ_CT], Ln[KQ_CT];
+  copy_x(0, sx0);
+  load_w(0, Lc);
+  for (int kb = 0; kb < KB; ++kb) {
+    uint8_t* const cur = (kb & 1) ? sx1 : sx0;
+    float* const sum = (kb & 1) ? sxs1 : sxs0;
+    ex_wait_vmcnt<0>();  // block kb's x copies and weights have landed
+    __syncthreads();     // ... for every wave, and every wave is done with block kb - 1's buffers
+    if (kb + 1 < KB) {   // uniform
+      copy_x(kb + 1, (kb & 1) ? sx0 : sx1);
+      load_w(kb + 1, Ln);
     }
-    __syncthreads();
     // sub-block sums of x: (row, sub-block) pairs
-    for (int t = tid; t < 16 * MS * F::kSub; t += 256) {
+    for (int t = tid; t < 16 * MS * F::kSub; t += KQ_W * 64) {
       const int r = t / F::kSub, j = t - r * F::kSub;
-      float sum = 0.0f;
+      float acc_s = 0.0f;
 #pragma unroll
       for (int c8 = 0; c8 < F::kSubLen / 8; ++c8) {
         const int c = j * (F::kSubLen / 8) + c8;
-        const u32x4_t v = *(const u32x4_t*)(sx + (r * 32 + (c ^ (r & 15))) * 16);
+        const u32x4_t v = *(const u32x4_t*)(cur + (r * 32 + (c ^ (r & 15))) * 16);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sum += KqOp<XT>::lo(v[e]) + KqOp<XT>::hi(v[e]);
+        for (int e = 0; e < 4; ++e) acc_s += KqOp<XT>::lo(v[e]) + KqOp<XT>::hi(v[e]);
       }
-      sxs[r * 16 + j] = sum;
+      sum[r * 16 + j] = acc_s;
     }
     __syncthreads();
 #pragma unroll
@@ -204,26 +225,26 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
 #pragma unroll
       for (int ct = 0; ct < KQ_CT; ++ct) {
         float b;
-        F::params(L[ct], j, s[ct], b);
+        F::params(Lc[ct], j, s[ct], b);
         bb[ct] = b - F::kOff * s[ct];
       }
 #pragma unroll
       for (int rt = 0; rt < MS; ++rt) {
         const int r = rt * 16 + j16;
         // this lane's accumulator rows 4q .. 4q + 3 of the m-subtile: their sub-block sums
-        const f32x4_t X = f32x4_t{sxs[(rt * 16 + 4 * q) * 16 + j], sxs[(rt * 16 + 4 * q + 1) * 16 + j],
-                                  sxs[(rt * 16 + 4 * q + 2) * 16 + j], sxs[(rt * 16 + 4 * q + 3) * 16 + j]};
+        const f32x4_t X = f32x4_t{sum[(rt * 16 + 4 * q) * 16 + j], sum[(rt * 16 + 4 * q + 1) * 16 + j],
+                                  sum[(rt * 16 + 4 * q + 2) * 16 + j], sum[(rt * 16 + 4 * q + 3) * 16 + j]};
         f32x4_t D[KQ_CT];
         if constexpr (FMT == 4) {
           const int c = 4 * j + q;  // values 32 j + 8 q .. + 7
-          const u32x4_t a = *(const u32x4_t*)(sx + (r * 32 + (c ^ (r & 15))) * 16);
+          const u32x4_t a = *(const u32x4_t*)(cur + (r * 32 + (c ^ (r & 15))) * 16);
 #pragma unroll
-          for (int ct = 0; ct < KQ_CT; ++ct) D[ct] = KqOp<XT>::k32(a, F::template codes<XT>(L[ct], j));
+          for (int ct = 0; ct < KQ_CT; ++ct) D[ct] = KqOp<XT>::k32(a, F::template codes<XT>(Lc[ct], j));
         } else {
           const int c = 2 * j + (q >> 1);  // values 16 j + 4 q .. + 3: half (q & 1) of chunk c
-          const u32x2_t a = *(const u32x2_t*)(sx + (r * 32 + (c ^ (r & 15))) * 16 + 8 * (q & 1));
+          const u32x2_t a = *(const u32x2_t*)(cur + (r * 32 + (c ^ (r & 15))) * 16 + 8 * (q & 1));
 #pragma unroll
-          for (int ct = 0; ct < KQ_CT; ++ct) D[ct] = KqOp<XT>::k16(a, F::template codes<XT>(L[ct], j));
+          for (int ct = 0; ct < KQ_CT; ++ct) D[ct] = KqOp<XT>::k16(a, F::template codes<XT>(Lc[ct], j));
         }
 #pragma unroll
         for (int ct = 0; ct < KQ_CT; ++ct)
@@ -232,6 +253,8 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
             acc[ct][rt][e] = __builtin_fmaf(s[ct], D[ct][e], __builtin_fmaf(bb[ct], X[e], acc[ct][rt][e]));
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < KQ_CT; ++ct) Lc[ct] = Ln[ct];
   }
   // outputs: lane holds column ncol0 + 16 ct for positions rt * 16 + 4q + e
 #pragma unroll
@@ -257,14 +280,17 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
 }
 
 template <int FMT, typename XT>
-__global__ __launch_bounds__(256) void experts_kq_kernel(const uint8_t* __restrict__ blocks, int64_t e, int64_t N,
-                                                         int64_t K, const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ perm_pos,
-                                                         const int32_t* __restrict__ order,
-                                                         const uint16_t* __restrict__ x, int64_t x_rows,
-                                                         int64_t pos_per_row, void* __restrict__ y, int ydt) {
-  __shared__ __attribute__((aligned(16))) uint8_t sx[KQ_MC * 256 * 2];
-  __shared__ float sxs[KQ_MC * 16];
+__global__ __launch_bounds__(KQ_W * 64, 2) void experts_kq_kernel(const uint8_t* __restrict__ blocks, int64_t e,
+                                                                  int64_t N, int64_t K,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  const int32_t* __restrict__ perm_pos,
+                                                                  const int32_t* __restrict__ order,
+                                                                  const uint16_t* __restrict__ x, int64_t x_rows,
+                                                                  int64_t pos_per_row, void* __restrict__ y, int ydt) {
+  // two x buffers and two tables of sub-block sums (blocks kb and kb + 1)
+  __shared__ __attribute__((aligned(16))) uint8_t sx0[KQ_MC * 256 * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t sx1[KQ_MC * 256 * 2];
+  __shared__ float sxs0[KQ_MC * 16], sxs1[KQ_MC * 16];
   __shared__ int32_t sPos[KQ_MC];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t n_tiles = (N + KQ_BN - 1) / KQ_BN;
@@ -287,14 +313,14 @@ __global__ __launch_bounds__(256) void experts_kq_kernel(const uint8_t* __restri
 
   for (int32_t mc = 0; mc < cnt; mc += KQ_MC) {
     const int rows = min(KQ_MC, cnt - mc);
-    __syncthreads();  // the previous chunk's readers of sPos are done
+    __syncthreads();  // the previous chunk's readers of sPos and of the buffers are done
     if (tid < KQ_MC) sPos[tid] = tid < rows ? perm_pos[off + mc + tid] : 0;
     __syncthreads();
     switch ((rows + 15) >> 4) {
-      case 1: kq_chunk<FMT, XT, 1>(sPos, rows, sx, sxs, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
-      case 2: kq_chunk<FMT, XT, 2>(sPos, rows, sx, sxs, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
-      case 3: kq_chunk<FMT, XT, 3>(sPos, rows, sx, sxs, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
-      default: kq_chunk<FMT, XT, 4>(sPos, rows, sx, sxs, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
+      case 1: kq_chunk<FMT, XT, 1>(sPos, rows, sx0, sx1, sxs0, sxs1, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
+      case 2: kq_chunk<FMT, XT, 2>(sPos, rows, sx0, sx1, sxs0, sxs1, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
+      case 3: kq_chunk<FMT, XT, 3>(sPos, rows, sx0, sx1, sxs0, sxs1, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
+      default: kq_chunk<FMT, XT, 4>(sPos, rows, sx0, sx1, sxs0, sxs1, rsX, rsW, K, N, ncol0, wrow_off, pos_per_row, y, ydt); break;
     }
   }
 }
@@ -306,7 +332,8 @@ hipError_t launch_experts_kq(int fmt, const uint8_t* blocks, int64_t e, int64_t 
                              int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
   const unsigned grid = (unsigned)(e * ((n + KQ_BN - 1) / KQ_BN));
 #define QL_KQ_LAUNCH(F, XT)                                                                                         \
-  experts_kq_kernel<F, XT><<<grid, 256, 0, s>>>(blocks, e, n, k, offsets, perm, order, x, x_rows, pos_per_row, y, ydt)
+  experts_kq_kernel<F, XT><<<grid, KQ_W * 64, 0, s>>>(blocks, e, n, k, offsets, perm, order, x, x_rows, pos_per_row, y, \
+                                                       ydt)
   if (fmt == 4 && xdt == DT_F16)
     QL_KQ_LAUNCH(4, F16);
   else if (fmt == 4)

@@ -26,8 +26,17 @@ using namespace ex_detail;
 // ring of XNS register buffers, XNS k-tiles ahead (one in-order counter, as in experts_kernel).
 // The workgroup's scale bytes (all k) are read once into LDS, coalesced, when they fit
 // (SCL_LDS); otherwise each lane loads its block's byte with its codes.
-constexpr int XBK = 128, XMC = 96, XCT = 3, XW = 8, XBN = XW * 16 * XCT, XNS = 3;
-constexpr int XSCL_MAX = 48 * 1024;  // LDS bytes for the staged scale bytes
+#ifndef EXPERTS_MX_MC
+#define EXPERTS_MX_MC 96  // positions per chunk (a multiple of 16, at most 96)
+#endif
+#ifndef EXPERTS_MX_SCL_MAX
+#define EXPERTS_MX_SCL_MAX (48 * 1024)  // LDS bytes for the staged scale bytes
+#endif
+#ifndef EXPERTS_MX_MINB
+#define EXPERTS_MX_MINB 1  // workgroups per compute unit the register allocation must allow
+#endif
+constexpr int XBK = 128, XMC = EXPERTS_MX_MC, XCT = 3, XW = 8, XBN = XW * 16 * XCT, XNS = 3;
+constexpr int XSCL_MAX = EXPERTS_MX_SCL_MAX;
 
 struct MxBuf {
   u32x4_t c[XCT];   // this lane's 32 codes (block 4 kt + q of its row), per column tile; BLK: the
@@ -77,7 +86,9 @@ __device__ __forceinline__ void mx_store(const f32x4_t (&acc)[XCT][MS], const in
     return (uint32_t)(ydt == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
   };
   if (N % 8 == 0 && ((uintptr_t)y & 15) == 0) {
-    uint8_t* wbuf = stg[0] + wave * 3072;
+    // 3 KB per wave: in stage 0, and in stage 1 for the waves that stage 0 cannot hold
+    constexpr int kStageBytes = XMC * XBK * 2, kFit = kStageBytes / 3072;
+    uint8_t* wbuf = wave < kFit ? stg[0] + wave * 3072 : stg[1] + (wave - kFit) * 3072;
     constexpr int rb = 48 * ESZ;          // bytes of a staged row
     constexpr int nch = 16 * rb / 16;     // 16-byte chunks of a block: 96 or 192
     const int64_t col0 = ncol0 - j16;     // the wave's first column
@@ -158,10 +169,10 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
   constexpr int NW = BLK ? 5 * XCT : (SCL_LDS ? XCT : 2 * XCT);  // weight loads per lane and k-tile
   constexpr int L = NW + (XNS - 2) * (CPW + NW);  // loads issued after x(kt) when kt is due
   static_assert(L < 64, "vmcnt range");
-  // the copies of a k-tile (1 KB each, at (XW i + w) KB) and the output blocks (3 KB per wave)
-  // stay inside one stage
+  // the copies of a k-tile (1 KB each, at (XW i + w) KB) stay inside one stage, the output blocks (3 KB
+  // per wave) inside stages 0 and 1
   static_assert(XW * CPW * 1024 <= XMC * XBK * 2, "x copies past the stage");
-  static_assert(XW * 3072 <= XMC * XBK * 2, "output blocks past the stage");
+  static_assert(XW * 3072 <= 2 * XMC * XBK * 2, "output blocks past stages 0 and 1");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j16 = lane & 15, q = lane >> 4;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -293,7 +304,7 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     for (int j = 0; j < XNS; ++j) step(kt + j, stg[j], stg[(j + XNS - 1) % XNS], wbr[j]);
   }
   ex_wait_vmcnt<0>();  // no copy may still be writing LDS
-  __syncthreads();     // every wave is done with the stages: stage 0 now holds the output blocks
+  __syncthreads();     // every wave is done with the stages: stages 0 and 1 now hold the output blocks
 
   // store: the output dtype is dispatched once, outside the loops
   if (ydt == DT_F32)
@@ -304,32 +315,25 @@ __device__ __forceinline__ void mx_chunk(const int32_t* __restrict__ sPos, int r
     mx_store<MS, 2>(acc, sPos, rows, stg, N, ncol0, y, DT_F16);
 }
 
-template <bool SCL_LDS, bool XF16, bool BLK>
+// The chunk's m-subtile count as a template argument: the smallest MS >= rows / 16.
+template <int MS, bool SCL_LDS, bool XF16, bool BLK>
 __device__ __forceinline__ void mx_chunks(const int32_t* __restrict__ sPos, int rows, uint8_t* const* stg,
                                           const uint8_t* __restrict__ sScl, __amdgpu_buffer_rsrc_t rsX,
                                           __amdgpu_buffer_rsrc_t rsW, __amdgpu_buffer_rsrc_t rsS, int64_t K,
                                           int64_t N, int64_t ncol0, const uint32_t* wo, const uint32_t* so,
                                           int64_t pos_per_row, void* __restrict__ y, int ydt) {
-  switch ((rows + 15) >> 4) {
-#define QL_MX_CASE(ms)                                                                                             \
-  case ms:                                                                                                         \
-    mx_chunk<ms, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y,   \
-                                     ydt);                                                                         \
-    break;
-    QL_MX_CASE(1)
-    QL_MX_CASE(2)
-    QL_MX_CASE(3)
-    QL_MX_CASE(4)
-    QL_MX_CASE(5)
-    default:
-      mx_chunk<6, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
-      break;
-#undef QL_MX_CASE
+  if constexpr (MS < XMC / 16) {
+    if (rows > 16 * MS) {
+      mx_chunks<MS + 1, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y,
+                                            ydt);
+      return;
+    }
   }
+  mx_chunk<MS, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
 }
 
 template <bool SCL_LDS, bool XF16, bool BLK>
-__global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(512, EXPERTS_MX_MINB) void experts_mx_kernel(const uint8_t* __restrict__ codes,
                                                             const uint8_t* __restrict__ scales, int64_t e, int64_t N,
                                                             int64_t K, const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ perm_pos,
@@ -392,11 +396,17 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
     }
   }
   if constexpr (SCL_LDS) {
-    // rows of the tile that exist, K/32 bytes each, from the aligned word at or below the first
+    // rows of the tile that exist, K/32 bytes each, from the aligned word at or below the first:
+    // copied HBM -> LDS by DMA, 64 words per wave instruction, all in flight at once (a load-store
+    // loop through registers would wait out one round trip per pass); the chunk loop's first
+    // barrier, after the wait below, publishes them
     const int64_t live = min((int64_t)XBN, N - nt * XBN);
     const int nd = (int)((ssh + live * (K / 32) + 3) / 4);
     const uint32_t a0 = (uint32_t)(sbase - ssh);
-    for (int i = tid; i < nd; i += XW * 64) sScl32[i] = __builtin_amdgcn_raw_buffer_load_b32(rsS, a0 + 4u * i, 0, 0);
+    for (int i0 = wave * 64; i0 < nd; i0 += XW * 64)
+      if (i0 + lane < nd)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sScl32 + i0), 4, a0 + 4u * (i0 + lane), 0, 0, 0);
+    ex_wait_vmcnt<0>();
   }
   const uint8_t* sScl = (const uint8_t*)sScl32;
   for (int32_t mc = 0; mc < cnt; mc += XMC) {
@@ -404,7 +414,7 @@ __global__ __launch_bounds__(512, 1) void experts_mx_kernel(const uint8_t* __res
     __syncthreads();  // previous chunk's readers of sPos are done (and the scale bytes are staged)
     if (tid < XMC) sPos[tid] = tid < rows ? perm_pos[off + mc + tid] : -1;
     __syncthreads();
-    mx_chunks<SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
+    mx_chunks<1, SCL_LDS, XF16, BLK>(sPos, rows, stg, sScl, rsX, rsW, rsS, K, N, ncol0, wo, so, pos_per_row, y, ydt);
   }
 }
 

@@ -187,12 +187,25 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   {
     // rows of the workgroup that exist, times groups / 2 words of scales (and of biases); read
     // coalesced, a group count per row that is even keeps every word inside one array
+    // coalesced, a group count per row that is even keeps every word inside one array.  PU passes'
+    // loads are issued before any of them is written (one round trip, not one per pass): the large
+    // workgroups of 4 to 8 x rows stage many passes.
     const int64_t prow = rows_left < geo.rows_per_wg ? rows_left : geo.rows_per_wg;
     const int pw = (int)(prow * groups / 2);
-    for (int t = threadIdx.x; t < pw; t += 256) {
-      const uint32_t sw = __builtin_amdgcn_raw_buffer_load_b32(rsc, 4 * t, 0, 0);
-      const uint32_t bw = __builtin_amdgcn_raw_buffer_load_b32(rbi, 4 * t, 0, 0);
-      *(u32x2_t*)(sp + 8 * t) = u32x2_t{perm(bw, sw, 0x05040100u), perm(bw, sw, 0x07060302u)};
+    constexpr int PU = MT >= 4 ? GEMV_MF_PU_M8 : GEMV_MF_PU;
+    for (int t0 = threadIdx.x; t0 < pw; t0 += 256 * PU) {
+      uint32_t sw[PU], bw[PU];
+#pragma unroll
+      for (int u = 0; u < PU; ++u) {
+        const int t = t0 + 256 * u;
+        sw[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, t < pw ? 4 * t : kOOB, 0, 0);
+        bw[u] = __builtin_amdgcn_raw_buffer_load_b32(rbi, t < pw ? 4 * t : kOOB, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < PU; ++u) {
+        const int t = t0 + 256 * u;
+        if (t < pw) *(u32x2_t*)(sp + 8 * t) = u32x2_t{perm(bw[u], sw[u], 0x05040100u), perm(bw[u], sw[u], 0x07060302u)};
+      }
     }
   }
   gptr<uint16_t> xg = (gptr<uint16_t>)d.x;

@@ -112,6 +112,12 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #ifndef GEMV_MF_AUX
 #define GEMV_MF_AUX 0  // cache policy bits of the weight-word loads
 #endif
+#ifndef GEMV_MF_PU
+#define GEMV_MF_PU 1  // passes of the parameter staging whose loads a thread issues at once
+#endif
+#ifndef GEMV_MF_PU_M8
+#define GEMV_MF_PU_M8 8  // the same for 4 to 8 x rows
+#endif
 #ifndef GEMV_MF_SU
 #define GEMV_MF_SU 4  // 16-byte chunks of x a thread loads at once when it stages x
 #endif
