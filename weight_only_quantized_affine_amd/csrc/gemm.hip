@@ -555,11 +555,14 @@ __device__ __forceinline__ void wprep_pp_block(int64_t blk, const uint16_t* __re
   const int64_t n0 = blk * 32;
   const int pitch = groups + 1;
   {
-    // eight threads per row, every load of the row in flight at once
+    // eight threads per row; with 16-byte aligned rows (groups a multiple of 8, aligned arrays)
+    // thread (r, part) reads the row's 8-group chunks part, part + 8, ... as 16-byte loads, four
+    // passes' loads issued before any is used; otherwise the groups part, part + 8, ... one by one
     const int r = tid >> 3, part = tid & 7;
     const int64_t n = n0 + r;
     float smax = 0.0f, bmax = 0.0f;
-    if (n < N) {
+    const bool wide = (groups & 7) == 0 && (((uintptr_t)scales | (uintptr_t)biases) & 15) == 0;
+    if (n < N && !wide) {
       const uint16_t* sr = scales + n * groups;
       const uint16_t* br = biases + n * groups;
       for (int g = part; g < groups; g += 8) {
@@ -567,6 +570,36 @@ __device__ __forceinline__ void wprep_pp_block(int64_t blk, const uint16_t* __re
         s_pair[r * pitch + g] = sbits | (bbits << 16);
         smax = fmaxf(smax, fabsf(param_to_f32<PT>(sbits)));
         bmax = fmaxf(bmax, fabsf(param_to_f32<PT>(bbits)));
+      }
+    }
+    if (n < N && wide) {
+      const uint16_t* sr = scales + n * groups;
+      const uint16_t* br = biases + n * groups;
+      const int chunks = groups / 8;
+      for (int c0 = part; c0 < chunks; c0 += 8 * 4) {
+        u32x4_t sv[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 8 * u;
+          if (c < chunks) {
+            sv[u] = *(const u32x4_t*)(sr + 8 * c);
+            bv[u] = *(const u32x4_t*)(br + 8 * c);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = c0 + 8 * u;
+          if (c < chunks) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t sbits = (sv[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const uint32_t bbits = (bv[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              s_pair[r * pitch + 8 * c + e] = sbits | (bbits << 16);
+              smax = fmaxf(smax, fabsf(param_to_f32<PT>(sbits)));
+              bmax = fmaxf(bmax, fabsf(param_to_f32<PT>(bbits)));
+            }
+          }
+        }
       }
     }
 #pragma unroll
