@@ -35,6 +35,9 @@ Readings of points the pages leave open:
   ggml's block_q4_K / block_q6_K for the layout; the placement of the 6-bit scales and mins inside
   Q4_K's 12 bytes and of the quants inside the quant bytes follows that layout as this oracle
   reads it (_q4_k_fields, _q6_k_fields).  No ggml bytes are at hand to check it against.
+* GPTQ_P: "weight packing follows rows" is read as the planar blocks running down each
+  column of qweight (the input axis, as GPTQ's continuous streams do) and "zero packing follows
+  columns" as the blocks running along each row of qzeros (the outputs).
 * AWQ lane order [0,2,4,6,1,3,5,7]: read as the columns that the nibbles of a word hold, from
   the low nibble up (nibble 1 holds column 2), applied to 4-bit qweight and qzeros alike; other
   widths are plain streams along the outputs.
@@ -74,6 +77,10 @@ __all__ = [
     "take",
     "gptq_transcode",
     "gptq_dequant_f64",
+    "gptq_planes",
+    "gptq_planar_codes",
+    "gptq_planar_transcode",
+    "gptq_planar_dequant_f64",
     "AWQ_LANE_ORDER",
     "awq_codes",
     "awq_transcode",
@@ -302,6 +309,67 @@ def gptq_dequant_f64(qweight, qzeros, scale_bits, bits: int, group_size: int, k:
     sg = np.repeat(s.T, group_size, axis=1)
     zg = np.repeat(zeros.T, group_size, axis=1)
     return sg * (codes - zg)
+
+
+def gptq_planes(bits: int) -> tuple:
+    """Plane widths of a GPTQ_P stream, low plane first (GPTQModel "Packing Formats and
+    Compatibility", GPTQ_P table: 3 = 2 + 1, 5 = 4 + 1, 6 = 4 + 2, 7 = 4 + 2 + 1, and one plane at
+    2, 4 and 8 bits): the powers of two that make up ``bits``, the largest first."""
+    assert 2 <= bits <= 8
+    return tuple(w for w in (8, 4, 2, 1) if bits & w)
+
+
+def gptq_planar_codes(words, bits: int, count: int) -> np.ndarray:
+    """The first ``count`` codes of each row of GPTQ_P words (GPTQModel "Packing Formats and
+    Compatibility", GPTQ_P): every 32 consecutive codes take ``bits`` adjacent words; those words
+    hold the planes one after another, low plane first, a plane of width w taking w words whose
+    32 w-bit fields are the block's codes in order, least significant field first; the code is
+    the low plane's field, plus the next plane's field shifted past it, and so on."""
+    w = np.asarray(words, dtype=np.uint32)
+    rows = w.shape[0]
+    assert count % 32 == 0 and w.shape[1] >= count // 32 * bits
+    nb = count // 32
+    blocks = w[:, : nb * bits].reshape(rows * nb, bits)
+    codes = np.zeros((rows * nb, 32), dtype=np.int64)
+    first, shift = 0, 0
+    for wp in gptq_planes(bits):
+        codes |= _read_stream(blocks[:, first:first + wp], wp, 32) << shift
+        first += wp
+        shift += wp
+    return codes.reshape(rows, count)
+
+
+def gptq_planar_transcode(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int,
+                          param_dtype: str):
+    """GPTQ_P (planar) -> MLX affine rows (GPTQModel "Packing Formats and Compatibility", GPTQ_P:
+    the GPTQ tensor names and shapes, qweight [K*b/32, N] with each column's codes as planar blocks
+    down the input axis, qzeros [G, N*b/32] with each group's zeros as planar blocks along the
+    outputs, zeros always true zero points (never the v1 minus-one form); GPTQModel wiki "MLX Apple
+    Silicon", Packed layouts and exact transcoding: scales to [out, groups], additive bias
+    -zero*scale, and a 7-bit source kept in 8-bit rows).
+
+    Returns (packed [n, k*tb/32], scales [n, G], biases [n, G]) with tb = 8 for 7-bit sources and
+    tb = bits otherwise; biases = RNE(-zero * scale) in param_dtype (exact in fp32 before that)."""
+    G = k // group_size
+    qweight = np.asarray(qweight, dtype=np.uint32)
+    qzeros = np.asarray(qzeros, dtype=np.uint32)
+    assert qweight.shape == (k * bits // 32, n) and qzeros.shape == (G, n * bits // 32)
+    tb = 8 if bits == 7 else bits
+    codes = gptq_planar_codes(qweight.T, bits, k)  # [n, k]
+    zeros = gptq_planar_codes(qzeros, bits, n)  # [G, n]
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))  # [G, n]
+    b32 = (-(zeros.astype(np.float64)) * s).astype(np.float32)
+    return (pack_codes(codes, tb), np.ascontiguousarray(np.asarray(scale_bits, dtype=np.uint16).T),
+            np.ascontiguousarray(to_bits(param_dtype, b32).T))
+
+
+def gptq_planar_dequant_f64(qweight, qzeros, scale_bits, bits: int, group_size: int, k: int, n: int,
+                            param_dtype: str):
+    """GPTQ_P's own reconstruction, scale * (code - zero) with true zeros, exactly in fp64: [n, k]."""
+    codes = gptq_planar_codes(np.asarray(qweight, dtype=np.uint32).T, bits, k).astype(np.float64)
+    zeros = gptq_planar_codes(qzeros, bits, n).astype(np.float64)
+    s = bits_to_f64(param_dtype, np.asarray(scale_bits, dtype=np.uint16))
+    return np.repeat(s.T, group_size, axis=1) * (codes - np.repeat(zeros.T, group_size, axis=1))
 
 
 AWQ_LANE_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)

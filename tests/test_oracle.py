@@ -76,7 +76,7 @@ def _stream_words_from_digits(codes, bits):
     significant first) are the codes in reverse order; written out as a digit string and parsed
     with Python's int(), then cut into little-endian 32-bit words (no shifts or masks)."""
     digits = "0123456789abcdefghijklmnopqrstuv"
-    if bits in (2, 3, 4, 5):
+    if bits in (1, 2, 3, 4, 5):
         text, base = "".join(digits[c] for c in reversed(codes)), 1 << bits
     elif bits == 6:  # two octal digits per code
         text, base = "".join(f"{c >> 3}{c & 7}" for c in reversed(codes)), 8
@@ -573,6 +573,104 @@ def test_gptq_dequant_is_scale_times_code_minus_zero(bits, pdt, g, v1):
     if v1:
         wrong = O.gptq_dequant_f64(qw.astype(np.uint32), qz.astype(np.uint32), sb, bits, g, k, n, pdt)
         np.testing.assert_allclose(wrong - got, np.repeat(sv.T, g, axis=1))
+
+
+# ---------------------------------------------------------------- GPTQ_P (planar) -> affine transcoder
+# (GPTQModel "Packing Formats and Compatibility", GPTQ_P: 32 codes per b adjacent words, planes low
+# first, fields least significant first; the plane table; true zeros; 2/4/8-bit planes identical to
+# the continuous words, 3-bit packing different)
+
+# the page's table of planes per width, as printed (the oracle derives it from the width's bits)
+_PLANES_TABLE = {2: (2,), 3: (2, 1), 4: (4,), 5: (4, 1), 6: (4, 2), 7: (4, 2, 1), 8: (8,)}
+
+
+def _planar_words(codes, bits):
+    """One GPTQ_P stream from codes: per block of 32, each plane's fields (the code's bits from the
+    plane's offset up) written as one little-endian stream with the digit-string construction."""
+    out = []
+    for b0 in range(0, len(codes), 32):
+        blk = [int(c) for c in codes[b0:b0 + 32]]
+        off = 0
+        for wp in _PLANES_TABLE[bits]:
+            out.append(_stream_words_from_digits([(c // (1 << off)) % (1 << wp) for c in blk], wp))
+            off += wp
+    return np.concatenate(out).astype(np.uint32)
+
+
+def test_gptq_planar_hand_blocks():
+    """Blocks worked out by hand from the layout: 3 bits, codes i % 8 (low plane fields i % 4 in
+    two words, high plane bits (i // 4) % 2 in one); 5 bits, codes i; 6 bits, codes 63 - i; 7 bits,
+    codes 96 + i (mid plane fields 2 then 3, high plane all ones)."""
+    cases = {
+        3: ([0xE4E4E4E4, 0xE4E4E4E4, 0xF0F0F0F0], [i % 8 for i in range(32)]),
+        5: ([0x76543210, 0xFEDCBA98, 0x76543210, 0xFEDCBA98, 0xFFFF0000], list(range(32))),
+        6: ([0x89ABCDEF, 0x01234567, 0x89ABCDEF, 0x01234567, 0xFFFFFFFF, 0xAAAAAAAA], [63 - i for i in range(32)]),
+        7: ([0x76543210, 0xFEDCBA98, 0x76543210, 0xFEDCBA98, 0xAAAAAAAA, 0xFFFFFFFF, 0xFFFFFFFF],
+            [96 + i for i in range(32)]),
+    }
+    for bits, (words, want) in cases.items():
+        assert O.gptq_planes(bits) == _PLANES_TABLE[bits]
+        got = O.gptq_planar_codes(np.array([words], dtype=np.uint32), bits, 32)
+        np.testing.assert_array_equal(got[0], want, err_msg=f"bits={bits}")
+        np.testing.assert_array_equal(_planar_words(want, bits), words)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_gptq_planar_single_plane_is_the_continuous_stream(bits):
+    """At 2, 4 and 8 bits the planar words are the continuous words (one plane)."""
+    w = np.random.default_rng(300 + bits).integers(0, 1 << 32, size=(5, 4 * bits), dtype=np.uint64).astype(np.uint32)
+    np.testing.assert_array_equal(O.gptq_planar_codes(w, bits, 128), O.unpack_codes(w, bits, 128))
+
+
+def test_gptq_planar_three_bits_differs_from_continuous():
+    w = np.random.default_rng(310).integers(0, 1 << 32, size=(4, 12), dtype=np.uint64).astype(np.uint32)
+    assert not np.array_equal(O.gptq_planar_codes(w, 3, 128), O.unpack_codes(w, 3, 128))
+
+
+def _planar_case(seed, k, n, bits, g, pow2_scales=False):
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 1 << bits, size=(k, n))  # [in, out]
+    zeros = rng.integers(0, 1 << bits, size=(k // g, n))
+    qweight = np.stack([_planar_words(codes[:, j], bits) for j in range(n)], axis=1)
+    qzeros = np.stack([_planar_words(zeros[r], bits) for r in range(k // g)])
+    if pow2_scales:
+        s = np.ldexp(1.0, rng.integers(-12, -2, size=(k // g, n))).astype(np.float32)
+    else:
+        s = (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32)
+    return codes, zeros, qweight.astype(np.uint32), qzeros.astype(np.uint32), s
+
+
+@pytest.mark.parametrize("bits,pdt,g", [(2, "f16", 64), (3, "bf16", 32), (4, "f16", 128), (5, "f16", 64),
+                                        (6, "bf16", 64), (7, "f16", 32), (8, "bf16", 64)])
+def test_gptq_planar_transcode_reconstructs_scale_times_code_minus_zero(bits, pdt, g):
+    k, n = 256, 64
+    codes, zeros, qw, qz, s = _planar_case(320 + bits, k, n, bits, g)
+    sb = O.to_bits(pdt, s)
+    pk, so, bo = O.gptq_planar_transcode(qw, qz, sb, bits, g, k, n, pdt)
+    tb = 8 if bits == 7 else bits
+    assert pk.shape == (n, k * tb // 32)
+    np.testing.assert_array_equal(O.unpack_codes(pk, tb, k), codes.T)
+    np.testing.assert_array_equal(so, sb.T)
+    deq = O.affine_dequant_f32(pk, so, bo, tb, g, pdt, k).astype(np.float64)
+    sv = O.bits_to_f64(pdt, sb)
+    own = O.gptq_planar_dequant_f64(qw, qz, sb, bits, g, k, n, pdt)
+    for j in range(0, n, 5):
+        for i in range(0, k, 3):
+            # true zeros: no v1 correction
+            want = float(sv[i // g, j]) * (int(codes[i, j]) - int(zeros[i // g, j]))
+            assert own[j, i] == want, (j, i)
+            bias_err = abs(float(O.bits_to_f64(pdt, bo[j, i // g])) + float(zeros[i // g, j]) * float(sv[i // g, j]))
+            assert abs(deq[j, i] - want) <= bias_err + abs(want) * 2.0 ** -23 + 1e-30, (j, i)
+
+
+def test_gptq_planar_transcode_exact_with_power_of_two_scales():
+    k, n, g, bits = 128, 64, 32, 6
+    codes, zeros, qw, qz, s = _planar_case(330, k, n, bits, g, pow2_scales=True)
+    sb = O.to_bits("f16", s)
+    pk, so, bo = O.gptq_planar_transcode(qw, qz, sb, bits, g, k, n, "f16")
+    deq = O.affine_dequant_f32(pk, so, bo, bits, g, "f16", k).astype(np.float64)
+    want = np.repeat(s.T.astype(np.float64), g, axis=1) * (codes.T - np.repeat(zeros.T, g, axis=1))
+    np.testing.assert_array_equal(deq, want)
 
 
 # ---------------------------------------------------------------- AWQ GEMM -> affine transcoder
