@@ -114,6 +114,31 @@ ql_status qlinear_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
                                  int v1_zeros, uint32_t* packed, void* scales_out, void* biases_out,
                                  void* stream);
 
+/* GPTQ_P (planar GPTQ) -> MLX affine rows (GPTQModel "Packing Formats and Compatibility",
+ * GPTQ_P; GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact transcoding):
+ *   in:  qweight [k*bits/32, n] uint32 (output column j's codes down the input axis as planar
+ *        blocks: every 32 codes take bits adjacent words holding the bit planes, low plane first,
+ *        plane widths the powers of two in bits (3 = 2+1, 5 = 4+1, 6 = 4+2, 7 = 4+2+1), fields
+ *        least significant first), qzeros [k/group_size, n*bits/32] (each group's true zero
+ *        points as planar blocks along the outputs; no v1 form), scales [k/group_size, n] in
+ *        scale_dtype; the value is scale * (code - zero).
+ *   out: packed [n, k*tb/32] (tb = 8 for bits = 7, else bits), scales_out [n, k/group_size],
+ *        biases_out [n, k/group_size] = RNE(-zero * scale) in scale_dtype.
+ * bits in 2..8 (at 2, 4 and 8 the words equal GPTQ's continuous ones); group_size in {32, 64,
+ * 128}; k and n multiples of 32, k a multiple of group_size (QL_ERR_SHAPE).  Word arrays 4-byte
+ * aligned, 16-bit arrays 2-byte aligned, all device memory; outputs must not overlap inputs. */
+ql_status qlinear_transcode_gptq_planar(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
+                                        ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size,
+                                        uint32_t* packed, void* scales_out, void* biases_out, void* stream);
+
+/* Host-side check of a GPTQ / GPTQ_P g_idx (GPTQModel "Packing Formats and Compatibility",
+ * g_idx: the input-channel-to-group map, and the exact affine holder's contract that it be
+ * arange(k) / group_size, activation order not dropped silently): g_idx is int32 [k] in HOST
+ * memory.  Returns QL_OK when g_idx[i] == i / group_size for every i, QL_ERR_UNSUPPORTED
+ * (naming the first row that differs) for an activation-order map, which the transcoders cannot
+ * express; launches nothing and touches no device. */
+ql_status qlinear_gptq_check_g_idx(const int32_t* g_idx, int64_t k, int group_size);
+
 /* AWQ GEMM -> MLX affine rows (GPTQModel wiki "MLX Apple Silicon", Packed layouts and exact
  * transcoding, the AWQ GEMM and seven-bit rows, and ParoQuant for the lane order; GPTQModel
  * "Packing Formats and Compatibility", AWQ GEMM):

@@ -146,3 +146,70 @@ def test_transcode_awq_leaves_bytes_past_outputs():
     assert bool((so_buf[n * groups:] == 0x7777).all()) and bool((bo_buf[n * groups:] == 0x7777).all())
     opk, _, _ = O.awq_transcode(qw, qz, sb, bits, g, k, n, "f16")
     np.testing.assert_array_equal(dev_to_u32(pk_buf[: n * words].view(n, words)), opk)
+
+
+# ---------------------------------------------------------------- GPTQ_P (planar) -> affine
+# (GPTQModel "Packing Formats and Compatibility", GPTQ_P: planar blocks of 32 codes, true zeros)
+
+
+def _planar(seed, k, n, bits, g, pdt):
+    rng = np.random.default_rng(seed)
+    qw = rng.integers(0, 1 << 32, size=(k * bits // 32, n), dtype=np.uint64).astype(np.uint32)
+    qz = rng.integers(0, 1 << 32, size=(k // g, n * bits // 32), dtype=np.uint64).astype(np.uint32)
+    sb = O.to_bits(pdt, (rng.random((k // g, n)) * 0.02 + 1e-3).astype(np.float32))
+    return qw, qz, sb
+
+
+@pytest.mark.parametrize("k,n,bits,g,pdt", [
+    (4096, 4096, 3, 128, "f16"),  # whole 512 x 64 tiles
+    (1088, 96, 3, 32, "bf16"),  # ragged rows (1088 = 2 * 512 + 64) and columns (96 = 64 + 32)
+    (640, 160, 5, 64, "f16"),
+    (384, 352, 6, 128, "bf16"),
+    (256, 288, 7, 32, "f16"),  # 7-bit source into 8-bit rows
+    (1024, 224, 2, 64, "bf16"),  # single plane: GPTQ's continuous words
+    (512, 96, 4, 128, "f16"),
+    (2048, 64, 8, 64, "bf16"),
+    (32, 32, 7, 32, "bf16"),  # one block
+])
+def test_transcode_gptq_planar_bitexact(k, n, bits, g, pdt):
+    qw, qz, sb = _planar(5 * k + n + bits, k, n, bits, g, pdt)
+    print(f"gptq_p transcode k={k} n={n} bits={bits} g={g} {pdt}", flush=True)
+    pk, so, bo = q.qlinear_transcode_gptq_planar(u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, pdt), bits=bits,
+                                                 group_size=g)
+    torch.cuda.synchronize()
+    opk, oso, obo = O.gptq_planar_transcode(qw, qz, sb, bits, g, k, n, pdt)
+    np.testing.assert_array_equal(dev_to_u32(pk), opk)
+    np.testing.assert_array_equal(dev_to_bits(so), oso)
+    np.testing.assert_array_equal(dev_to_bits(bo), obo)
+
+
+def test_transcoded_gptq_planar_weight_through_gemv():
+    k, n, bits, g = 2048, 1024, 6, 128
+    qw, qz, sb = _planar(25, k, n, bits, g, "f16")
+    pk, so, bo = q.qlinear_transcode_gptq_planar(u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, "f16"), bits=bits,
+                                                 group_size=g, g_idx=np.arange(k, dtype=np.int32) // g)
+    xb = synth.acts_bits(26, 2, k, "bf16")
+    y = q.qlinear_gemv(bits_to_dev(xb, "bf16"), pk, so, bo, bits=bits, group_size=g, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.apply(O.bits_to_f64("bf16", xb), O.gptq_planar_dequant_f64(qw, qz, sb, bits, g, k, n, "f16"))
+    err = O.rel_l2_per_row(out_f64(y), ref)
+    print(f"gptq_p transcode + gemv max rel-l2 {err.max():.3e}")
+    assert err.max() <= 2e-3
+
+
+def test_transcode_gptq_planar_leaves_bytes_past_outputs():
+    k, n, bits, g = 1088, 160, 7, 64
+    qw, qz, sb = _planar(31, k, n, bits, g, "bf16")
+    words, groups = k * 8 // 32, k // g
+    pk_buf = torch.full((n * words + 64,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    so_buf = torch.full((n * groups + 64,), 0x7777, dtype=torch.int16, device=DEV)
+    bo_buf = torch.full((n * groups + 64,), 0x7777, dtype=torch.int16, device=DEV)
+    q.qlinear_transcode_gptq_planar(u32_to_dev(qw), u32_to_dev(qz), bits_to_dev(sb, "bf16"), bits=bits, group_size=g,
+                                    packed=pk_buf[: n * words].view(n, words),
+                                    scales_out=so_buf[: n * groups].view(n, groups),
+                                    biases_out=bo_buf[: n * groups].view(n, groups))
+    torch.cuda.synchronize()
+    assert bool((pk_buf[n * words:] == 0x5A5A5A5A).all())
+    assert bool((so_buf[n * groups:] == 0x7777).all()) and bool((bo_buf[n * groups:] == 0x7777).all())
+    opk, _, _ = O.gptq_planar_transcode(qw, qz, sb, bits, g, k, n, "bf16")
+    np.testing.assert_array_equal(dev_to_u32(pk_buf[: n * words].view(n, words)), opk)

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import weight_only_quantized_affine_amd as q
@@ -259,6 +260,48 @@ def test_transcode_awq_rejects_bad_arguments(lib):
     assert call(qw=FAKE + 2) == QL_ERR_ALIGN
     assert call(bo=FAKE + 1) == QL_ERR_ALIGN
     assert call(n=0) == QL_OK
+
+
+def test_transcode_gptq_planar_rejects_bad_arguments(lib):
+    args = [FAKE, FAKE, FAKE, F16, 256, 64, 5, 64, FAKE, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["qw", "qz", "sc", "sdt", "k", "n", "bits", "g", "pk", "so", "bo", "s"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return lib.qlinear_transcode_gptq_planar(*a)
+
+    assert call(bits=1) == QL_ERR_UNSUPPORTED
+    assert call(bits=9) == QL_ERR_UNSUPPORTED
+    assert call(g=16) == QL_ERR_UNSUPPORTED
+    assert call(k=250) == QL_ERR_SHAPE
+    assert call(k=96, g=64) == QL_ERR_SHAPE
+    assert call(n=48) == QL_ERR_SHAPE  # zeros come in planar blocks of 32 columns
+    assert call(sdt=F32) == QL_ERR_DTYPE
+    assert call(qw=None) == QL_ERR_NULL
+    assert call(pk=FAKE + 2) == QL_ERR_ALIGN
+    assert call(sc=FAKE + 1) == QL_ERR_ALIGN
+    assert call(k=0) == QL_OK
+
+
+def test_gptq_g_idx_check_on_host(lib):
+    """The exact affine form needs g_idx == arange(k) // group_size (GPTQModel "Packing Formats and
+    Compatibility": GPTQ holders require it; activation order is not dropped silently)."""
+    k, g = 512, 128
+    ok = np.ascontiguousarray(np.arange(k, dtype=np.int32) // g)
+    assert lib.qlinear_gptq_check_g_idx(ok.ctypes.data, k, g) == QL_OK
+    perm = ok.copy()
+    perm[[3, 300]] = perm[[300, 3]]  # two inputs of different groups swapped: an activation order
+    assert lib.qlinear_gptq_check_g_idx(perm.ctypes.data, k, g) == QL_ERR_UNSUPPORTED
+    assert "g_idx[3]" in _err(lib)
+    assert lib.qlinear_gptq_check_g_idx(ok.ctypes.data, k, 64) == QL_ERR_UNSUPPORTED  # another group size
+    assert lib.qlinear_gptq_check_g_idx(None, k, g) == QL_ERR_NULL
+    assert lib.qlinear_gptq_check_g_idx(None, 0, g) == QL_OK
+    assert lib.qlinear_gptq_check_g_idx(ok.ctypes.data, k, 0) == QL_ERR_UNSUPPORTED
+    with pytest.raises(q.QLError):
+        q.qlinear_gptq_check_g_idx(perm, g)
+    q.qlinear_gptq_check_g_idx(ok, g)
 
 
 def test_apply_experts_noalloc_rejects_sizes_past_its_scratch(lib):

@@ -28,6 +28,8 @@ __all__ = [
     "qlinear_quantize_q8_0",
     "qlinear_take",
     "qlinear_transcode_gptq",
+    "qlinear_transcode_gptq_planar",
+    "qlinear_gptq_check_g_idx",
     "qlinear_transcode_awq",
     "qlinear_gemv",
     "qlinear_gemm",
@@ -96,6 +98,8 @@ _SIGNATURES = {
     "qlinear_quantize_q8_0": (_INT, [_P, _I64, _I64, _P, _P]),
     "qlinear_take": (_INT, [_P, _I64, _P, _I64, _I64, _P, _P]),
     "qlinear_transcode_gptq": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P]),
+    "qlinear_transcode_gptq_planar": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
+    "qlinear_gptq_check_g_idx": (_INT, [_P, _I64, _INT]),
     "qlinear_transcode_awq": (_INT, [_P, _P, _P, _INT, _I64, _I64, _INT, _INT, _P, _P, _P, _P]),
     "qlinear_gemv": (_INT, [_P, _INT, _I64, _I64, _P, _P, _P, _INT, _I64, _INT, _INT, _P, _P, _INT, _P]),
     "qlinear_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _INT, _INT]),
@@ -207,15 +211,26 @@ def qlinear_take(pos, src, dst=None):
     return dst
 
 
+def qlinear_gptq_check_g_idx(g_idx, group_size: int):
+    """Raise QLError unless g_idx (int32 [k], any device; copied to host) is arange(k) //
+    group_size: an activation-order map has no exact affine form."""
+    import numpy as np
+    lib = load_library()
+    h = np.ascontiguousarray(np.asarray(g_idx.cpu() if hasattr(g_idx, "cpu") else g_idx, dtype=np.int32))
+    _check(lib.qlinear_gptq_check_g_idx(h.ctypes.data, h.shape[0], group_size))
+
+
 def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: int, v1_zeros: bool = False,
-                           packed=None, scales_out=None, biases_out=None):
+                           g_idx=None, packed=None, scales_out=None, biases_out=None):
     """GPTQ (continuous layout, contiguous groups) -> affine (packed [n, k*bits/32] int32, scales and
     biases [n, k/group_size] in scales' dtype).  qweight [k*bits/32, n], qzeros [G, n*bits/32]
-    (int32), scales [G, n]."""
+    (int32), scales [G, n].  A g_idx, when given, is checked first (qlinear_gptq_check_g_idx)."""
     torch = _torch()
     lib = load_library()
     n = scales.shape[1]
     k = qweight.shape[0] * 32 // bits
+    if g_idx is not None:
+        qlinear_gptq_check_g_idx(g_idx, group_size)
     if packed is None:
         packed = torch.empty((n, qweight.shape[0]), dtype=torch.int32, device=qweight.device)
     so = scales_out if scales_out is not None else torch.empty((n, scales.shape[0]), dtype=scales.dtype,
@@ -223,6 +238,29 @@ def qlinear_transcode_gptq(qweight, qzeros, scales, *, bits: int, group_size: in
     bo = biases_out if biases_out is not None else torch.empty_like(so)
     _check(lib.qlinear_transcode_gptq(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits, group_size,
                                       1 if v1_zeros else 0, _ptr(packed), _ptr(so), _ptr(bo), _stream()))
+    return packed, so, bo
+
+
+def qlinear_transcode_gptq_planar(qweight, qzeros, scales, *, bits: int, group_size: int, g_idx=None, packed=None,
+                                  scales_out=None, biases_out=None):
+    """GPTQ_P (planar blocks, true zeros) -> affine (packed [n, k*tb/32] int32 with tb = 8 for 7-bit
+    sources, else bits; scales and biases [n, k/group_size] in scales' dtype).  qweight
+    [k*bits/32, n], qzeros [G, n*bits/32] (int32), scales [G, n].  A g_idx, when given, is checked
+    first (qlinear_gptq_check_g_idx)."""
+    torch = _torch()
+    lib = load_library()
+    n = scales.shape[1]
+    k = qweight.shape[0] * 32 // bits
+    if g_idx is not None:
+        qlinear_gptq_check_g_idx(g_idx, group_size)
+    tb = 8 if bits == 7 else bits
+    if packed is None:
+        packed = torch.empty((n, k * tb // 32), dtype=torch.int32, device=qweight.device)
+    so = scales_out if scales_out is not None else torch.empty((n, scales.shape[0]), dtype=scales.dtype,
+                                                                device=qweight.device)
+    bo = biases_out if biases_out is not None else torch.empty_like(so)
+    _check(lib.qlinear_transcode_gptq_planar(_ptr(qweight), _ptr(qzeros), _ptr(scales), _dt(scales), k, n, bits,
+                                             group_size, _ptr(packed), _ptr(so), _ptr(bo), _stream()))
     return packed, so, bo
 
 

@@ -188,6 +188,9 @@ hipError_t launch_take(const int64_t* pos, int64_t n_pos, const void* src, int64
 hipError_t launch_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
                                  int64_t k, int64_t n, int bits, int g, int v1, uint32_t* packed, void* scales_out,
                                  void* biases_out, hipStream_t s);
+hipError_t launch_transcode_gptq_planar(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
+                                        int64_t k, int64_t n, int bits, int g, uint32_t* packed, void* scales_out,
+                                        void* biases_out, hipStream_t s);
 hipError_t launch_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
                                 int64_t k, int64_t n, int bits, int g, uint32_t* packed, void* scales_out,
                                 void* biases_out, hipStream_t s);

@@ -141,6 +141,45 @@ ql_status qlinear_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
                   fn);
 }
 
+ql_status qlinear_transcode_gptq_planar(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
+                                        ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size,
+                                        uint32_t* packed, void* scales_out, void* biases_out, void* stream) {
+  const char* fn = "qlinear_transcode_gptq_planar";
+  CHECK(k >= 0 && n >= 0, QL_ERR_SHAPE, "%s: k and n must be >= 0", fn);
+  CHECK(bits >= 2 && bits <= 8, QL_ERR_UNSUPPORTED, "%s: bits=%d not supported (GPTQ_P widths 2 to 8)", fn, bits);
+  CHECK(group_size == 32 || group_size == 64 || group_size == 128, QL_ERR_UNSUPPORTED,
+        "%s: group_size=%d not supported (32, 64 or 128)", fn, group_size);
+  CHECK(k % 32 == 0 && k % group_size == 0, QL_ERR_SHAPE, "%s: k=%lld must be a multiple of 32 and of group_size", fn,
+        (long long)k);
+  CHECK(n % 32 == 0, QL_ERR_SHAPE, "%s: n=%lld must be a multiple of 32 (whole planar blocks of zeros)", fn,
+        (long long)n);
+  CHECK(is16(scale_dtype), QL_ERR_DTYPE, "%s: scale_dtype must be QL_F16 or QL_BF16", fn);
+  if (k == 0 || n == 0) return ok();
+  CHECK(qweight && qzeros && scales && packed && scales_out && biases_out, QL_ERR_NULL,
+        "%s: qweight, qzeros, scales, packed, scales_out and biases_out must not be NULL", fn);
+  CHECK(aligned(qweight, 4) && aligned(qzeros, 4) && aligned(packed, 4), QL_ERR_ALIGN,
+        "%s: qweight, qzeros and packed must be 4-byte aligned", fn);
+  CHECK(aligned(scales, 2) && aligned(scales_out, 2) && aligned(biases_out, 2), QL_ERR_ALIGN,
+        "%s: scales, scales_out and biases_out must be 2-byte aligned", fn);
+  CHECK(n * k / 32 * 8 < (int64_t(1) << 31), QL_ERR_UNSUPPORTED, "%s: weight too large", fn);
+  return launched(ql::launch_transcode_gptq_planar(qweight, qzeros, scales, dt(scale_dtype), k, n, bits, group_size,
+                                                   packed, scales_out, biases_out, (hipStream_t)stream),
+                  fn);
+}
+
+ql_status qlinear_gptq_check_g_idx(const int32_t* g_idx, int64_t k, int group_size) {
+  const char* fn = "qlinear_gptq_check_g_idx";
+  CHECK(k >= 0, QL_ERR_SHAPE, "%s: k must be >= 0", fn);
+  CHECK(group_size > 0, QL_ERR_UNSUPPORTED, "%s: group_size=%d must be > 0", fn, group_size);
+  if (k == 0) return ok();
+  CHECK(g_idx, QL_ERR_NULL, "%s: g_idx must not be NULL", fn);
+  for (int64_t i = 0; i < k; ++i)
+    CHECK(g_idx[i] == (int32_t)(i / group_size), QL_ERR_UNSUPPORTED,
+          "%s: g_idx[%lld]=%d, not %lld: an activation-order permutation has no exact affine form", fn, (long long)i,
+          (int)g_idx[i], (long long)(i / group_size));
+  return ok();
+}
+
 ql_status qlinear_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales,
                                 ql_dtype scale_dtype, int64_t k, int64_t n, int bits, int group_size, uint32_t* packed,
                                 void* scales_out, void* biases_out, void* stream) {

@@ -7,6 +7,13 @@
 // -zero * scale, exact in fp32 (zero < 2^8, scale of at most 11 significant bits) and rounded
 // once to the scale dtype.  v1 checkpoints store zero - 1.
 //
+// GPTQ_P ("Packing Formats and Compatibility", GPTQ_P) keeps GPTQ's tensors but stores every 32
+// codes as b adjacent words of bit planes, low plane first (widths: the powers of two that make
+// up b, largest first; fields least significant first inside a plane), with true zero points.
+// At 2, 4 and 8 bits the single plane is GPTQ's continuous word, so those widths take the GPTQ
+// path; at 3, 5, 6 and 7 bits a workgroup stages 16 blocks x 64 columns of qweight in LDS and
+// rewrites each (column, block) as the affine row's continuous words (8-bit words for 7 bits).
+//
 // AWQ GEMM (same pages, AWQ GEMM row and ParoQuant; "Packing Formats and Compatibility", AWQ GEMM)
 // packs the other axis: qweight [K, N*b/32] holds each input row's codes as one b-bit stream
 // along the outputs, qzeros [G, N*b/32] the true zeros the same way, and at 4 bits the nibbles
@@ -40,13 +47,31 @@ __global__ __launch_bounds__(256) void transpose_words_kernel(const uint32_t* __
   }
 }
 
+// Field i (0..31) of the planar block at w (bits words): each plane's field shifted past the
+// planes below it.
+__device__ __forceinline__ uint32_t planar_field(const uint32_t* __restrict__ w, int i, int bits) {
+  uint32_t v = 0u;
+  int first = 0, off = 0;
+#pragma unroll
+  for (int wp = 8; wp >= 1; wp >>= 1) {
+    if (!(bits & wp)) continue;
+    const int pos = i * wp;
+    v |= ((w[first + (pos >> 5)] >> (pos & 31)) & ((1u << wp) - 1u)) << off;
+    first += wp;
+    off += wp;
+  }
+  return v;
+}
+
 // One lane per (output n, group g), g fastest: the zero is bits [b n, b n + b) of row g of qzeros.
 // With awq4 the zeros are 4-bit AWQ words: column c of a word's 8 sits in nibble slot
-// (c >> 1) | ((c & 1) << 2), the inverse of the lane order 0, 2, 4, 6, 1, 3, 5, 7.
+// (c >> 1) | ((c & 1) << 2), the inverse of the lane order 0, 2, 4, 6, 1, 3, 5, 7.  With planar
+// the row is GPTQ_P blocks: the zero is field n % 32 of the block at word b (n / 32).
 template <typename PT>
 __global__ __launch_bounds__(256) void gptq_params_kernel(const uint32_t* __restrict__ qzeros,
                                                           const uint16_t* __restrict__ scales, int64_t n, int groups,
-                                                          int bits, int v1, int awq4, uint16_t* __restrict__ scales_out,
+                                                          int bits, int v1, int awq4, int planar,
+                                                          uint16_t* __restrict__ scales_out,
                                                           uint16_t* __restrict__ biases_out) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n * groups) return;
@@ -58,9 +83,14 @@ __global__ __launch_bounds__(256) void gptq_params_kernel(const uint32_t* __rest
   const int64_t pos = slot * bits;
   const int64_t wi = pos >> 5;
   const int sh = (int)(pos & 31);
-  uint32_t z = zrow[wi] >> sh;
-  if (sh + bits > 32) z |= zrow[wi + 1] << (32 - sh);  // the zero continues in the next word
-  z &= (1u << bits) - 1u;
+  uint32_t z;
+  if (planar) {
+    z = planar_field(zrow + (o >> 5) * bits, (int)(o & 31), bits);
+  } else {
+    z = zrow[wi] >> sh;
+    if (sh + bits > 32) z |= zrow[wi + 1] << (32 - sh);  // the zero continues in the next word
+    z &= (1u << bits) - 1u;
+  }
   const int zero = (int)z + (v1 ? 1 : 0);
   const uint16_t sb = scales[(int64_t)g * n + o];
   // -(zero * scale): the product is exact and rounding to nearest even is symmetric, so the bias
@@ -76,14 +106,62 @@ __global__ __launch_bounds__(256) void gptq_params_kernel(const uint32_t* __rest
 }
 
 hipError_t launch_params(const uint32_t* qzeros, const void* scales, int pdt, int64_t n, int groups, int bits, int v1,
-                         int awq4, void* scales_out, void* biases_out, hipStream_t s) {
+                         int awq4, int planar, void* scales_out, void* biases_out, hipStream_t s) {
   const unsigned nb = (unsigned)((n * groups + 255) / 256);
   if (pdt == DT_BF16)
-    gptq_params_kernel<BF16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4,
+    gptq_params_kernel<BF16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4, planar,
                                                 (uint16_t*)scales_out, (uint16_t*)biases_out);
   else
-    gptq_params_kernel<F16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4,
+    gptq_params_kernel<F16><<<nb, 256, 0, s>>>(qzeros, (const uint16_t*)scales, n, groups, bits, v1, awq4, planar,
                                                (uint16_t*)scales_out, (uint16_t*)biases_out);
+  return hipGetLastError();
+}
+
+constexpr int PKB = 16;  // planar tile: 16 blocks of 32 codes (512 inputs) x 64 output columns
+
+// Tile (k0, n0): word rows k0 / 32 * B .. + 16 B of qweight, columns n0 .. n0 + 63, into LDS (one
+// padding word per row); then item (column c, block kb) decodes its B words and writes the TB
+// words of target row n0 + c from word (k0 / 32 + kb) TB.  k is a multiple of 32, so a block is
+// wholly inside or outside the matrix.
+template <int B, int TB>
+__global__ __launch_bounds__(256) void planar_codes_kernel(const uint32_t* __restrict__ qweight, int64_t k, int64_t n,
+                                                           uint32_t* __restrict__ packed) {
+  __shared__ uint32_t tile[PKB * B][65];
+  const int64_t tiles_n = (n + 63) / 64;
+  const int64_t k0 = (int64_t)(blockIdx.x / tiles_n) * (32 * PKB), n0 = (int64_t)(blockIdx.x % tiles_n) * 64;
+  const int64_t src_rows = k / 32 * B, row0 = k0 / 32 * B, dst_words = k / 32 * TB;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < PKB * B; r += 4) {
+    const int64_t wr = row0 + r, c = n0 + tx;
+    tile[r][tx] = (wr < src_rows && c < n) ? qweight[wr * n + c] : 0u;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < 64 * PKB; it += 256) {
+    const int c = it / PKB, kb = it % PKB;
+    if (n0 + c >= n || k0 + 32 * kb >= k) continue;
+    uint32_t w[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) w[i] = tile[kb * B + i][c];
+    uint32_t o[TB];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) o[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t v = planar_field(w, j, B);
+      const int pos = j * TB, wi = pos >> 5, sh = pos & 31;
+      o[wi] |= v << sh;
+      if (sh + TB > 32) o[wi + 1] |= v >> (32 - sh);
+    }
+    uint32_t* dst = packed + (n0 + c) * dst_words + (k0 / 32 + kb) * TB;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) dst[i] = o[i];
+  }
+}
+
+template <int B, int TB>
+hipError_t launch_planar_codes(const uint32_t* qweight, int64_t k, int64_t n, uint32_t* packed, hipStream_t s) {
+  const int64_t tiles = ((k + 32 * PKB - 1) / (32 * PKB)) * ((n + 63) / 64);
+  planar_codes_kernel<B, TB><<<(unsigned)tiles, 256, 0, s>>>(qweight, k, n, packed);
   return hipGetLastError();
 }
 
@@ -162,7 +240,31 @@ hipError_t launch_transcode_gptq(const uint32_t* qweight, const uint32_t* qzeros
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int groups = (int)(k / g);
-  return launch_params(qzeros, scales, pdt, n, groups, bits, v1, 0, scales_out, biases_out, s);
+  return launch_params(qzeros, scales, pdt, n, groups, bits, v1, 0, 0, scales_out, biases_out, s);
+}
+
+hipError_t launch_transcode_gptq_planar(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
+                                        int64_t k, int64_t n, int bits, int g, uint32_t* packed, void* scales_out,
+                                        void* biases_out, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  switch (bits) {
+    case 2:
+    case 4:
+    case 8: {  // one plane: GPTQ's continuous words
+      const int64_t rows = k * bits / 32;
+      const int64_t tiles = ((rows + TT - 1) / TT) * ((n + TT - 1) / TT);
+      transpose_words_kernel<<<(unsigned)tiles, 256, 0, s>>>(qweight, rows, n, packed);
+      e = hipGetLastError();
+      break;
+    }
+    case 3: e = launch_planar_codes<3, 3>(qweight, k, n, packed, s); break;
+    case 5: e = launch_planar_codes<5, 5>(qweight, k, n, packed, s); break;
+    case 6: e = launch_planar_codes<6, 6>(qweight, k, n, packed, s); break;
+    case 7: e = launch_planar_codes<7, 8>(qweight, k, n, packed, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  return launch_params(qzeros, scales, pdt, n, (int)(k / g), bits, 0, 0, 1, scales_out, biases_out, s);
 }
 
 hipError_t launch_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros, const void* scales, int pdt,
@@ -181,7 +283,8 @@ hipError_t launch_transcode_awq(const uint32_t* qweight, const uint32_t* qzeros,
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
-  return launch_params(qzeros, scales, pdt, n, (int)(k / g), bits, 0, bits == 4 ? 1 : 0, scales_out, biases_out, s);
+  return launch_params(qzeros, scales, pdt, n, (int)(k / g), bits, 0, bits == 4 ? 1 : 0, 0, scales_out, biases_out,
+                       s);
 }
 
 }  // namespace ql
