@@ -55,6 +55,12 @@ namespace {
 #ifndef GEMM_PP_PRIO
 #define GEMM_PP_PRIO 0  // raise the wave priority during the ping-pong compute phase
 #endif
+#ifndef GEMM_PP_DEQ_MEM
+#define GEMM_PP_DEQ_MEM 3  // 3: dequantize in the mem phase, copies among the products; 0: dequantize among the products
+#endif
+#ifndef GEMM_PP_DEQ16
+#define GEMM_PP_DEQ16 1  // 4-bit codes: one shift per word, odd nibbles masked in place with scale/16
+#endif
 #ifndef GEMM_PP_BAND
 #define GEMM_PP_BAND 4  // m-tiles per band of the ping-pong kernel's tile order
 #endif
@@ -128,6 +134,17 @@ template <> struct Deq<4> {
   __device__ __forceinline__ static void runp(const uint32_t* w, uint32_t* r, f16x2_t S2, f16x2_t B2, uint32_t mk) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = deq2p((w[0] >> (4 * j)) & mk, S2, B2);
+  }
+  // The same pairs with one shift per word: the odd nibbles of each 16-bit half are masked in place
+  // (16 q, still a subnormal pattern, so 16 q 2^-24 exactly) and take S/16 (S16), so that every
+  // product is the same as above whenever S/16 is exact.  mk4 = mk << 4.
+  __device__ __forceinline__ static void runp16(const uint32_t* w, uint32_t* r, f16x2_t S2, f16x2_t S16, f16x2_t B2,
+                                                uint32_t mk, uint32_t mk4) {
+    const uint32_t hi = w[0] >> 8;
+    r[0] = deq2p(w[0] & mk, S2, B2);
+    r[1] = deq2p(w[0] & mk4, S16, B2);
+    r[2] = deq2p(hi & mk, S2, B2);
+    r[3] = deq2p(hi & mk4, S16, B2);
   }
 };
 // Two 8-bit words (codes 0..7) -> operand pairs (0,2), (1,3), (4,6), (5,7).
@@ -537,6 +554,74 @@ __global__ __launch_bounds__(256, TWO ? 2 : 1) void gemm16_kernel(const uint16_t
 }
 
 // ---------------------------------------------------------------- ping-pong kernel
+// Output of one wave of the ping-pong kernel (x rows wrow0 .. + 32 RT of the tile, columns ncol0 ..
+// + 63), for y rows of 16-byte multiples (N a multiple of 8, y 16-byte aligned): one 32-row block at
+// a time, the scaled values (acc * x row scale * column scale + layer bias, rounded once to y's
+// dtype) go into this wave's part of the LDS stages, row-major with a padded pitch (the two lane
+// halves' rows 4 apart land on distinct banks), then each lane writes whole 16-byte pieces of rows.
+// ESZ = bytes per output element.
+template <int ESZ, int RT>
+__device__ __forceinline__ void pp_store(const f32x16_t (&acc)[RT][2], const float* sXs, const float* __restrict__ wsc,
+                                         const uint16_t* __restrict__ lbias, int lb_bf16, int64_t M, int64_t N,
+                                         int64_t m0, int wrow0, int64_t ncol0, uint8_t* st0, uint8_t* st1,
+                                         uint8_t* st2, int stage_bytes, void* __restrict__ y, int ydt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, h = lane >> 5;
+  constexpr int P = 64 * ESZ + 32;        // LDS pitch of a block row (bytes)
+  constexpr int BLK = 32 * P;             // one 32-row block
+  constexpr int CPR = 64 * ESZ / 16;      // 16-byte pieces per row
+  const int per_stage = stage_bytes / BLK;
+  uint8_t* wbuf = wave < per_stage ? st0 + wave * BLK
+                                   : (wave < 2 * per_stage ? st1 + (wave - per_stage) * BLK
+                                                           : st2 + (wave - 2 * per_stage) * BLK);
+  float cs[2], add[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int64_t col = ncol0 + ct * 32 + l32;
+    const bool ok = col < N;
+    cs[ct] = ok ? wsc[col] : 0.0f;
+    add[ct] = (ok && lbias) ? (lb_bf16 ? bf16_bits_to_f32(lbias[col]) : f16_bits_to_f32(lbias[col])) : 0.0f;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float xs[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t v = *(const f32x4_t*)(sXs + wrow0 + rt * 32 + 8 * q + 4 * h);
+      xs[4 * q + 0] = v[0];
+      xs[4 * q + 1] = v[1];
+      xs[4 * q + 2] = v[2];
+      xs[4 * q + 3] = v[3];
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = acc[rt][ct][r] * (xs[r] * cs[ct]) + add[ct];
+        uint8_t* dst = wbuf + (8 * (r >> 2) + 4 * h + (r & 3)) * P + (ct * 32 + l32) * ESZ;
+        if constexpr (ESZ == 4)
+          *(float*)dst = v;
+        else
+          *(uint16_t*)dst = (uint16_t)(ydt == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v));
+      }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the block is in LDS for every lane
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < CPR / 2; ++j) {
+      const int i = j * 64 + lane;
+      const int row = i / CPR, c = i % CPR;
+      const int64_t grow = m0 + wrow0 + rt * 32 + row;
+      const int64_t gcol = ncol0 + c * (16 / ESZ);
+      const u32x4_t v = *(const u32x4_t*)(wbuf + row * P + c * 16);
+      if (grow < M && gcol < N) *(u32x4_t*)((uint8_t*)y + (grow * N + gcol) * ESZ) = v;
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the next block is written
+    asm volatile("" ::: "memory");
+  }
+}
+
 // Records of the ping-pong kernel: group-major, rec4[group * n + row] = S | B << 16 (the fp16 pair
 // of the four-wave kernel's records), so that the records of one group for 32 consecutive rows are
 // 128 contiguous bytes.
@@ -733,7 +818,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
-  __shared__ float sXs[BMT];
+  __shared__ __attribute__((aligned(16))) float sXs[BMT];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -804,7 +889,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
                       stage + j * A_HALF + (grp_u * (BMT / 2) + w4_u * (BMT / 8) + 8 * i) * 128);
     } else if (c < NA + NB) {
       const int i = c - NA;
-      copy_to_lds<16>(rsB, b_off[i], (uint32_t)((int64_t)kt * BK * BITS / 8),
+      copy_to_lds<16>(rsB, kt < KT ? b_off[i] : kOOB, (uint32_t)((int64_t)kt * BK * BITS / 8),
                       stage + A_BYTES + (grp_u * 128 + w4_u * 32 + 16 * i) * B_ROW);
     } else {
       const int i = c - NA - NB;
@@ -894,13 +979,19 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
         fa[rt][t] = *(const u32x4_t*)(half + (r * 8 + (slot ^ xswz(r))) * 16);
       }
   };
+  const uint32_t mk4 = vconst(0x00F000F0u);
   auto dequant = [&](int t, u32x4_t* bq) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const uint32_t word = GPK > 2 ? sb[ct][t >= KS / 2 ? 1 : 0] : sb[ct][0];
       const f16x2_t sbv = __builtin_bit_cast(f16x2_t, word);
       uint32_t r[4];
-      Deq<BITS>::runp(&cw[ct][t * (BITS / 4)], r, f16x2_t{sbv[0], sbv[0]}, f16x2_t{sbv[1], sbv[1]}, mk);
+      if constexpr (BITS == 4 && GEMM_PP_DEQ16) {
+        const _Float16 s16 = sbv[0] * (_Float16)0.0625f;
+        Deq<4>::runp16(&cw[ct][t], r, f16x2_t{sbv[0], sbv[0]}, f16x2_t{s16, s16}, f16x2_t{sbv[1], sbv[1]}, mk, mk4);
+      } else {
+        Deq<BITS>::runp(&cw[ct][t * (BITS / 4)], r, f16x2_t{sbv[0], sbv[0]}, f16x2_t{sbv[1], sbv[1]}, mk);
+      }
       bq[ct] = u32x4_t{r[0], r[1], r[2], r[3]};
     }
   };
@@ -941,6 +1032,9 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
+  // The dequantized operands of the whole k-tile, made in the mem phase: the vector work then runs
+  // while the other wave of the SIMD issues its products, and the compute phase is products only.
+  u32x4_t bq[GEMM_PP_DEQ_MEM ? KS : 1][2];
   // One k-tile: mem phase (the copies of tile t+2 into the stage tile t-1 freed, then tile t's
   // fragments; at its end this wave's copies of tile t+1 must have landed), barrier, compute phase
   // (products only), barrier.
@@ -956,6 +1050,38 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
       if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(1);
       compute(t + 2 < KT ? t + 2 : -1, free_stage);
       if (GEMM_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+      barrier();
+      return;
+    }
+    if (GEMM_PP_DEQ_MEM == 3) {
+      // mem phase: fragments and the dequantized codes of tile t; this wave's copies of tile t+1,
+      // issued during its previous compute phase, must have landed (vmcnt(0)) before the barrier
+      // that precedes the first read of tile t+1.  Compute phase: the products, with this wave's
+      // copies of tile t+2 issued among them (one after each k-step's products), so that the
+      // copy stream drains over both phases; past the last tile they read nothing (out-of-range
+      // offsets) into the free stage.
+      mem_frag(cur);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ts = 0; ts < KS; ++ts) {
+        dequant(ts, bq[ts]);
+        // pin the results in this phase: otherwise they are sunk to their use among the products
+        asm volatile("" : "+v"(bq[ts][0]), "+v"(bq[ts][1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt_lgkm0<0>();
+      barrier();
+      constexpr int per = (NC + KS - 1) / KS;
+#pragma unroll
+      for (int ts = 0; ts < KS; ++ts) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) acc[rt][ct] = mfma16(fa[rt][ts], bq[ts][ct], acc[rt][ct]);
+#pragma unroll
+        for (int c = ts * per; c < (ts + 1) * per && c < NC; ++c) copy_one(t + 2, free_stage, c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       barrier();
       return;
     }
@@ -992,12 +1118,28 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(const PPArgs a) {
     if (t + 1 < KT) step(t + 1, st1, st0);
     if (t + 2 < KT) step(t + 2, st2, st1);
   }
+  wait_vmcnt<0>();            // no copy may still be writing LDS when the workgroup ends
   if (grp_u == 0) barrier();  // the same number of barriers on every wave
 
   // Epilogue: lane holds column l32 of each 32x32 tile, rows 8*(r/4) + 4*h + (r%4).
+  const int64_t ncol0 = n0 + grp * 128 + wn * 64;  // the wave's first column
+  if (N % 8 == 0 && ((uintptr_t)W.y & 15) == 0) {
+    // every copy has landed and no wave reads the stages any more: they take the output blocks
+    barrier();
+    if (a.ydt == DT_F32)
+      pp_store<4, RT>(acc, sXs, W.wsc, W.layer_bias, a.lb_bf16, M, N, m0, wm * WM, ncol0, st0, st1, st2, STAGE, W.y,
+                      DT_F32);
+    else if (a.ydt == DT_BF16)
+      pp_store<2, RT>(acc, sXs, W.wsc, W.layer_bias, a.lb_bf16, M, N, m0, wm * WM, ncol0, st0, st1, st2, STAGE, W.y,
+                      DT_BF16);
+    else
+      pp_store<2, RT>(acc, sXs, W.wsc, W.layer_bias, a.lb_bf16, M, N, m0, wm * WM, ncol0, st0, st1, st2, STAGE, W.y,
+                      DT_F16);
+    return;
+  }
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    const int64_t col = n0 + grp * 128 + wn * 64 + ct * 32 + l32;
+    const int64_t col = ncol0 + ct * 32 + l32;
     if (col >= N) continue;
     const float cs = W.wsc[col];
     const float add = W.layer_bias ? (a.lb_bf16 ? bf16_bits_to_f32(W.layer_bias[col]) : f16_bits_to_f32(W.layer_bias[col]))
