@@ -263,10 +263,10 @@ def _time_launches(fn, reps, warmup, stream):
 
 
 def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which="all"):
-    sel = set(which.split(",")) if which != "all" else None
+    selected = frozenset(which.split(",")) if which != "all" else None
 
     def want(name):
-        return sel is None or name in sel
+        return selected is None or name in selected
 
     legs = {}
     # ---------------- 8-bit decode at batch 1 and 8, 4-bit decode at batch 8
@@ -294,12 +294,12 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
         for label, pick in (("lm_head_alone", lambda pr: pr[-1:]), ("layers_alone", lambda pr: pr[:-1])):
             sub = []
             for probs, _, kw in sets_b:
-                sel = pick(probs)
-                arr = q.qlinear_problem_list(sel)
+                picked = pick(probs)
+                arr = q.qlinear_problem_list(picked)
                 ws = torch.empty(q.qlinear_gemv_batched_workspace_size(arr), dtype=torch.uint8, device=dev)
                 kw2 = dict(kw, workspace=ws)
                 q.qlinear_gemv_batched(arr, upload=True, **kw2)
-                sub.append((sel, arr, kw2))
+                sub.append((picked, arr, kw2))
             byts = sum(p_["packed"].numel() * 4 + p_["scales"].numel() * 4 for p_ in sub[0][0])
             _, avg = time_decode(sub, 200, 300)
             out[label] = {"kernel_ms": round(avg, 5), "weight_gbs": round(byts / (avg * 1e-3) / 1e9, 1),
