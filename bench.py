@@ -492,7 +492,7 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
             "tflops": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1),
             "layer_ms": round(tot_ms, 4),
             "per_projection": per6,
-            "kernel": "stream_to_bytes + prep16 + gemm16_kernel<8,false,false> (+ splitk_reduce on k/v)",
+            "kernel": "stream_to_bytes + prep_pp + gemm_pp_kernel<8,64,128> (k, v alone: prep16 + gemm16_kernel<8> + splitk_reduce)",
         }
 
     # ---------------- bitstream widths (2, 3, 5, 6 bits): the decode step at batch 1, one problem-list
