@@ -320,7 +320,7 @@ def test_gemm_parity(m, n, k, bits, g, xdt, pdt):
     y = q.qlinear_gemm(x, pk, sc, bi, bits=bits, group_size=g, y_dtype=torch.float32)
     _sync()
     # the GEMM rounds each dequantized weight once to fp16 (2^-12 relative) before the fp32
-    # accumulation: ~1.5e-4 per row, inside the 2e-3 bound on products
+    # accumulation: ~1.5e-4 per row, inside GEMM_TOL
     _assert_rel(y, O.apply(xf, D), GEMM_TOL, "gemm")
 
 
