@@ -19,9 +19,9 @@
 //
 // x is staged once per workgroup in LDS, permuted to the order the code unpacking gives, with a
 // zero row that the lanes of non-matching (row, group) pairs read, and the table of group sums.
-// The workgroup's scales and biases are read once, coalesced, into LDS (reading them per u-block
-// and lane touches 16 rows' cache lines per instruction).  Weight words are read with a plain
-// cache policy: a 128-byte line is consumed by two consecutive u-blocks.
+// The workgroup's scales and biases are copied once, coalesced, into LDS by DMA (reading them
+// per u-block and lane touches 16 rows' cache lines per instruction).  Weight words are read with
+// a plain cache policy: a 128-byte line is consumed by two consecutive u-blocks.
 #pragma once
 #include "gemv_impl.hpp"
 
@@ -61,27 +61,31 @@ template <int WPB> struct MfBuf {
   u32x4_t w[MRS][MNU][WPB];
 };
 
-// The (scale | bias << 16) words of the u-block's groups for one row, from LDS (G = 32: four
-// groups; 64: two; 128: one).
+// The scales and biases of the u-block's groups for one row, from the two LDS arrays that hold
+// the workgroup's rows as they lie in memory (G = 32: four groups, two words of each; 64: two
+// groups, one word; 128: one group, one 16-bit value in the low half).
 template <int G> struct MfParams;
 template <> struct MfParams<32> {
-  uint32_t v[4];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    const u32x4_t t = *(const u32x4_t*)p;
-    v[0] = t[0], v[1] = t[1], v[2] = t[2], v[3] = t[3];
+  uint32_t s[2], b[2];
+  __device__ __forceinline__ void load(const uint8_t* ps, const uint8_t* pb) {
+    const u32x2_t ts = *(const u32x2_t*)ps, tb = *(const u32x2_t*)pb;
+    s[0] = ts[0], s[1] = ts[1], b[0] = tb[0], b[1] = tb[1];
   }
 };
 template <> struct MfParams<64> {
-  uint32_t v[2];
-  __device__ __forceinline__ void load(const uint8_t* p) {
-    const u32x2_t t = *(const u32x2_t*)p;
-    v[0] = t[0], v[1] = t[1];
+  uint32_t s[1], b[1];
+  __device__ __forceinline__ void load(const uint8_t* ps, const uint8_t* pb) {
+    s[0] = *(const uint32_t*)ps, b[0] = *(const uint32_t*)pb;
   }
 };
 template <> struct MfParams<128> {
-  uint32_t v[1];
-  __device__ __forceinline__ void load(const uint8_t* p) { v[0] = *(const uint32_t*)p; }
+  uint32_t s[1], b[1];
+  __device__ __forceinline__ void load(const uint8_t* ps, const uint8_t* pb) {
+    s[0] = *(const uint16_t*)ps, b[0] = *(const uint16_t*)pb;
+  }
 };
+
+typedef __attribute__((address_space(3))) void mf_lds_void;
 
 template <int MT, int G, typename XT, typename PT, int BITS>
 __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc single, const GemvDesc* __restrict__ table,
@@ -179,34 +183,23 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
 
   // -- LDS: MT rows of x, each KP values at pitch XP, permuted per 8 values as the codes unpack;
   //    then a zero row; then the sums X[ub][i] of accumulator row i's x values in u-block ub;
-  //    then the workgroup's scales and biases as (scale | bias << 16) words, `groups` per row.
+  //    then the workgroup's scales, then its biases, each `groups` 16-bit values per row.
   const GemvMfLds lay = gemv_mf_lds(k, MT, G, d.batches);
   float* xsum = (float*)((uint8_t*)sx + lay.xsum_off);
   float* xscale = (float*)((uint8_t*)sx + lay.xscale_off);
-  uint8_t* sp = (uint8_t*)sx + lay.param_off;
+  uint8_t* sps = (uint8_t*)sx + lay.param_off;
+  uint8_t* spb = (uint8_t*)sx + lay.bias_off;
   {
-    // rows of the workgroup that exist, times groups / 2 words of scales (and of biases); read
-    // coalesced, a group count per row that is even keeps every word inside one array
-    // coalesced, a group count per row that is even keeps every word inside one array.  PU passes'
-    // loads are issued before any of them is written (one round trip, not one per pass): the large
-    // workgroups of 4 to 8 x rows stage many passes.
-    const int64_t prow = rows_left < geo.rows_per_wg ? rows_left : geo.rows_per_wg;
-    const int pw = (int)(prow * groups / 2);
-    constexpr int PU = MT >= 4 ? GEMV_MF_PU_M8 : GEMV_MF_PU;
-    for (int t0 = threadIdx.x; t0 < pw; t0 += 256 * PU) {
-      uint32_t sw[PU], bw[PU];
-#pragma unroll
-      for (int u = 0; u < PU; ++u) {
-        const int t = t0 + 256 * u;
-        sw[u] = __builtin_amdgcn_raw_buffer_load_b32(rsc, t < pw ? 4 * t : kOOB, 0, 0);
-        bw[u] = __builtin_amdgcn_raw_buffer_load_b32(rbi, t < pw ? 4 * t : kOOB, 0, 0);
+    // The scales and biases of the rows of the workgroup that exist (groups / 2 words per row,
+    // contiguous in memory) are copied HBM -> LDS by DMA, 64 words per wave instruction, every
+    // pass in flight at once and no registers held: the x staging below issues its loads behind
+    // them, so both take one round trip.  The wait before the barrier below lands them.
+    const int pw = (int)((rows_left < geo.rows_per_wg ? rows_left : geo.rows_per_wg) * groups / 2);
+    for (int i0 = wave * 64; i0 < pw; i0 += 256)
+      if (i0 + lane < pw) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (mf_lds_void*)(sps + 4 * i0), 4, 4 * (i0 + lane), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbi, (mf_lds_void*)(spb + 4 * i0), 4, 4 * (i0 + lane), 0, 0, 0);
       }
-#pragma unroll
-      for (int u = 0; u < PU; ++u) {
-        const int t = t0 + 256 * u;
-        if (t < pw) *(u32x2_t*)(sp + 8 * t) = u32x2_t{perm(bw[u], sw[u], 0x05040100u), perm(bw[u], sw[u], 0x07060302u)};
-      }
-    }
   }
   gptr<uint16_t> xg = (gptr<uint16_t>)d.x;
   const int c8n = KP / 8;
@@ -295,6 +288,9 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
       xsum[ub * 16 + i] = 0.0f;
     }
   }
+  // this wave's parameter copies have landed (vmcnt 0; expcnt and lgkmcnt left alone), then the
+  // barrier publishes every wave's
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
   // A row of this lane is j: x row j / GU, group slot j % GU; its k-slots (quadrant h) lie in
@@ -343,8 +339,8 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   };
 
   auto compute = [&](int b, int i, const MfBuf<WPB>& q) __attribute__((always_inline)) {
-    // this lane's parameter words of u-block i * MNU, per row set
-    const uint8_t* pb = sp + ((lrow0 + b * kSetRows) * groups + i * MNU * GU) * 4;
+    // this lane's (row, group) index at u-block i * MNU, per row set
+    const int pe = (lrow0 + b * kSetRows) * groups + i * MNU * GU;
 #pragma unroll
     for (int u = 0; u < MNU; ++u) {
       const int ub = i * MNU + u;  // past UB the x rows and sums are zero
@@ -367,12 +363,13 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
         for (int t = 0; t < 4; ++t) D = MfOp<CT>::mma(a[t], u32x4_t{c[4 * t], c[4 * t + 1], c[4 * t + 2], c[4 * t + 3]}, D);
         // past UB the words of the row's last u-block stand in (finite; they meet zeros)
         MfParams<G> pr;
-        pr.load(pb + (rs * 16 * groups + min(u, UB - 1 - i * MNU) * GU) * 4);
+        const int e = pe + rs * 16 * groups + min(u, UB - 1 - i * MNU) * GU;
+        pr.load(sps + 2 * e, spb + 2 * e);
         float sv[GU < NR ? GU : NR], bv[GU < NR ? GU : NR];
 #pragma unroll
         for (int gp = 0; gp < (GU < NR ? GU : NR); ++gp) {
-          sv[gp] = half_param<PT>(pr.v[gp], false);
-          bv[gp] = half_param<PT>(pr.v[gp], true);
+          sv[gp] = half_param<PT>(pr.s[gp / 2], gp % 2 == 1);
+          bv[gp] = half_param<PT>(pr.b[gp / 2], gp % 2 == 1);
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {

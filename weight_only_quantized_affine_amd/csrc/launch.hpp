@@ -107,16 +107,10 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #define GEMV_MF_SCHED 1
 #endif
 #ifndef GEMV_MF_MINB
-#define GEMV_MF_MINB 1  // workgroups per CU the register allocation must allow
+#define GEMV_MF_MINB 1  // waves per SIMD the register allocation must allow
 #endif
 #ifndef GEMV_MF_AUX
 #define GEMV_MF_AUX 0  // cache policy bits of the weight-word loads
-#endif
-#ifndef GEMV_MF_PU
-#define GEMV_MF_PU 1  // passes of the parameter staging whose loads a thread issues at once
-#endif
-#ifndef GEMV_MF_PU_M8
-#define GEMV_MF_PU_M8 8  // the same for 4 to 8 x rows
 #endif
 #ifndef GEMV_MF_SU
 #define GEMV_MF_SU 4  // 16-byte chunks of x a thread loads at once when it stages x
@@ -141,10 +135,9 @@ __host__ __device__ inline GemvMfGeom gemv_mf_geometry(int64_t k, int batches) {
 __host__ __device__ constexpr int gemv_mf_gu(int g) { return g >= 128 ? 1 : 128 / g; }
 // LDS of a matrix-core GEMV launch, in this order: mt x rows and one zero row of kpad + 8
 // elements; the table of x sums (one float per u-block and accumulator row); the x row factors
-// (8 floats); the workgroup's scales and biases, interleaved per group (scale | bias << 16, one
-// word per row and group).
+// (8 floats); the workgroup's scales, then its biases (16 bits per row and group, as in memory).
 struct GemvMfLds {
-  size_t xsum_off, xscale_off, param_off, bytes;
+  size_t xsum_off, xscale_off, param_off, bias_off, bytes;
 };
 __host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int batches) {
   const GemvMfGeom geo = gemv_mf_geometry(k, batches);
@@ -152,7 +145,8 @@ __host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int b
   r.xsum_off = ((size_t)(mt + 1) * (geo.kpad + 8) * 2 + 15) / 16 * 16;
   r.xscale_off = r.xsum_off + (size_t)geo.steps_per_row * GEMV_MF_NU * 16 * 4;
   r.param_off = r.xscale_off + 32;
-  r.bytes = r.param_off + (size_t)geo.rows_per_wg * (k / g) * 4;
+  r.bias_off = r.param_off + (size_t)geo.rows_per_wg * (k / g) * 2;
+  r.bytes = r.bias_off + (size_t)geo.rows_per_wg * (k / g) * 2;
   return r;
 }
 #ifndef GEMV_MF_ENABLE
