@@ -33,7 +33,7 @@ int gemv_mf_batches(int64_t n, int64_t k, int bits, int g, int mt, int64_t min_t
   int nb = set_bytes > 0 ? (int)((target + set_bytes / 2) / set_bytes) : 1;
   nb = nb < 1 ? 1 : (nb > 32 ? 32 : nb);
   while (nb > 1 &&
-         ((n + rows * nb - 1) / (rows * nb) < min_tiles || gemv_mf_lds(k, mt, g, nb).bytes > GEMV_MF_LDS_MAX))
+         ((n + rows * nb - 1) / (rows * nb) < min_tiles || gemv_mf_lds(k, mt, g, nb, bits).bytes > GEMV_MF_LDS_MAX))
     --nb;
   return nb;
 }

@@ -136,9 +136,28 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   const int lrow0 = wave * 16 * MRS + j;  // this lane's weight row in row set 0 of batch 0
   constexpr int kSetRows = 64 * MRS;       // rows of one batch of the workgroup
 
+  // 4-bit codes, 5 to 8 x rows (whose loads run three steps ahead): a step's 16 rows x 128 bytes
+  // (u-blocks 2i, 2i + 1) are read by two loads that each cover 8 whole 128-byte lines,
+  // non-temporally (lane 8q + p of half f reads 16-byte chunk (p - q) mod 8 of row 8f + q: the
+  // rotation spreads the chunks one product reads over the LDS banks); before the products the
+  // wave regroups them through its LDS area into the product layout (lane (j, h) of u-block u:
+  // row j, chunk 4u + h).  Rows past n read zeros; a u-block past the row's last is clamped to
+  // it, as below.
+  constexpr bool kLines = gemv_mf_lines(BITS, MT);
   auto issue = [&](int st, MfBuf<WPB>& q) __attribute__((always_inline)) {
     const int b = st / SR, i = st - b * SR;
     const bool live = st < steps;
+    if constexpr (kLines) {
+      const int qr = lane >> 3, c = ((lane & 7) - qr) & 7;
+      const int ub = min(2 * i + (c >> 2), UB - 1);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int lr = wave * 16 + b * kSetRows + 8 * f + qr;
+        const uint32_t off = live ? (uint32_t)(lr * row_bytes + ub * 64 + 16 * (c & 3)) : (uint32_t)kOOB;
+        q.w[0][f][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, GEMV_MF_LAUX));
+      }
+      return;
+    }
 #pragma unroll
     for (int rs = 0; rs < MRS; ++rs) {
       const int lr = lrow0 + b * kSetRows + rs * 16;
@@ -183,8 +202,9 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
 
   // -- LDS: MT rows of x, each KP values at pitch XP, permuted per 8 values as the codes unpack;
   //    then a zero row; then the sums X[ub][i] of accumulator row i's x values in u-block ub;
-  //    then the workgroup's scales, then its biases, each `groups` 16-bit values per row.
-  const GemvMfLds lay = gemv_mf_lds(k, MT, G, d.batches);
+  //    then the workgroup's scales, then its biases, each `groups` 16-bit values per row; then,
+  //    for 4-bit codes and 5 to 8 x rows, each wave's regrouping area.
+  const GemvMfLds lay = gemv_mf_lds(k, MT, G, d.batches, BITS);
   float* xsum = (float*)((uint8_t*)sx + lay.xsum_off);
   float* xscale = (float*)((uint8_t*)sx + lay.xscale_off);
   uint8_t* sps = (uint8_t*)sx + lay.param_off;
@@ -380,10 +400,23 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
     }
   };
 
+  uint8_t* sre = (uint8_t*)sx + lay.regroup_off + wave * kGemvMfRegroupBytes;
   auto run = [&](int st, const MfBuf<WPB>& q) __attribute__((always_inline)) {
     if (st < steps) {
       const int b = st / SR, i = st - b * SR;
-      compute(b, i, q);
+      if constexpr (kLines) {
+        // the wave's LDS accesses run in order: the previous step's reads of the area are done
+#pragma unroll
+        for (int f = 0; f < 2; ++f) *(u32x4_t*)(sre + f * kGemvMfHalfOff + 16 * lane) = q.w[0][f][0];
+        MfBuf<WPB> r;
+        const int q7 = j & 7;
+        const uint8_t* sb = sre + (j >> 3) * kGemvMfHalfOff + 128 * q7;
+#pragma unroll
+        for (int u = 0; u < MNU; ++u) r.w[0][u][0] = *(const u32x4_t*)(sb + 16 * ((4 * u + h + q7) & 7));
+        compute(b, i, r);
+      } else {
+        compute(b, i, q);
+      }
       if (i == SR - 1) finish_batch(b);
     }
   };

@@ -115,6 +115,19 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #ifndef GEMV_MF_SU
 #define GEMV_MF_SU 4  // 16-byte chunks of x a thread loads at once when it stages x
 #endif
+#ifndef GEMV_MF_LINES
+#define GEMV_MF_LINES 1  // 4-bit codes, 5 to 8 x rows: whole 128-byte lines per load, regrouped through LDS
+#endif
+#ifndef GEMV_MF_LAUX
+#define GEMV_MF_LAUX 2  // cache policy bits of those loads (non-temporal: each line is read once)
+#endif
+// A wave's regrouping area: its 16 rows x 128 bytes as two 1 KB halves (rows 0-7, rows 8-15),
+// the second 128 bytes after the first's end so that the two halves' lanes meet different banks.
+constexpr int kGemvMfRegroupBytes = 2304;
+constexpr int kGemvMfHalfOff = 1152;
+__host__ __device__ constexpr bool gemv_mf_lines(int bits, int mt) {
+  return GEMV_MF_LINES && bits == 4 && mt >= 8 && GEMV_MF_NU == 2 && GEMV_MF_RS == 1;
+}
 struct GemvMfGeom {
   int ublocks;        // k / 128
   int steps_per_row;  // ceil(ublocks / GEMV_MF_NU)
@@ -135,18 +148,20 @@ __host__ __device__ inline GemvMfGeom gemv_mf_geometry(int64_t k, int batches) {
 __host__ __device__ constexpr int gemv_mf_gu(int g) { return g >= 128 ? 1 : 128 / g; }
 // LDS of a matrix-core GEMV launch, in this order: mt x rows and one zero row of kpad + 8
 // elements; the table of x sums (one float per u-block and accumulator row); the x row factors
-// (8 floats); the workgroup's scales, then its biases (16 bits per row and group, as in memory).
+// (8 floats); the workgroup's scales, then its biases (16 bits per row and group, as in memory);
+// for 4-bit codes and 5 to 8 x rows, each wave's regrouping area (16-byte aligned).
 struct GemvMfLds {
-  size_t xsum_off, xscale_off, param_off, bias_off, bytes;
+  size_t xsum_off, xscale_off, param_off, bias_off, regroup_off, bytes;
 };
-__host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int batches) {
+__host__ __device__ inline GemvMfLds gemv_mf_lds(int64_t k, int mt, int g, int batches, int bits) {
   const GemvMfGeom geo = gemv_mf_geometry(k, batches);
   GemvMfLds r;
   r.xsum_off = ((size_t)(mt + 1) * (geo.kpad + 8) * 2 + 15) / 16 * 16;
   r.xscale_off = r.xsum_off + (size_t)geo.steps_per_row * GEMV_MF_NU * 16 * 4;
   r.param_off = r.xscale_off + 32;
   r.bias_off = r.param_off + (size_t)geo.rows_per_wg * (k / g) * 2;
-  r.bytes = r.bias_off + (size_t)geo.rows_per_wg * (k / g) * 2;
+  r.regroup_off = (r.bias_off + (size_t)geo.rows_per_wg * (k / g) * 2 + 15) / 16 * 16;
+  r.bytes = r.regroup_off + (gemv_mf_lines(bits, mt) ? (size_t)4 * kGemvMfRegroupBytes : 0);
   return r;
 }
 #ifndef GEMV_MF_ENABLE
@@ -161,7 +176,7 @@ inline bool gemv_mf_eligible(int64_t m, int64_t k, int bits, int g, const void* 
     return false;
   if ((k / g) % 2 != 0 || ((uintptr_t)scales | (uintptr_t)biases) % 4 != 0) return false;
   const int mt = gemv_mt(m);
-  return mt * gemv_mf_gu(g) <= 16 && gemv_mf_lds(k, mt, g, 1).bytes <= GEMV_MF_LDS_MAX;
+  return mt * gemv_mf_gu(g) <= 16 && gemv_mf_lds(k, mt, g, 1, bits).bytes <= GEMV_MF_LDS_MAX;
 }
 // Batches per workgroup: about GEMV_MF_WG_BYTES (GEMV_MF_WG_BYTES_M8 for mt = 8) of packed words,
 // fewer when `min_tiles` workgroups would otherwise not be reached or the LDS would pass

@@ -327,7 +327,7 @@ ql_status qlinear_gemv(const void* x, ql_dtype x_dtype, int64_t m, int64_t k, co
       const ql::GemvMfGeom g = ql::gemv_mf_geometry(k, d.batches);
       const int64_t tiles = (n + g.rows_per_wg - 1) / g.rows_per_wg;
       e = ql::launch_gemv_mf(d, nullptr, nullptr, tiles, (int)mm, bits, group_size, dt(x_dtype), dt(param_dtype),
-                             dt(y_dtype), ql::gemv_mf_lds(k, mt, group_size, d.batches).bytes, (hipStream_t)stream);
+                             dt(y_dtype), ql::gemv_mf_lds(k, mt, group_size, d.batches, bits).bytes, (hipStream_t)stream);
     } else {
       d.batches = ql::gemv_batches(n, k, bits, 1024);
       const ql::GemvGeom g = ql::gemv_geometry(k, bits, d.batches);
@@ -513,7 +513,7 @@ void make_plan(const ql_problem* probs, int count, BatchedPlan& plan) {
       if (c.mf_g) {
         d.batches = ql::gemv_mf_batches(p.n, p.k, p.bits, p.group_size, ql::gemv_mt(p.m), 1);
         const ql::GemvMfGeom g = ql::gemv_mf_geometry(p.k, d.batches);
-        lds_x = std::max(lds_x, ql::gemv_mf_lds(p.k, ql::gemv_mt(p.m), p.group_size, d.batches).bytes);
+        lds_x = std::max(lds_x, ql::gemv_mf_lds(p.k, ql::gemv_mt(p.m), p.group_size, d.batches, p.bits).bytes);
         const int64_t t = (p.n + g.rows_per_wg - 1) / g.rows_per_wg;
         for (int64_t i = 0; i < t; ++i) plan.tiles.push_back(ql::GemvTile{q, (int32_t)i});
         continue;
