@@ -29,7 +29,7 @@ hipError_t launch_gemv_mf_m8(const GemvDesc&, const GemvDesc*, const GemvTile*, 
 int gemv_mf_batches(int64_t n, int64_t k, int bits, int g, int mt, int64_t min_tiles) {
   const int64_t rows = gemv_mf_geometry(k, 1).rows_per_wg;
   const int64_t set_bytes = rows * (k * bits / 8);
-  const int64_t target = mt >= 8 ? GEMV_MF_WG_BYTES_M8 : GEMV_MF_WG_BYTES;
+  const int64_t target = mt >= 8 ? (bits == 8 ? GEMV_MF_WG_BYTES_M8_B8 : GEMV_MF_WG_BYTES_M8) : GEMV_MF_WG_BYTES;
   int nb = set_bytes > 0 ? (int)((target + set_bytes / 2) / set_bytes) : 1;
   nb = nb < 1 ? 1 : (nb > 32 ? 32 : nb);
   while (nb > 1 &&

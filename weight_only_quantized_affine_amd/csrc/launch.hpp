@@ -91,6 +91,9 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #ifndef GEMV_MF_WG_BYTES_M8
 #define GEMV_MF_WG_BYTES_M8 262144  // the same for 5 to 8 x rows (staging x costs more per workgroup)
 #endif
+#ifndef GEMV_MF_WG_BYTES_M8_B8
+#define GEMV_MF_WG_BYTES_M8_B8 524288  // the same for 5 to 8 x rows of 8-bit codes
+#endif
 #ifndef GEMV_MF_LDS_MAX
 #define GEMV_MF_LDS_MAX (80 * 1024)  // LDS of one workgroup (two fit a compute unit)
 #endif
