@@ -214,6 +214,10 @@ GEMV_CASES = [
     (6, 300, 2560, 4, 64, "bf16", "bf16", "f32"),
     (8, 70, 768, 4, 128, "bf16", "bf16", "f32"),
     (7, 1100, 3072, 4, 64, "f16", "bf16", "bf16"),
+    # 5-8 x rows at 4 bits read whole lines regrouped through LDS: an odd u-block count (the last
+    # step's second u-block clamped) and a single u-block per row
+    (5, 200, 1152, 4, 64, "bf16", "bf16", "f32"),
+    (8, 33, 128, 4, 64, "bf16", "f16", "f32"),
     # m = 5..8 with group size 32 needs 32 accumulator rows: the vector-ALU kernel
     (5, 100, 512, 4, 32, "bf16", "bf16", "f32"),
     # 8-bit, k a multiple of 128: the matrix-core kernel with f16 products (bf16 x converted)
