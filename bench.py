@@ -262,6 +262,34 @@ def _time_launches(fn, reps, warmup, stream):
     return sum(ms) / len(ms), sorted(ms)[len(ms) // 2]
 
 
+def _time_graph(fn, reps, warmup):
+    """Average milliseconds per call of `reps` calls fn(0) .. fn(reps - 1) captured as one HIP graph
+    (no host work between calls, as in the decode step), after `warmup` eager calls and three
+    replays; HIP events on the replaying stream around a fourth replay."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            fn(i)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del g
+    return ms
+
+
 def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which="all"):
     selected = frozenset(which.split(",")) if which != "all" else None
 
@@ -410,9 +438,10 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
                     blocks = torch.cat([d, qv], dim=3).reshape(e, n, nb * 34).contiguous()
                     copies.append((blocks, None))
                     wb = blocks.numel()
-            avg, med = _time_launches(
+            # calls captured in a graph: each one is the routing launch and the products launch
+            avg = _time_graph(
                 lambda i: q.qlinear_apply_experts(fmt, copies[i % 3][0], copies[i % 3][1], ids, x, n=n, k=k,
-                                                  pos_per_row=top, y=y, workspace=ws), 20, 20, stream)
+                                                  pos_per_row=top, y=y, workspace=ws), 30, 10)
             byts = wb + x.numel() * 2 + y.numel() * 2
             gbs = byts / (avg * 1e-3) / 1e9
             legs[f"experts_{fname}"] = {
@@ -451,9 +480,9 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
                 blocks[..., dat:dat + 2 * nd] = d.to(torch.float16).view(torch.uint8).view(e, n, nb, 2 * nd)
                 copies.append(blocks.reshape(e, n, nb * nbytes).contiguous())
             wb = copies[0].numel()
-            avg, med = _time_launches(
+            avg = _time_graph(
                 lambda i: q.qlinear_apply_experts(fmt, copies[i % 3], None, ids, x, n=n, k=k, pos_per_row=top, y=y,
-                                                  workspace=ws), 20, 20, stream)
+                                                  workspace=ws), 20, 10)
             byts = wb + x.numel() * 2 + y.numel() * 2
             gbs = byts / (avg * 1e-3) / 1e9
             legs[f"experts_{fname}"] = {

@@ -618,6 +618,31 @@ def test_apply_experts_small(fmt, ydt):
 
 
 @pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
+def test_apply_experts_graph_replay_matches_eager(fmt):
+    """Routed apply (routing and products launches) captured in a HIP graph and replayed 4 times,
+    with eager work in between: every replay gives the eager bits."""
+    (w0, w1), _, ids, xb, n, k, top = _experts_small(fmt, 81 + fmt)
+    idt = torch.from_numpy(ids.reshape(-1)).to(DEV)
+    x = bits_to_dev(xb, "bf16")
+    y = torch.empty((ids.size, n), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(q.qlinear_apply_experts_workspace_size(ids.size, w0.shape[0]), dtype=torch.uint8, device=DEV)
+    kw = dict(n=n, k=k, pos_per_row=top, y=y, workspace=ws)
+    q.qlinear_apply_experts(fmt, w0, w1, idt, x, **kw)
+    _sync()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        q.qlinear_apply_experts(fmt, w0, w1, idt, x, **kw)
+    for rep in range(4):
+        y.fill_(rep + 1)
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), f"replay {rep}"
+
+
+@pytest.mark.parametrize("fmt", [q.QL_MXFP4, q.QL_Q8_0])
 def test_apply_experts_f16_x(fmt):
     """fp16 activations (Nx_quant Products, apply_experts: any float x): MXFP4 takes them as the
     exact sum of two bf16 parts, Q8_0 as they are; the same bounds as bf16 x."""

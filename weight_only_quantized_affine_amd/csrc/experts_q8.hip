@@ -23,6 +23,9 @@ using namespace ex_detail;
 // the block; the four lanes of a row read the tile's 136 bytes.  x rows go straight into QNS LDS
 // stages, QNS - 1 k-tiles ahead, and are converted to fp16 in place once they have landed; the
 // weight windows go into a ring of QNS register buffers.
+#ifndef EXPERTS_Q8_CONV_AHEAD
+#define EXPERTS_Q8_CONV_AHEAD 1  // convert x one k-tile ahead, one barrier per k-tile
+#endif
 constexpr int QBK = 128, QMC = 96, QCT = 2, QW = 8, QBN = QW * 16 * QCT, QNS = 3;
 
 struct Q8Buf {
@@ -168,6 +171,55 @@ __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const
   };
 
   Q8Buf wbr[QNS];
+#if EXPERTS_Q8_CONV_AHEAD
+  // One k-tile kt: wait until this wave's copies of x(kt + 1) have landed (and the weights of kt),
+  // barrier (every wave's copies of x(kt + 1) are in LDS, and every wave is done with step kt - 1:
+  // the products of kt - 1 and the conversion of x(kt)), copy x(kt + 2) into the stage kt - 1
+  // freed, products of kt, convert x(kt + 1) in place while other waves issue their products,
+  // load the weights of kt + 3 into the ring slot just consumed.  One barrier per k-tile; x is
+  // copied one k-tile ahead of its conversion.
+  auto step2 = [&](int kt, const uint8_t* cur, uint8_t* next, uint8_t* refill, Q8Buf& wb) __attribute__((always_inline)) {
+    ex_wait_vmcnt<NW>();
+    __builtin_amdgcn_s_barrier();
+    copy_x(kt + 2 < KT ? kt + 2 : KT - 1, refill);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt < KT) compute(kt, cur, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!XF16) {
+      if (kt + 1 < KT) convert_x(next);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this thread's conversions are in LDS
+      asm volatile("" ::: "memory");
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(kt + QNS < KT ? kt + QNS : KT - 1, wb);
+    asm volatile("" ::: "memory");
+  };
+  copy_x(0, stg[0]);
+  asm volatile("" ::: "memory");
+  load_w(0, wbr[0]);
+  asm volatile("" ::: "memory");
+  copy_x(1 < KT ? 1 : KT - 1, stg[1]);
+  asm volatile("" ::: "memory");
+  load_w(1 < KT ? 1 : KT - 1, wbr[1]);
+  load_w(2 < KT ? 2 : KT - 1, wbr[2]);
+  asm volatile("" ::: "memory");
+  ex_wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();  // x(0) of every wave is in LDS
+  if constexpr (!XF16) {
+    convert_x(stg[0]);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+  }
+#pragma unroll
+  for (int j = 0; j < QNS; ++j) step2(j, stg[j], stg[(j + 1) % QNS], stg[(j + 2) % QNS], wbr[j]);
+  for (int kt = QNS; kt < KT; kt += QNS) {
+#pragma unroll
+    for (int j = 0; j < QNS; ++j) step2(kt + j, stg[j], stg[(j + 1) % QNS], stg[(j + 2) % QNS], wbr[j]);
+  }
+#else
   // One k-tile: wait for its x copies and weights, barrier (every wave is done with the stage the
   // copies below refill), copy x of kt + QNS - 1, convert this tile's x, barrier, compute, load the
   // weights of kt + QNS into the ring slot just consumed.  Steps past the last tile (completing a
@@ -207,6 +259,7 @@ __device__ __forceinline__ void q8_chunk(const int32_t* __restrict__ sPos, const
 #pragma unroll
     for (int j = 0; j < QNS; ++j) step(kt + j, stg[j], stg[(j + QNS - 1) % QNS], wbr[j]);
   }
+#endif
   ex_wait_vmcnt<0>();  // no copy may still be writing LDS
   if (big) *sFlag = 1;
   __syncthreads();     // every wave is done with the stages: stage 0 now holds the output blocks
