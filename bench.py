@@ -500,28 +500,38 @@ def run_legs(q, torch, synth, dev, stream, gen, build_decode, time_decode, which
     if want("prefill6"):
         log("leg: prefill GEMM 9B layer, M=2048, 6-bit")
         m = 2048
-        tot_flop = tot_ms = 0.0
-        per6 = {}
+        wts = {}
         for i, (name, k, n) in enumerate(synth.PREFILL_9B_LAYER):
             w = torch.randn((n, k), generator=gen(45_000 + i), device=dev) * 0.02
             pk, sc, bi = q.qlinear_quantize(w, 6, 64, torch.bfloat16)
             del w
-            x = torch.randn((m, k), generator=gen(46_000 + i), device=dev).to(torch.bfloat16)
-            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            ws = torch.empty(q.qlinear_gemm_workspace_size(m, n, k, 6, 64), dtype=torch.uint8, device=dev)
-            avg, _ = _time_launches(
-                lambda _i: q.qlinear_gemm(x, pk, sc, bi, bits=6, group_size=64, y=y, workspace=ws), 10, 20, stream)
-            flop = 2.0 * m * n * k
-            per6[name] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+            wts[name] = dict(packed=pk, scales=sc, biases=bi, y=torch.empty((m, n), dtype=torch.bfloat16, device=dev),
+                             k=k, n=n)
+        calls = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gate_up", ["gate", "up"]), ("down", ["down"])]
+        tot_flop = tot_ms = 0.0
+        per6 = {}
+        for ci, (cname, members) in enumerate(calls):
+            k = wts[members[0]]["k"]
+            x = torch.randn((m, k), generator=gen(46_000 + ci), device=dev).to(torch.bfloat16)
+            ws_list = [dict(packed=wts[nm]["packed"], scales=wts[nm]["scales"], biases=wts[nm]["biases"], y=wts[nm]["y"])
+                       for nm in members]
+            ws = torch.empty(q.qlinear_gemm_grouped_workspace_size(m, k, ws_list, 6, 64), dtype=torch.uint8,
+                             device=dev)
+            avg, _ = _time_launches(lambda _i: q.qlinear_gemm_grouped(x, ws_list, bits=6, group_size=64, workspace=ws),
+                                    10, 20, stream)
+            flop = sum(2.0 * m * wts[nm]["n"] * k for nm in members)
+            per6[cname] = {"ms": round(avg, 4), "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
             tot_flop += flop
             tot_ms += avg
-            del pk, sc, bi, x, y, ws
+            del x, ws
+        del wts
         torch.cuda.empty_cache()
         legs["prefill_gemm_9b_layer_6bit"] = {
             "tflops": round(tot_flop / (tot_ms * 1e-3) / 1e12, 1),
             "layer_ms": round(tot_ms, 4),
-            "per_projection": per6,
-            "kernel": "stream_to_bytes + prep_pp + gemm_pp_kernel<8,64,128> (k, v alone: prep16 + gemm16_kernel<8> + splitk_reduce)",
+            "per_call": per6,
+            "kernel": "stream_to_bytes (per weight) + prep_pp + gemm_pp_kernel<8,64,128> (q|k|v and gate|up grouped; "
+                      "o, down alone)",
         }
 
     # ---------------- bitstream widths (2, 3, 5, 6 bits): the decode step at batch 1, one problem-list

@@ -231,9 +231,10 @@ typedef struct {
 /* Prefill GEMM of up to four weights that read the same x (the projections one layer input feeds,
  * such as q, k and v, or gate and up): y_j = x . dequant(W_j)^T for each, the product of
  * qlinear_gemm (Nx_quant Products, apply), with x converted once and one launch over the tiles of
- * every weight, so that small weights do not need a launch of their own.  Each y_j equals what
- * qlinear_gemm gives for W_j alone whenever that call runs on the same kernel (4- and 8-bit codes
- * and enough output tiles: then the grouped call always does); at other shapes and widths the
+ * every weight, so that small weights do not need a launch of their own (at 2, 3, 5 and 6 bits
+ * each weight's codes are first written as bytes into the workspace and the launch takes them as
+ * 8-bit codes).  Each y_j equals what qlinear_gemm gives for W_j alone whenever that call runs on
+ * the same kernel (enough output tiles: then the grouped call always does); at other shapes the
  * call runs qlinear_gemm once per weight.  Arguments as qlinear_gemm; count in [0, 4]; the
  * workspace is qlinear_gemm_grouped_workspace_size bytes, 16-byte aligned. */
 size_t qlinear_gemm_grouped_workspace_size(int64_t m, int64_t k, const ql_gemm_weight* weights, int count,

@@ -28,6 +28,9 @@ def _weight(seed, n, k, bits, g, pdt):
     (900, (3000, 257, 1100, 500), 1024, 4, 128, "f16", "bf16", "f16"),
     (1200, (2300, 1000), 768, 8, 64, "bf16", "bf16", "f32"),
     (1000, (1500, 1700), 1088, 8, 32, "f16", "f16", "f32"),
+    # bitstream widths: the codes of every weight as bytes, then the 8-bit launch over all of them
+    (1100, (2600, 300, 700), 1024, 6, 64, "bf16", "bf16", "f32"),
+    (1050, (2600, 1300), 1088, 3, 32, "f16", "bf16", "bf16"),
 ])
 def test_gemm_grouped_ragged(m, ns, k, bits, g, xdt, pdt, ydt):
     weights, Ds, lbs = [], [], []

@@ -1368,19 +1368,36 @@ hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint3
 // weight.  Either way each weight's result is the one its own qlinear_gemm call gives when that
 // call takes the ping-pong kernel (the tiles and their sums do not depend on the other weights).
 bool gemm_grouped_pp(int64_t m, int64_t k, const GemmWeight* w, int count, int bits, int g) {
-  if (bits != 4 && bits != 8) return false;
+  if (bits != 4 && bits != 8 && !is_stream_bits(bits)) return false;
   GemmW ww[4];
   for (int j = 0; j < count; ++j) ww[j] = GemmW{w[j].packed, w[j].scales, w[j].biases, w[j].layer_bias, w[j].y, w[j].n};
   return pp_eligible(m, k, g, ww, count);
 }
 
+// With the ping-pong launch at the bitstream widths, every weight's codes as bytes follow (n * k
+// bytes each, padded to 256).
 size_t gemm_grouped_workspace_bytes(int64_t m, int64_t k, const GemmWeight* w, int count, int bits, int g) {
   size_t pp = ws_x_bytes(m, k), single = 0;
   for (int j = 0; j < count; ++j) {
-    pp += ws_w_bytes(w[j].n, k, g);
+    pp += ws_w_bytes(w[j].n, k, g) + (is_stream_bits(bits) ? pad256((size_t)(w[j].n * k)) : 0u);
     single = std::max(single, gemm_workspace_bytes(m, w[j].n, k, bits, g));
   }
   return gemm_grouped_pp(m, k, w, count, bits, g) ? pp : single;
+}
+
+// Bitstream rows (2, 3, 5, 6 bits) -> one byte per code (the 8-bit layout) at codes8.
+hipError_t launch_stream_to_bytes(const uint32_t* packed, int64_t n, int64_t k, int bits, uint8_t* codes8,
+                                  hipStream_t s) {
+  const unsigned nb = (unsigned)((n * (k / 32) + 255) / 256);
+  if (bits == 2)
+    stream_to_bytes_kernel<2><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+  else if (bits == 3)
+    stream_to_bytes_kernel<3><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+  else if (bits == 5)
+    stream_to_bytes_kernel<5><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+  else
+    stream_to_bytes_kernel<6><<<nb, 256, 0, s>>>(packed, n, k, codes8);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_grouped(const void* x, int xdt, int64_t m, int64_t k, const GemmWeight* w, int count, int pdt,
@@ -1396,8 +1413,22 @@ hipError_t launch_gemm_grouped(const void* x, int xdt, int64_t m, int64_t k, con
   }
   GemmW ww[4];
   int nw = 0;
-  for (int j = 0; j < count; ++j)
-    if (w[j].n > 0) ww[nw++] = GemmW{w[j].packed, w[j].scales, w[j].biases, w[j].layer_bias, w[j].y, w[j].n};
+  // bitstream widths: every weight's codes become bytes after the ping-pong launch's own workspace,
+  // and the launch takes them as 8-bit codes
+  uint8_t* codes8 = (uint8_t*)ws + ws_x_bytes(m, k);
+  for (int j = 0; j < count; ++j) codes8 += ws_w_bytes(w[j].n, k, g);
+  for (int j = 0; j < count; ++j) {
+    if (w[j].n == 0) continue;
+    const uint32_t* packed = w[j].packed;
+    if (is_stream_bits(bits)) {
+      const hipError_t e = launch_stream_to_bytes(w[j].packed, w[j].n, k, bits, codes8, s);
+      if (e != hipSuccess) return e;
+      packed = (const uint32_t*)codes8;
+      codes8 += pad256((size_t)(w[j].n * k));
+    }
+    ww[nw++] = GemmW{packed, w[j].scales, w[j].biases, w[j].layer_bias, w[j].y, w[j].n};
+  }
+  if (is_stream_bits(bits)) bits = 8;
   const bool xb = xdt == DT_BF16, pb = pdt == DT_BF16;
   if (bits == 4) {
     if (xb && pb) return launch_pp<4, BF16, BF16>(x, m, k, ww, nw, g, ydt, ws, s);
@@ -1417,16 +1448,7 @@ hipError_t launch_gemm(const void* x, int xdt, int64_t m, int64_t k, const uint3
   const bool xb = xdt == DT_BF16, pb = pdt == DT_BF16;
   if (is_stream_bits(bits)) {
     uint8_t* codes8 = (uint8_t*)ws + gemm_base_bytes(m, n, k, g);
-    const unsigned nb = (unsigned)((n * (k / 32) + 255) / 256);
-    if (bits == 2)
-      stream_to_bytes_kernel<2><<<nb, 256, 0, s>>>(packed, n, k, codes8);
-    else if (bits == 3)
-      stream_to_bytes_kernel<3><<<nb, 256, 0, s>>>(packed, n, k, codes8);
-    else if (bits == 5)
-      stream_to_bytes_kernel<5><<<nb, 256, 0, s>>>(packed, n, k, codes8);
-    else
-      stream_to_bytes_kernel<6><<<nb, 256, 0, s>>>(packed, n, k, codes8);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e = launch_stream_to_bytes(packed, n, k, bits, codes8, s);
     if (e != hipSuccess) return e;
     packed = (const uint32_t*)codes8;
     bits = 8;
