@@ -32,6 +32,9 @@ using namespace ex_detail;
 #ifndef EXPERTS_MX_SCL_MAX
 #define EXPERTS_MX_SCL_MAX (48 * 1024)  // LDS bytes for the staged scale bytes
 #endif
+#ifndef EXPERTS_MX_SCL16
+#define EXPERTS_MX_SCL16 1  // stage the scale bytes 16 per lane (else 4)
+#endif
 #ifndef EXPERTS_MX_MINB
 #define EXPERTS_MX_MINB 1  // workgroups per compute unit the register allocation must allow
 #endif
@@ -401,11 +404,21 @@ __global__ __launch_bounds__(512, EXPERTS_MX_MINB) void experts_mx_kernel(const 
     // loop through registers would wait out one round trip per pass); the chunk loop's first
     // barrier, after the wait below, publishes them
     const int64_t live = min((int64_t)XBN, N - nt * XBN);
-    const int nd = (int)((ssh + live * (K / 32) + 3) / 4);
     const uint32_t a0 = (uint32_t)(sbase - ssh);
-    for (int i0 = wave * 64; i0 < nd; i0 += XW * 64)
-      if (i0 + lane < nd)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sScl32 + i0), 4, a0 + 4u * (i0 + lane), 0, 0, 0);
+    if (EXPERTS_MX_SCL16) {
+      // 16 bytes per lane: the last chunk may copy up to 15 bytes past the tile's scale bytes into
+      // the rest of the 1 KB-rounded allocation (bytes past every scale read zero)
+      const int nd = (int)((ssh + live * (K / 32) + 15) / 16);
+      for (int i0 = wave * 64; i0 < nd; i0 += XW * 64)
+        if (i0 + lane < nd)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sScl32 + 4 * i0), 16, a0 + 16u * (i0 + lane), 0, 0,
+                                                   0);
+    } else {
+      const int nd = (int)((ssh + live * (K / 32) + 3) / 4);
+      for (int i0 = wave * 64; i0 < nd; i0 += XW * 64)
+        if (i0 + lane < nd)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsS, (lds_void*)(sScl32 + i0), 4, a0 + 4u * (i0 + lane), 0, 0, 0);
+    }
     ex_wait_vmcnt<0>();
   }
   const uint8_t* sScl = (const uint8_t*)sScl32;
@@ -424,7 +437,10 @@ hipError_t launch_experts_mx(const uint8_t* codes, const uint8_t* scales, int64_
                              const int32_t* offsets, const int32_t* perm, const int32_t* order, const uint16_t* x,
                              int xdt, int64_t x_rows, int64_t pos_per_row, void* y, int ydt, hipStream_t s) {
   const unsigned grid = (unsigned)(e * ((n + XBN - 1) / XBN));
-  const size_t scl = (size_t)((3 + XBN * (k / 32) + 3) / 4 * 4);
+  // the staged scale bytes (from the aligned word at or below the first), rounded up to whole
+  // 1 KB copies when they are copied 16 bytes per lane
+  const size_t scl = EXPERTS_MX_SCL16 ? (size_t)((3 + XBN * (k / 32) + 1023) / 1024 * 1024)
+                                      : (size_t)((3 + XBN * (k / 32) + 3) / 4 * 4);
   const bool blk = scales == nullptr;  // GGUF blocks: codes holds the 17-byte blocks
   const bool in_lds = !blk && scl <= (size_t)XSCL_MAX;
   const bool h = xdt == DT_F16;
