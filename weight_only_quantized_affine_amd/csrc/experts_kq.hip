@@ -194,31 +194,39 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
   };
 
   typename F::Lane Lc[KQ_CT], Ln[KQ_CT];
+  // Sub-block sums of the rows this wave copied: each lane sums the 8 values of the chunk its own
+  // copy wrote, and the lanes of a sub-block (an aligned group of KQ_SL slots: the slot order is
+  // the chunk order xor row % 16) add theirs; the first of them writes the sum.  Only this wave's
+  // copies are read, so its own wait for them suffices; the barrier that follows publishes the sums.
+  constexpr int KQ_SL = F::kSubLen / 8;  // chunks (and lanes) per sub-block: 4 or 2
+  auto own_sums = [&](const uint8_t* buf, float* sum) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      if (2 * (KQ_W * i + wave_u) < 16 * MS) {  // uniform
+        const int r = 2 * (KQ_W * i + wave) + (lane >> 5), slot = lane & 31;
+        const u32x4_t v = *(const u32x4_t*)(buf + (r * 32 + slot) * 16);
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ps += KqOp<XT>::lo(v[e]) + KqOp<XT>::hi(v[e]);
+#pragma unroll
+        for (int o = 1; o < KQ_SL; o <<= 1) ps += __shfl_xor(ps, o);
+        if ((slot & (KQ_SL - 1)) == 0) sum[r * 16 + (slot ^ (r & 15)) / KQ_SL] = ps;
+      }
+    }
+  };
   copy_x(0, sx0);
   load_w(0, Lc);
   for (int kb = 0; kb < KB; ++kb) {
     uint8_t* const cur = (kb & 1) ? sx1 : sx0;
     float* const sum = (kb & 1) ? sxs1 : sxs0;
-    ex_wait_vmcnt<0>();  // block kb's x copies and weights have landed
-    __syncthreads();     // ... for every wave, and every wave is done with block kb - 1's buffers
+    ex_wait_vmcnt<0>();  // this wave's copies of block kb's x and its weights have landed
+    own_sums(cur, sum);
+    __syncthreads();     // every wave's x and sums of block kb are in LDS, and every wave is done
+                         // with block kb - 1's buffers
     if (kb + 1 < KB) {   // uniform
       copy_x(kb + 1, (kb & 1) ? sx0 : sx1);
       load_w(kb + 1, Ln);
     }
-    // sub-block sums of x: (row, sub-block) pairs
-    for (int t = tid; t < 16 * MS * F::kSub; t += KQ_W * 64) {
-      const int r = t / F::kSub, j = t - r * F::kSub;
-      float acc_s = 0.0f;
-#pragma unroll
-      for (int c8 = 0; c8 < F::kSubLen / 8; ++c8) {
-        const int c = j * (F::kSubLen / 8) + c8;
-        const u32x4_t v = *(const u32x4_t*)(cur + (r * 32 + (c ^ (r & 15))) * 16);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc_s += KqOp<XT>::lo(v[e]) + KqOp<XT>::hi(v[e]);
-      }
-      sum[r * 16 + j] = acc_s;
-    }
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < F::kSub; ++j) {
       float s[KQ_CT], bb[KQ_CT];
