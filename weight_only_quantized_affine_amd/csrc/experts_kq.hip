@@ -210,7 +210,7 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
         for (int e = 0; e < 4; ++e) ps += KqOp<XT>::lo(v[e]) + KqOp<XT>::hi(v[e]);
 #pragma unroll
         for (int o = 1; o < KQ_SL; o <<= 1) ps += __shfl_xor(ps, o);
-        if ((slot & (KQ_SL - 1)) == 0) sum[r * 16 + (slot ^ (r & 15)) / KQ_SL] = ps;
+        if ((slot & (KQ_SL - 1)) == 0) sum[((slot ^ (r & 15)) / KQ_SL) * KQ_MC + r] = ps;
       }
     }
   };
@@ -240,8 +240,7 @@ __device__ __forceinline__ void kq_chunk(const int32_t* __restrict__ sPos, int r
       for (int rt = 0; rt < MS; ++rt) {
         const int r = rt * 16 + j16;
         // this lane's accumulator rows 4q .. 4q + 3 of the m-subtile: their sub-block sums
-        const f32x4_t X = f32x4_t{sum[(rt * 16 + 4 * q) * 16 + j], sum[(rt * 16 + 4 * q + 1) * 16 + j],
-                                  sum[(rt * 16 + 4 * q + 2) * 16 + j], sum[(rt * 16 + 4 * q + 3) * 16 + j]};
+        const f32x4_t X = *(const f32x4_t*)(sum + j * KQ_MC + rt * 16 + 4 * q);
         f32x4_t D[KQ_CT];
         if constexpr (FMT == 4) {
           const int c = 4 * j + q;  // values 32 j + 8 q .. + 7
@@ -295,10 +294,12 @@ __global__ __launch_bounds__(KQ_W * 64, 2) void experts_kq_kernel(const uint8_t*
                                                                   const int32_t* __restrict__ order,
                                                                   const uint16_t* __restrict__ x, int64_t x_rows,
                                                                   int64_t pos_per_row, void* __restrict__ y, int ydt) {
-  // two x buffers and two tables of sub-block sums (blocks kb and kb + 1)
+  // two x buffers and two tables of sub-block sums (blocks kb and kb + 1), [sub-block][row] so
+  // that a lane's four accumulator rows are one 16-byte read
   __shared__ __attribute__((aligned(16))) uint8_t sx0[KQ_MC * 256 * 2];
   __shared__ __attribute__((aligned(16))) uint8_t sx1[KQ_MC * 256 * 2];
-  __shared__ float sxs0[KQ_MC * 16], sxs1[KQ_MC * 16];
+  __shared__ __attribute__((aligned(16))) float sxs0[KQ_MC * 16];
+  __shared__ __attribute__((aligned(16))) float sxs1[KQ_MC * 16];
   __shared__ int32_t sPos[KQ_MC];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t n_tiles = (N + KQ_BN - 1) / KQ_BN;
