@@ -328,3 +328,19 @@ def test_gemm_grouped_rejects_bad_arguments(lib):
     assert lib.qlinear_gemm_grouped(FAKE, BF16, 8, 64, arr, 2, BF16, 4, 64, F32, None, 0, None) == QL_ERR_WORKSPACE
     assert lib.qlinear_gemm_grouped(FAKE, BF16, 0, 64, arr, 2, BF16, 4, 64, F32, None, 0, None) == QL_OK
     assert lib.qlinear_gemm_grouped(None, BF16, 8, 64, None, 0, BF16, 4, 64, F32, None, 0, None) == QL_OK
+
+
+def test_gemm_grouped_workspace_at_bitstream_widths(lib):
+    """With enough tiles for one launch over all weights, the grouped call at 2, 3, 5 and 6 bits
+    holds every weight's codes as bytes after the 8-bit launch's own workspace; with too few it
+    runs qlinear_gemm per weight and needs the largest single call's workspace."""
+    W = q._GemmWeight
+    m, k, ns = 2048, 4096, (4096, 1024, 1024)
+    arr = (W * 3)(*[W(FAKE, FAKE, FAKE, None, FAKE, n) for n in ns])
+    need8 = lib.qlinear_gemm_grouped_workspace_size(m, k, arr, 3, 8, 64)
+    for bits in (2, 3, 5, 6):
+        need = lib.qlinear_gemm_grouped_workspace_size(m, k, arr, 3, bits, 64)
+        assert need == need8 + sum(n * k for n in ns), bits
+    small = (W * 2)(W(FAKE, FAKE, FAKE, None, FAKE, 256), W(FAKE, FAKE, FAKE, None, FAKE, 512))
+    assert lib.qlinear_gemm_grouped_workspace_size(64, k, small, 2, 6, 64) == \
+        lib.qlinear_gemm_workspace_size(64, 512, k, 6, 64)
