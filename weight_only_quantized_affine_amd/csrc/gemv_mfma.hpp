@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, GEMV_MF_MINB) void gemv_mf_kernel(GemvDesc sin
   const int c8n = KP / 8;
   // x is staged MSU chunks of 8 values per thread at a time, their loads issued together (one
   // round trip per MSU chunks); chunk t is (x row t / c8n, values 8 (t % c8n) ..), zero past m or k
-  constexpr int MSU = GEMV_MF_SU;
+  constexpr int MSU = MT >= 8 ? GEMV_MF_SU_M8 : GEMV_MF_SU;
   auto load_x = [&](int t, int total) __attribute__((always_inline)) {
     const int xr = t / c8n, c8 = t - xr * c8n;
     u32x4_t r = {0u, 0u, 0u, 0u};

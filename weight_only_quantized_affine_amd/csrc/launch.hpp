@@ -118,6 +118,9 @@ GemvLds gemv_lds(int64_t k, int bits, int64_t mt, int batches);
 #ifndef GEMV_MF_SU
 #define GEMV_MF_SU 4  // 16-byte chunks of x a thread loads at once when it stages x
 #endif
+#ifndef GEMV_MF_SU_M8
+#define GEMV_MF_SU_M8 8  // the same with 5 to 8 x rows
+#endif
 #ifndef GEMV_MF_LINES
 #define GEMV_MF_LINES 1  // 4-bit codes, 5 to 8 x rows: whole 128-byte lines per load, regrouped through LDS
 #endif
